@@ -1,0 +1,173 @@
+/*
+ * libbifocal -- dynamic bifocal RoPE attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method (Jet-Long, "Efficient Long-Context Extension with Dynamic
+ * Bifocal RoPE"): causal softmax attention whose score for query position q
+ * and key position k is
+ *     RoPE(x_q, q)    . RoPE(x_k, k)       when q - k <= w0   (local window)
+ *     RoPE(x_q, f(q)) . RoPE(x_k, f(k))    when q - k >  w0   (remote view)
+ * with f(x) = floor(x / G) and G = max(1, ceil(L / w_pretrained)).
+ *   - r9-hu paper digest of the paper, section Method: Eq. 1 (the score), the
+ *     "Dynamic group size" paragraph (G, f), the "KV cache invariant"
+ *     paragraph (absolute keys in the cache, correction offsets
+ *     Delta = f(x) - x, R_a R_b = R_{a+b}) and the "Inclusion-exclusion
+ *     prefill" paragraph (three passes merged by LSE weights).
+ *   - pith.science review of arXiv 2607.07740, axiom ledger: Sec. 3.1 Eq. 2,
+ *     Sec. 3.2 Eqs. 5-6, Sec. 3.3 Eq. 7.
+ *
+ * Conventions shared by every entry point:
+ *   - Positions are 0-based and restart at each sequence's first token.
+ *   - RoPE rotates the pair (x_i, x_{i+d/2}) by p * theta^(-2i/d),
+ *     i = 0 .. d/2-1 (rotate-half pairing). Angles are formed and reduced
+ *     modulo 2*pi in float64 before float32 sin/cos.
+ *   - q - k == w0 is local. The softmax scale defaults to 1/sqrt(d).
+ *   - GQA: query head h reads KV head h / (Hq / Hkv).
+ *   - Token-major packed layouts: [T, H, d] row-major, d contiguous, every
+ *     base pointer 16-byte aligned. LSE is [Hq, T] float32, natural log.
+ *   - "void* stream" is a hipStream_t (NULL = the default stream). All device
+ *     work is asynchronous on that stream; the caller owns every buffer.
+ *   - The library never allocates device memory, keeps no state between
+ *     calls and never writes the inputs (the KV cache included).
+ *   - Errors: arguments are validated on the host BEFORE any launch; a
+ *     failing check returns a negative status and launches nothing. A HIP
+ *     launch failure returns JL_EHIP (see jl_last_hip_error()). Faults that
+ *     happen later on the device surface at the caller's synchronisation.
+ *     No entry point aborts or prints.
+ */
+#ifndef BIFOCAL_H
+#define BIFOCAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JL_OK 0
+#define JL_EINVAL (-1)       /* bad scalar, shape or pointer argument            */
+#define JL_EUNSUPPORTED (-2) /* head dim / dtype / mode combination not built    */
+#define JL_EHIP (-3)         /* HIP launch or runtime error                      */
+#define JL_EWORKSPACE (-4)   /* workspace NULL or smaller than the size query    */
+
+typedef enum { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
+
+/* FUSED: one pass, each (query tile, key tile) classified local / remote /
+ *        boundary, per-element select on boundary tiles.
+ * IE:    the pages' three attention passes (window+absolute, causal+remapped,
+ *        window+remapped) merged by Eq. 7. A checked alternative.
+ * PLAIN: ordinary causal RoPE attention (every pair local) -- the baseline
+ *        the bifocal overhead is measured against. */
+typedef enum { JL_MODE_FUSED = 0, JL_MODE_IE = 1, JL_MODE_PLAIN = 2 } jl_mode;
+
+/* Eq. 2: G = max(1, ceil(L / w_pre)) in exact integer arithmetic.
+ * Returns G >= 1, or JL_EINVAL when L < 1 or w_pre < 1. Host only. */
+int64_t jl_group_size(int64_t L, int64_t w_pre);
+
+/* Class of the tile with query positions q0..q1 and key positions k0..k1
+ * (inclusive, sequence-relative), from the routing condition of Eq. 1:
+ *   0 masked   (k0 > q1: no causal pair)
+ *   1 local    (q1 - k0 <= w0: every causal pair is in the window)
+ *   2 remote   (q0 - k1 >  w0: every causal pair is outside it)
+ *   3 boundary (both kinds)
+ *   +4 when the causal diagonal crosses the tile (k1 > q0), for classes 1/3.
+ * Depends on distances only, never on G. JL_EINVAL if q0 > q1, k0 > k1, any
+ * position is negative, or w0 < 0. Host only. */
+int jl_tile_class(int64_t q0, int64_t q1, int64_t k0, int64_t k1, int64_t w0);
+
+/* Query-tile rows (BM) and key-tile width (BN) the prefill kernels use for
+ * dtype dt and head dim d. JL_EUNSUPPORTED if that combination is not built. */
+int jl_prefill_tile_shape(jl_dtype dt, int d, int* bm, int* bn);
+
+/* Absolute RoPE in place: x[t, h, :] = RoPE(x[t, h, :], pos(t)) where
+ * pos(t) = pos_offset + (t - start of t's sequence). x: [T, H, d] bf16 or
+ * fp32 on the device. cu_seqlens: device int32 [B+1] prefix offsets
+ * (cu_seqlens[0] = 0, cu_seqlens[B] = T), or NULL for one sequence (B is then
+ * ignored). This is how keys enter the absolute KV cache ("KV cache
+ * invariant" paragraph of the digest's Method section).
+ * Errors: JL_EINVAL (NULL x, T < 0, H < 1, d odd or > 256, pos_offset < 0,
+ * theta <= 1, B < 1 with cu_seqlens), JL_EUNSUPPORTED (d not a multiple of
+ * 16), JL_EHIP. T == 0 is a no-op. */
+int jl_rope_apply(void* x, int64_t T, int H, int d, const int32_t* cu_seqlens, int B,
+                  int64_t pos_offset, double theta, jl_dtype dt, void* stream);
+
+/* Bytes of device workspace jl_bifocal_prefill needs for these sizes. */
+size_t jl_prefill_workspace_size(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt,
+                                 jl_mode mode);
+
+/* Byte offset, inside a prefill workspace sized for these arguments, of the
+ * float32 [Hq, T] array where JL_MODE_IE stores each row's cancellation ratio
+ * (W_B + W_C) / (W_A + W_B - W_C) of Eq. 7: how much the subtraction of
+ * pass C can amplify rounding in that row (small values are benign). */
+size_t jl_prefill_ie_ratio_offset(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt);
+
+/* Causal bifocal attention over a packed batch (Eq. 1; Eq. 7 in IE mode).
+ *   xq  [T, Hq, d]  RAW (not yet rotated) queries      bf16 | fp32
+ *   xk  [T, Hkv, d] RAW keys                            bf16 | fp32
+ *   v   [T, Hkv, d] values                              bf16 | fp32
+ *   o   [T, Hq, d]  output (overwritten)                bf16 | fp32
+ *   lse [Hq, T]     float32 natural-log LSE per row, or NULL
+ *   kcache_out [T, Hkv, d] or NULL: receives RoPE(xk, absolute position),
+ *       the same values jl_rope_apply writes, so one call also fills the
+ *       absolute KV cache for later decoding.
+ *   cu_seqlens: device int32 [B+1] (as in jl_rope_apply) or NULL for one
+ *       sequence of length T (B must then be 1). Every sequence takes its own
+ *       G from its own length.
+ *   w0 >= 0, w_pre >= 1, theta > 1, scale <= 0 selects 1/sqrt(d).
+ * The kernels rotate the raw vectors directly to the absolute and the
+ * remapped positions (the correction rotation of the cached keys by
+ * R_{f(k)-k} gives the same vectors by R_a R_b = R_{a+b}; starting from the
+ * raw inputs avoids rounding the absolute vectors twice).
+ * Supported: bf16 with d = 128 (all modes); fp32 with d = 64 or 128.
+ * Workspace: jl_prefill_workspace_size(...) bytes of device memory, any
+ * contents, 256-byte aligned; it holds the rotated key tiles, the transposed
+ * values and the tile schedule. Errors: JL_EINVAL, JL_EUNSUPPORTED,
+ * JL_EWORKSPACE, JL_EHIP. T == 0 is a no-op. */
+int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, float* lse,
+                       void* kcache_out, const int32_t* cu_seqlens, int B, int64_t T, int Hq,
+                       int Hkv, int d, int64_t w0, int64_t w_pre, double theta, float scale,
+                       jl_dtype dt, jl_mode mode, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace jl_bifocal_decode needs (for any pos < capacity
+ * and any num_splits it would choose or accept). */
+size_t jl_decode_workspace_size(int64_t capacity, int Hq, int d);
+
+/* One generation step at position pos (0-based) against the absolute cache:
+ * L = pos + 1 and G = max(1, ceil(L / w_pre)); keys 0..pos are read, the
+ * cache is never written ("KV cache invariant" paragraph; Pith ledger
+ * Sec. 3.2 Eqs. 5-6).
+ *   xq      [Hq, d]            RAW query of the token at pos   bf16 | fp32
+ *   kcache  [capacity, Hkv, d] keys already rotated at their absolute
+ *                              positions (jl_rope_apply / kcache_out)
+ *   vcache  [capacity, Hkv, d] values
+ *   o       [Hq, d] output; lse [Hq] float32 or NULL.
+ * Remote keys (pos - k > w0) are corrected on the fly by R_{f(k) - k} and
+ * scored against RoPE(xq, f(pos)); local keys are scored against
+ * RoPE(xq, pos). JL_MODE_PLAIN scores every key as local (the baseline);
+ * JL_MODE_IE is not a decode mode (JL_EUNSUPPORTED).
+ * num_splits: key-range splits merged by LSE; 0 lets the library choose.
+ * Supported: bf16 or fp32, d = 128 or 64, Hq / Hkv in {1, 2, 4, 8}.
+ * Errors: JL_EINVAL (pos < 0, pos >= capacity, bad heads, NULL pointers,
+ * num_splits < 0), JL_EUNSUPPORTED, JL_EWORKSPACE, JL_EHIP. */
+int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, void* o, float* lse,
+                      int64_t pos, int64_t capacity, int Hq, int Hkv, int d, int64_t w0,
+                      int64_t w_pre, double theta, float scale, jl_dtype dt, jl_mode mode,
+                      int num_splits, void* workspace, size_t ws_bytes, void* stream);
+
+/* Device-side tile classifier dump: out_dev[i * nk + j] (int8, device) gets
+ * the class the prefill kernels compute for query tile i and key tile j of a
+ * length-L sequence, nq = ceil(L / BM), nk = ceil(L / BN) with BM, BN from
+ * jl_prefill_tile_shape(JL_BF16, 128, ...). For bit-exact checks against
+ * jl_tile_class and an independent definition. */
+int jl_debug_tile_classes(int64_t L, int64_t w0, int8_t* out_dev, void* stream);
+
+/* Static English text for a status code; never NULL. */
+const char* jl_status_string(int status);
+
+/* hipError_t of the most recent JL_EHIP on the calling thread (0 if none). */
+int jl_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BIFOCAL_H */

@@ -1,0 +1,222 @@
+"""Python binding of libbifocal (dynamic bifocal RoPE attention, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libbifocal.so, reached through its C ABI (include/bifocal.h).
+PyTorch supplies device memory and the current HIP stream. There is no CPU
+fallback: without the built library, or given CPU tensors, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "BifocalError", "lib", "group_size", "tile_class", "prefill_tile_shape",
+    "status_string", "rope_apply", "prefill_workspace_size", "bifocal_prefill",
+    "decode_workspace_size", "bifocal_decode", "debug_tile_classes", "ie_ratio_view",
+    "MODES",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbifocal.so")
+JL_BF16, JL_FP32 = 0, 1
+MODES = {"fused": 0, "ie": 1, "plain": 2}
+
+_c_i64, _c_int, _c_dbl, _c_flt, _c_p, _c_sz = (ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                                              ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t)
+
+_SIGS = {
+    "jl_group_size": (_c_i64, [_c_i64, _c_i64]),
+    "jl_tile_class": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
+    "jl_prefill_tile_shape": (_c_int, [_c_int, _c_int, ctypes.POINTER(_c_int),
+                                       ctypes.POINTER(_c_int)]),
+    "jl_rope_apply": (_c_int, [_c_p, _c_i64, _c_int, _c_int, _c_p, _c_int, _c_i64, _c_dbl, _c_int,
+                               _c_p]),
+    "jl_prefill_workspace_size": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "jl_prefill_ie_ratio_offset": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "jl_bifocal_prefill": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_i64,
+                                    _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_dbl, _c_flt,
+                                    _c_int, _c_int, _c_p, _c_sz, _c_p]),
+    "jl_decode_workspace_size": (_c_sz, [_c_i64, _c_int, _c_int]),
+    "jl_bifocal_decode": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_int,
+                                   _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int, _c_int, _c_int,
+                                   _c_p, _c_sz, _c_p]),
+    "jl_debug_tile_classes": (_c_int, [_c_i64, _c_i64, _c_p, _c_p]),
+    "jl_status_string": (ctypes.c_char_p, [_c_int]),
+    "jl_last_hip_error": (_c_int, []),
+}
+
+_lib = None
+
+
+class BifocalError(RuntimeError):
+    """A libbifocal call returned a negative status."""
+
+    def __init__(self, fn: str, status: int):
+        msg = status_string(status)
+        if status == -3:
+            msg += f" (hipError_t {lib().jl_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [{status}]")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbifocal.so (built in-tree by build.py). Raises if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libbifocal.so not built at {LIB_PATH}; run "
+                              "`python -m rope_context_extension_jl_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().jl_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status < 0:
+        raise BifocalError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return JL_BF16
+    if t.dtype == torch.float32:
+        return JL_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _dev(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libbifocal has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ---------------------------------------------------------------- host-only calls
+def group_size(L: int, w_pre: int) -> int:
+    g = lib().jl_group_size(int(L), int(w_pre))
+    _check("jl_group_size", g)
+    return int(g)
+
+
+def tile_class(q0: int, q1: int, k0: int, k1: int, w0: int) -> int:
+    c = lib().jl_tile_class(int(q0), int(q1), int(k0), int(k1), int(w0))
+    _check("jl_tile_class", c)
+    return int(c)
+
+
+def prefill_tile_shape(dtype=torch.bfloat16, d: int = 128):
+    bm, bn = _c_int(), _c_int()
+    code = JL_BF16 if dtype == torch.bfloat16 else JL_FP32
+    _check("jl_prefill_tile_shape", lib().jl_prefill_tile_shape(code, d, ctypes.byref(bm),
+                                                                ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def prefill_workspace_size(T, B, Hq, Hkv, d, dtype=torch.bfloat16, mode="fused") -> int:
+    code = JL_BF16 if dtype == torch.bfloat16 else JL_FP32
+    n = lib().jl_prefill_workspace_size(int(T), int(B), int(Hq), int(Hkv), int(d), code,
+                                        MODES[mode])
+    if n == 0 and T > 0:
+        raise ValueError("invalid prefill shape")
+    return int(n)
+
+
+def decode_workspace_size(capacity, Hq, d) -> int:
+    return int(lib().jl_decode_workspace_size(int(capacity), int(Hq), int(d)))
+
+
+# ---------------------------------------------------------------- device calls
+def rope_apply(x: torch.Tensor, theta: float, cu_seqlens: Optional[torch.Tensor] = None,
+               pos_offset: int = 0) -> torch.Tensor:
+    """In place: x[t, h, :] <- RoPE(x[t, h, :], position of t). x: [T, H, d]."""
+    T, H, d = x.shape
+    B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    st = lib().jl_rope_apply(_dev(x, "x"), T, H, d, _dev(cu_seqlens, "cu_seqlens"), B,
+                             int(pos_offset), float(theta), _dtype_code(x), _stream(x.device))
+    _check("jl_rope_apply", st)
+    return x
+
+
+def bifocal_prefill(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, w0: int, w_pre: int,
+                    theta: float, scale: float = 0.0, mode: str = "fused",
+                    cu_seqlens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, kcache_out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """Causal bifocal attention; xq/xk/v are RAW [T, H, d]. Returns (o, lse)."""
+    T, Hq, d = xq.shape
+    Hkv = xk.shape[1]
+    B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty_like(xq)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=xq.device)
+    need = prefill_workspace_size(T, B, Hq, Hkv, d, xq.dtype, mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
+    st = lib().jl_bifocal_prefill(
+        _dev(xq, "xq"), _dev(xk, "xk"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
+        _dev(kcache_out, "kcache_out"), _dev(cu_seqlens, "cu_seqlens"), B, T, Hq, Hkv, d,
+        int(w0), int(w_pre), float(theta), float(scale), _dtype_code(xq), MODES[mode],
+        _dev(workspace, "workspace"), workspace.numel(), _stream(xq.device))
+    _check("jl_bifocal_prefill", st)
+    return out, lse
+
+
+def ie_ratio_view(workspace: torch.Tensor, T, B, Hq, Hkv, d, dtype=torch.bfloat16):
+    """[Hq, T] float32 view of the Eq. 7 cancellation ratios an IE prefill left
+    in `workspace`."""
+    code = JL_BF16 if dtype == torch.bfloat16 else JL_FP32
+    off = int(lib().jl_prefill_ie_ratio_offset(T, B, Hq, Hkv, d, code))
+    return workspace[off: off + Hq * T * 4].view(torch.float32).view(Hq, T)
+
+
+def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, pos: int,
+                   w0: int, w_pre: int, theta: float, scale: float = 0.0, mode: str = "fused",
+                   num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   want_lse: bool = True):
+    """One decode step at `pos` with a RAW query xq [Hq, d] against the absolute
+    cache [capacity, Hkv, d]. Returns (o [Hq, d], lse [Hq])."""
+    Hq, d = xq.shape
+    C, Hkv, _ = kcache.shape
+    if out is None:
+        out = torch.empty_like(xq)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq,), dtype=torch.float32, device=xq.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_size(C, Hq, d), dtype=torch.uint8,
+                                device=xq.device)
+    st = lib().jl_bifocal_decode(
+        _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
+        _dev(lse, "lse"), int(pos), C, Hq, Hkv, d, int(w0), int(w_pre), float(theta),
+        float(scale), _dtype_code(xq), MODES[mode], int(num_splits), _dev(workspace, "workspace"),
+        workspace.numel(), _stream(xq.device))
+    _check("jl_bifocal_decode", st)
+    return out, lse
+
+
+def debug_tile_classes(L: int, w0: int, device="cuda") -> torch.Tensor:
+    """Device-side tile classes of a length-L sequence, [ceil(L/BM), ceil(L/BN)] int8."""
+    bm, bn = prefill_tile_shape(torch.bfloat16, 128)
+    out = torch.empty(((L + bm - 1) // bm, (L + bn - 1) // bn), dtype=torch.int8, device=device)
+    _check("jl_debug_tile_classes", lib().jl_debug_tile_classes(int(L), int(w0), _dev(out, "out"),
+                                                                _stream(out.device)))
+    return out

@@ -1,0 +1,258 @@
+// C ABI of libbifocal: argument validation, workspace layout and dispatch.
+// Every check runs on the host before any launch (see include/bifocal.h).
+#include "../../include/bifocal.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "jl_internal.hpp"
+
+namespace jl {
+
+static thread_local int g_last_hip_error = 0;
+
+static int hip_status(hipError_t e) {
+  if (e == hipSuccess) return JL_OK;
+  g_last_hip_error = (int)e;
+  return JL_EHIP;
+}
+
+void make_freqs(RopeFreqs& f, int d, double theta) { f.nl2t = -2.0 * log2(theta) / (double)d; }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+PrefillLayout prefill_layout(int64_t T, int B, int Hq, int Hkv, int d, int dtype, int mode) {
+  PrefillLayout L{};
+  const int bm = dtype == JL_BF16 ? PF_BM : PF32_BM;
+  // Every sequence starts on a 64-row boundary of the padded key layout.
+  L.R = ((T + 63) / 64) * 64 + 64 * (int64_t)B;
+  L.max_tiles = (T + bm - 1) / bm + B;
+  const size_t elem = dtype == JL_BF16 ? 2 : 4;
+  size_t off = 0;
+  L.hdr = off;   off += 256;
+  L.seqs = off;  off += align256((size_t)B * sizeof(SeqInfo));
+  // tile schedule: sorted sequence order [B], per-depth active counts and
+  // bases [max_tiles + 1] each (see the plan kernel).
+  L.tiles = off; off += align256(((size_t)B + 2 * ((size_t)L.max_tiles + 1)) * sizeof(int));
+  L.kabs = off;  off += align256((size_t)Hkv * L.R * d * elem);
+  if (mode == JL_MODE_PLAIN) {
+    L.krem = L.kabs;
+  } else {
+    L.krem = off; off += align256((size_t)Hkv * L.R * d * elem);
+  }
+  if (dtype == JL_BF16) {
+    L.vt = off; off += align256((size_t)Hkv * L.R * d * 2);
+  } else {
+    L.vt = L.kabs;
+  }
+  L.ie_o = L.ie_lse = L.ie_ratio = off;
+  if (mode == JL_MODE_IE) {
+    L.ie_o = off;     off += align256(3 * (size_t)T * Hq * d * 4);
+    L.ie_lse = off;   off += align256(3 * (size_t)T * Hq * 4);
+    L.ie_ratio = off; off += align256((size_t)T * Hq * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace jl
+
+using namespace jl;
+
+extern "C" {
+
+int64_t jl_group_size(int64_t L, int64_t w_pre) {
+  if (L < 1 || w_pre < 1) return JL_EINVAL;
+  return jl::group_size(L, w_pre);
+}
+
+int jl_tile_class(int64_t q0, int64_t q1, int64_t k0, int64_t k1, int64_t w0) {
+  if (q0 < 0 || k0 < 0 || q1 < q0 || k1 < k0 || w0 < 0) return JL_EINVAL;
+  return jl::tile_class(q0, q1, k0, k1, w0);
+}
+
+int jl_prefill_tile_shape(jl_dtype dt, int d, int* bm, int* bn) {
+  if (!bm || !bn) return JL_EINVAL;
+  if (dt == JL_BF16 && d == PF_D) {
+    *bm = PF_BM;
+    *bn = PF_BN;
+    return JL_OK;
+  }
+  if (dt == JL_FP32 && (d == 64 || d == 128)) {
+    *bm = PF32_BM;
+    *bn = PF32_BN;
+    return JL_OK;
+  }
+  return JL_EUNSUPPORTED;
+}
+
+int jl_rope_apply(void* x, int64_t T, int H, int d, const int32_t* cu_seqlens, int B,
+                  int64_t pos_offset, double theta, jl_dtype dt, void* stream) {
+  if (T < 0 || H < 1 || d < 2 || d > 256 || (d & 1) || pos_offset < 0 || !(theta > 1.0))
+    return JL_EINVAL;
+  if (dt != JL_BF16 && dt != JL_FP32) return JL_EINVAL;
+  if (d % 16) return JL_EUNSUPPORTED;
+  if (cu_seqlens && B < 1) return JL_EINVAL;
+  if (T == 0) return JL_OK;
+  if (!x) return JL_EINVAL;
+  if (T > (int64_t)INT32_MAX || (double)T * H * d > 9.0e15) return JL_EINVAL;
+  RopeFreqs fr;
+  make_freqs(fr, d, theta);
+  return hip_status(launch_rope_apply(x, T, H, d, cu_seqlens, cu_seqlens ? B : 1, pos_offset, fr,
+                                      dt == JL_FP32, (hipStream_t)stream));
+}
+
+static bool prefill_shape_ok(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt, jl_mode mode) {
+  if (T < 0 || B < 1 || B > 4096 || Hq < 1 || Hkv < 1 || Hq % Hkv) return false;
+  if (T > (int64_t)INT32_MAX / 2) return false;
+  if (dt != JL_BF16 && dt != JL_FP32) return false;
+  if (mode != JL_MODE_FUSED && mode != JL_MODE_IE && mode != JL_MODE_PLAIN) return false;
+  (void)d;
+  return true;
+}
+
+size_t jl_prefill_workspace_size(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt,
+                                 jl_mode mode) {
+  if (!prefill_shape_ok(T, B, Hq, Hkv, d, dt, mode)) return 0;
+  return prefill_layout(T, B, Hq, Hkv, d, dt, mode).total;
+}
+
+size_t jl_prefill_ie_ratio_offset(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt) {
+  if (!prefill_shape_ok(T, B, Hq, Hkv, d, dt, JL_MODE_IE)) return 0;
+  return prefill_layout(T, B, Hq, Hkv, d, dt, JL_MODE_IE).ie_ratio;
+}
+
+int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, float* lse,
+                       void* kcache_out, const int32_t* cu_seqlens, int B, int64_t T, int Hq,
+                       int Hkv, int d, int64_t w0, int64_t w_pre, double theta, float scale,
+                       jl_dtype dt, jl_mode mode, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  if (!cu_seqlens && B != 1) return JL_EINVAL;
+  if (!prefill_shape_ok(T, B, Hq, Hkv, d, dt, mode)) return JL_EINVAL;
+  if (w0 < 0 || w_pre < 1 || !(theta > 1.0) || !(scale == scale)) return JL_EINVAL;
+  if (w0 > (int64_t)INT32_MAX) w0 = INT32_MAX;  // every pair of a 32-bit sequence is local
+  if (dt == JL_BF16 && d != PF_D) return JL_EUNSUPPORTED;
+  if (dt == JL_FP32 && d != 64 && d != 128) return JL_EUNSUPPORTED;
+  if (T == 0) return JL_OK;
+  if (!xq || !xk || !v || !o) return JL_EINVAL;
+  const PrefillLayout lay = prefill_layout(T, B, Hq, Hkv, d, dt, mode);
+  if (!workspace || ws_bytes < lay.total) return JL_EWORKSPACE;
+  if (((uintptr_t)workspace) & 255) return JL_EINVAL;
+  const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d));
+  RopeFreqs fr;
+  make_freqs(fr, d, theta);
+  hipStream_t st = (hipStream_t)stream;
+  const int bm = dt == JL_BF16 ? PF_BM : PF32_BM;
+  hipError_t e = launch_prefill_plan(cu_seqlens, B, T, w_pre, bm, workspace, lay, st);
+  if (e != hipSuccess) return hip_status(e);
+  const int need_rem = mode != JL_MODE_PLAIN;
+  if (dt == JL_BF16) {
+    e = launch_prefill_prep_bf16(xk, v, kcache_out, T, B, Hkv, need_rem, fr, workspace, lay, st);
+    if (e != hipSuccess) return hip_status(e);
+    if (mode == JL_MODE_IE) {
+      float* base_o = (float*)((char*)workspace + lay.ie_o);
+      float* base_l = (float*)((char*)workspace + lay.ie_lse);
+      const size_t on = (size_t)T * Hq * d, ln = (size_t)T * Hq;
+      const int passes[3] = {PASS_IE_A, PASS_IE_B, PASS_IE_C};
+      for (int i = 0; i < 3; ++i) {
+        e = launch_prefill_bf16(passes[i], xq, base_o + i * on, base_l + i * ln, T, B, Hq, Hkv,
+                                w0, sc, fr, workspace, lay, st);
+        if (e != hipSuccess) return hip_status(e);
+      }
+      e = launch_ie_merge(o, lse, 0, T, Hq, d, workspace, lay, st);
+    } else {
+      e = launch_prefill_bf16(mode == JL_MODE_PLAIN ? PASS_PLAIN : PASS_FUSED, xq, o, lse, T, B,
+                              Hq, Hkv, w0, sc, fr, workspace, lay, st);
+    }
+  } else {
+    e = launch_prefill_prep_f32(xk, kcache_out, T, B, Hkv, d, need_rem, fr, workspace, lay, st);
+    if (e != hipSuccess) return hip_status(e);
+    if (mode == JL_MODE_IE) {
+      float* base_o = (float*)((char*)workspace + lay.ie_o);
+      float* base_l = (float*)((char*)workspace + lay.ie_lse);
+      const size_t on = (size_t)T * Hq * d, ln = (size_t)T * Hq;
+      const int passes[3] = {PASS_IE_A, PASS_IE_B, PASS_IE_C};
+      for (int i = 0; i < 3; ++i) {
+        e = launch_prefill_f32(passes[i], xq, v, base_o + i * on, base_l + i * ln, T, B, Hq, Hkv,
+                               d, w0, sc, fr, workspace, lay, st);
+        if (e != hipSuccess) return hip_status(e);
+      }
+      e = launch_ie_merge(o, lse, 1, T, Hq, d, workspace, lay, st);
+    } else {
+      e = launch_prefill_f32(mode == JL_MODE_PLAIN ? PASS_PLAIN : PASS_FUSED, xq, v, o, lse, T, B,
+                             Hq, Hkv, d, w0, sc, fr, workspace, lay, st);
+    }
+  }
+  return hip_status(e);
+}
+
+static int decode_max_splits(int64_t capacity) {
+  int64_t s = (capacity + 63) / 64;
+  return (int)(s < 1024 ? s : 1024);
+}
+
+size_t jl_decode_workspace_size(int64_t capacity, int Hq, int d) {
+  if (capacity < 1 || Hq < 1 || d < 2) return 0;
+  return align256((size_t)Hq * decode_max_splits(capacity) * (d + 2) * sizeof(float));
+}
+
+int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, void* o, float* lse,
+                      int64_t pos, int64_t capacity, int Hq, int Hkv, int d, int64_t w0,
+                      int64_t w_pre, double theta, float scale, jl_dtype dt, jl_mode mode,
+                      int num_splits, void* workspace, size_t ws_bytes, void* stream) {
+  if (pos < 0 || capacity < 1 || pos >= capacity || capacity > (int64_t)INT32_MAX) return JL_EINVAL;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 0 || w_pre < 1 || !(theta > 1.0)) return JL_EINVAL;
+  if (num_splits < 0 || !(scale == scale)) return JL_EINVAL;
+  if (dt != JL_BF16 && dt != JL_FP32) return JL_EINVAL;
+  if (mode == JL_MODE_IE) return JL_EUNSUPPORTED;
+  if (mode != JL_MODE_FUSED && mode != JL_MODE_PLAIN) return JL_EINVAL;
+  if (d != 128 && d != 64) return JL_EUNSUPPORTED;
+  {
+    const int r = Hq / Hkv;
+    if (r != 1 && r != 2 && r != 4 && r != 8) return JL_EUNSUPPORTED;
+  }
+  if (!xq || !kcache || !vcache || !o) return JL_EINVAL;
+  const int maxs = decode_max_splits(capacity);
+  const int64_t keys = pos + 1;
+  int S = num_splits;
+  if (S == 0) {
+    // ~4 workgroups per CU over the KV heads, at least 64 keys per split.
+    int64_t want = (1024 + Hkv - 1) / Hkv;
+    int64_t by_keys = (keys + 63) / 64;
+    S = (int)(want < by_keys ? want : by_keys);
+  }
+  if (S < 1) S = 1;
+  if (S > maxs) return JL_EINVAL;
+  if ((int64_t)S > keys) S = (int)keys;
+  const size_t need = (size_t)Hq * S * (d + 2) * sizeof(float);
+  if (!workspace || ws_bytes < need) return JL_EWORKSPACE;
+  if (((uintptr_t)workspace) & 15) return JL_EINVAL;
+  const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d));
+  RopeFreqs fr;
+  make_freqs(fr, d, theta);
+  const int64_t G = jl::group_size(pos + 1, w_pre);
+  return hip_status(launch_decode(xq, kcache, vcache, o, lse, pos, Hq, Hkv, d,
+                                  w0 > (int64_t)INT32_MAX ? INT32_MAX : w0, G, sc, fr,
+                                  mode == JL_MODE_PLAIN, dt == JL_FP32, S, workspace,
+                                  (hipStream_t)stream));
+}
+
+int jl_debug_tile_classes(int64_t L, int64_t w0, int8_t* out_dev, void* stream) {
+  if (L < 1 || L > (int64_t)1 << 24 || w0 < 0 || !out_dev) return JL_EINVAL;
+  return hip_status(launch_tile_dump(L, w0, out_dev, (hipStream_t)stream));
+}
+
+const char* jl_status_string(int status) {
+  switch (status) {
+    case JL_OK: return "ok";
+    case JL_EINVAL: return "invalid argument";
+    case JL_EUNSUPPORTED: return "unsupported head dim, dtype or mode";
+    case JL_EHIP: return "HIP runtime or launch error";
+    case JL_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int jl_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Internal declarations shared by the libbifocal sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jl {
+
+// ---------------------------------------------------------------------------
+// Tile classification from the routing condition of Eq. 1 (r9-hu digest,
+// Method). Distance-only: the class never depends on G.
+//   0 masked, 1 local, 2 remote, 3 boundary; +4 when the diagonal crosses.
+// ---------------------------------------------------------------------------
+enum TileClass : int { TC_MASKED = 0, TC_LOCAL = 1, TC_REMOTE = 2, TC_BOUNDARY = 3, TC_DIAG = 4 };
+
+__host__ __device__ inline int tile_class(int64_t q0, int64_t q1, int64_t k0, int64_t k1,
+                                          int64_t w0) {
+  if (k0 > q1) return TC_MASKED;
+  int c;
+  if (q1 - k0 <= w0) c = TC_LOCAL;        // largest causal distance inside the window
+  else if (q0 - k1 > w0) c = TC_REMOTE;   // smallest distance outside it
+  else c = TC_BOUNDARY;
+  if (k1 > q0) c += TC_DIAG;              // some pair has k > q
+  return c;
+}
+
+// Eq. 2 in integer arithmetic.
+__host__ __device__ inline int64_t group_size(int64_t L, int64_t w_pre) {
+  int64_t g = (L + w_pre - 1) / w_pre;
+  return g < 1 ? 1 : g;
+}
+
+// Rotary frequencies omega_i = theta^(-2i/d) = 2^(i * (-2 log2(theta) / d)),
+// evaluated in float64 where they are used (one scalar travels in the kernel
+// arguments instead of a table that lanes would index).
+struct RopeFreqs {
+  double nl2t;  // -2 * log2(theta) / d
+  __host__ __device__ double w(int i) const { return exp2((double)i * nl2t); }
+};
+void make_freqs(RopeFreqs& f, int d, double theta);
+
+// Per-sequence record built on the device by the plan kernel.
+struct SeqInfo {
+  int start;    // first token (row of the packed [T, H, d] tensors)
+  int len;      // tokens in the sequence
+  int G;        // Eq. 2 group size from this sequence's length
+  int pad_off;  // first row of this sequence in the 64-row padded workspace layout
+};
+
+// Prefill tile shapes of the bf16 MFMA kernel.
+constexpr int PF_BM = 128;   // query rows per workgroup (4 waves x 32)
+constexpr int PF_BN = 64;    // keys per tile
+constexpr int PF_D = 128;    // head dim
+// fp32 VALU kernel.
+constexpr int PF32_BM = 64;
+constexpr int PF32_BN = 32;
+
+enum Pass : int { PASS_FUSED = 0, PASS_PLAIN = 1, PASS_IE_A = 2, PASS_IE_B = 3, PASS_IE_C = 4 };
+
+// Workspace carving shared by the API and the kernels' launchers.
+struct PrefillLayout {
+  size_t hdr, seqs, tiles, kabs, krem, vt, ie_o, ie_lse, ie_ratio, total;
+  int64_t R;          // padded rows per KV head
+  int64_t max_tiles;  // upper bound on query tiles
+};
+PrefillLayout prefill_layout(int64_t T, int B, int Hq, int Hkv, int d, int dtype, int mode);
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipError_t of the launch).
+// ---------------------------------------------------------------------------
+hipError_t launch_rope_apply(void* x, int64_t T, int H, int d, const int32_t* cu, int B,
+                             int64_t pos_offset, const RopeFreqs& fr, int is_f32,
+                             hipStream_t st);
+
+hipError_t launch_prefill_plan(const int32_t* cu, int B, int64_t T, int64_t w_pre, int bm,
+                               void* ws, const PrefillLayout& lay, hipStream_t st);
+
+hipError_t launch_prefill_prep_bf16(const void* xk, const void* v, void* kcache_out, int64_t T,
+                                    int B, int Hkv, int need_rem, const RopeFreqs& fr, void* ws,
+                                    const PrefillLayout& lay, hipStream_t st);
+
+hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, int64_t T, int B,
+                               int Hq, int Hkv, int64_t w0, float scale, const RopeFreqs& fr,
+                               void* ws, const PrefillLayout& lay, hipStream_t st);
+
+hipError_t launch_prefill_prep_f32(const void* xk, void* kcache_out, int64_t T, int B, int Hkv,
+                                   int d, int need_rem, const RopeFreqs& fr, void* ws,
+                                   const PrefillLayout& lay, hipStream_t st);
+
+hipError_t launch_prefill_f32(int pass, const void* xq, const void* v, void* o, float* lse,
+                              int64_t T, int B, int Hq, int Hkv, int d, int64_t w0, float scale,
+                              const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
+                              hipStream_t st);
+
+hipError_t launch_ie_merge(void* o, float* lse, int out_f32, int64_t T, int Hq, int d, void* ws,
+                           const PrefillLayout& lay, hipStream_t st);
+
+hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
+                         int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
+                         const RopeFreqs& fr, int plain, int is_f32, int num_splits, void* ws,
+                         hipStream_t st);
+
+hipError_t launch_tile_dump(int64_t L, int64_t w0, int8_t* out, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+#ifdef __HIPCC__
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+
+// cos/sin of p * w: the product and its reduction modulo 2*pi are done in
+// float64 (|p*w| reaches ~1.3e5 rad at 128K positions, where a float32
+// product alone would be off by ~1e-2 rad); sin/cos of the reduced angle in
+// float32.
+__device__ inline void rope_cs(double p, double w, float& c, float& s) {
+  double a = p * w;
+  double n = __builtin_rint(a * kInvTwoPi);
+  double r = __builtin_fma(-n, kTwoPi, a);
+  sincosf((float)r, &s, &c);
+}
+
+// Same rotation with the angle in turns: t = p * (w / 2pi) is formed and
+// reduced to [-1/2, 1/2] in float64, then the hardware sine and cosine (which
+// take turns) finish it in float32. For paths whose operands are rounded to
+// 16-bit floats. w2pi = w / (2 pi).
+__device__ inline void rope_cs_turns(double p, double w2pi, float& c, float& s) {
+  const double t = p * w2pi;
+  const float f = (float)(t - __builtin_rint(t));
+  s = __builtin_amdgcn_sinf(f);
+  c = __builtin_amdgcn_cosf(f);
+}
+
+__device__ inline float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ inline uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ inline uint16_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)x;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+#endif
+
+}  // namespace jl

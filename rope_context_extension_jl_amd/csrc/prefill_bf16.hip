@@ -1,0 +1,662 @@
+// Bifocal prefill for bf16 I/O on gfx950: plan, key/value pre-pass, fused
+// MFMA attention pass, device tile-class dump.
+//
+// Method (r9-hu digest of Jet-Long, section Method): Eq. 1 routes each
+// query/key pair by distance -- q - k <= w0 scores the vectors rotated at
+// (q, k), otherwise at (f(q), f(k)) with f(x) = floor(x / G) and
+// G = max(1, ceil(L / w_pretrained)) per sequence ("Dynamic group size").
+//
+// Design:
+//   * The pre-pass rotates every raw key ONCE to its absolute and its
+//     remapped position (fp32 arithmetic, float64-reduced angles) and stores
+//     both as fp16 tiles in the workspace, head-major and padded so every
+//     sequence starts on a 64-row boundary. It also writes V transposed
+//     (d-major) so the PV product can read 16-byte MFMA operands, and
+//     optionally the bf16 absolute key cache.
+//   * The attention kernel gives each workgroup (4 waves, 256 threads) 128
+//     query rows of one query head. Each lane of a wave owns ONE query row:
+//     scores are computed transposed, S^T = K Q^T, so the 32x32 MFMA output
+//     puts a row's scores in one lane (plus its partner lane l^32) and the
+//     row max / row sum need a single cross-lane exchange.
+//   * Every 64-key tile is classified (local / remote / boundary, plus the
+//     causal diagonal) from distances only. Local tiles use the absolute
+//     operands, remote tiles the remapped ones, boundary tiles compute both
+//     products and select per element; only boundary tiles (a few tenths of
+//     a percent at 64K-128K) pay for the second product.
+//   * QK^T uses fp16 operands (the rotated vectors keep the raw norm, so the
+//     fp16 range holds them, and fp16 carries 3 more mantissa bits than bf16
+//     at the same MFMA rate); PV uses bf16 P and the raw bf16 V. Accumulation
+//     is fp32 throughout; O is rounded to bf16 once.
+//   * The schedule hands the heaviest query tiles out first (longest causal
+//     key range), and consecutive workgroups of one XCD share a KV head so
+//     the key tiles they stream stay in that XCD's L2.
+#include "jl_internal.hpp"
+
+namespace jl {
+
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef __bf16 b8v __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int KS = PF_D + 8;   // LDS row stride (elements) of a key tile: 272 B, conflict-free b128 reads
+constexpr int VS = PF_BN + 8;  // LDS row stride of a transposed value tile: 144 B
+
+// ---------------------------------------------------------------------------
+// Plan: per-sequence records and the heaviest-first tile order.
+//   seqs[b]   = {start, len, G, pad_off}
+//   order[rho]: sequences sorted by query-tile count, descending (ties by b)
+//   tact[t]   = number of sequences with more than t query tiles
+//   tbase[t]  = sum of tact[t'] over t' > t
+// Slot s of the schedule is tile depth t (smallest t with tbase[t] <= s) of
+// sequence order[s - tbase[t]]: deepest (heaviest) tiles first.
+// hdr[0] = number of tiles, hdr[1] = deepest tile count, hdr[2] = padded rows.
+// ---------------------------------------------------------------------------
+constexpr int PLAN_THREADS = 1024;
+
+__device__ inline int block_excl_scan(int v, int* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
+    int add = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  int incl = sh[tid];
+  int total = sh[PLAN_THREADS - 1];
+  __syncthreads();
+  sh[PLAN_THREADS] = total;
+  return incl - v;
+}
+
+__global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(
+    const int32_t* __restrict__ cu, int B, int T, int64_t w_pre, int bm, int* __restrict__ hdr,
+    SeqInfo* __restrict__ seqs, int* __restrict__ order, int* __restrict__ tact,
+    int* __restrict__ tbase) {
+  // Every value one thread produces for another goes through LDS (B <= 4096).
+  __shared__ int nt_s[4096];
+  __shared__ int len_s[4096];
+  __shared__ int ord_s[4096];
+  __shared__ int sh[PLAN_THREADS + 1];
+  __shared__ int maxnt_s;
+  const int tid = threadIdx.x;
+  if (tid == 0) maxnt_s = 0;
+  __syncthreads();
+  for (int b = tid; b < B; b += PLAN_THREADS) {
+    const int s = cu ? cu[b] : 0;
+    const int e = cu ? cu[b + 1] : T;
+    const int len = e > s ? e - s : 0;
+    len_s[b] = len;
+    nt_s[b] = (len + bm - 1) / bm;
+    atomicMax(&maxnt_s, nt_s[b]);
+    seqs[b].start = s;
+    seqs[b].len = len;
+    seqs[b].G = (int)group_size(len > 0 ? len : 1, w_pre);
+  }
+  __syncthreads();
+  // pad_off: exclusive prefix sum of the 64-rounded lengths, `per` per thread
+  {
+    const int per = (B + PLAN_THREADS - 1) / PLAN_THREADS;
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+      const int b = tid * per + i;
+      if (b < B) local += (len_s[b] + 63) & ~63;
+    }
+    int run = block_excl_scan(local, sh);
+    if (tid == 0) hdr[2] = sh[PLAN_THREADS];
+    for (int i = 0; i < per; ++i) {
+      const int b = tid * per + i;
+      if (b < B) {
+        seqs[b].pad_off = run;
+        run += (len_s[b] + 63) & ~63;
+      }
+    }
+  }
+  // stable rank by tile count, descending
+  for (int b = tid; b < B; b += PLAN_THREADS) {
+    int rank = 0;
+    const int nb = nt_s[b];
+    for (int c = 0; c < B; ++c) rank += (nt_s[c] > nb) || (nt_s[c] == nb && c < b);
+    ord_s[rank] = b;
+  }
+  __syncthreads();
+  for (int i = tid; i < B; i += PLAN_THREADS) order[i] = ord_s[i];
+  const int maxnt = maxnt_s;
+  // tact[t] = #{rho : nt[order[rho]] > t} (sorted counts are non-increasing);
+  // tbase[t] = sum of tact[t'] over t' > t, scanned in order of decreasing t.
+  int carry = 0;
+  for (int c0 = 0; c0 < maxnt; c0 += PLAN_THREADS) {
+    const int u = c0 + tid;
+    const int t = maxnt - 1 - u;
+    int act = 0;
+    if (u < maxnt) {
+      int lo = 0, hi = B;  // first rho with nt <= t
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (nt_s[ord_s[mid]] > t) lo = mid + 1; else hi = mid;
+      }
+      act = lo;
+    }
+    const int ex = block_excl_scan(act, sh);
+    if (u < maxnt) {
+      tact[t] = act;
+      tbase[t] = carry + ex;
+    }
+    carry += sh[PLAN_THREADS];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    hdr[0] = carry;  // total tiles
+    hdr[1] = maxnt;
+  }
+}
+
+hipError_t launch_prefill_plan(const int32_t* cu, int B, int64_t T, int64_t w_pre, int bm,
+                               void* ws, const PrefillLayout& lay, hipStream_t st) {
+  char* w = (char*)ws;
+  int* order = (int*)(w + lay.tiles);
+  int* tact = order + B;
+  int* tbase = tact + (lay.max_tiles + 1);
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, cu, B, (int)T,
+                     w_pre, bm, (int*)(w + lay.hdr), (SeqInfo*)(w + lay.seqs), order, tact, tbase);
+  return hipGetLastError();
+}
+
+__device__ inline int seq_of_padded_row(const SeqInfo* seqs, int B, int r) {
+  int lo = 0, hi = B - 1;  // largest b with pad_off <= r
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (seqs[mid].pad_off <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Pre-pass: 64 padded rows per workgroup (rows of one sequence, or padding).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
+    const uint16_t* __restrict__ xk, const uint16_t* __restrict__ v, uint16_t* __restrict__ kcache,
+    const SeqInfo* __restrict__ seqs, const int* __restrict__ hdr, int B, int Hkv, int R,
+    int need_rem, uint16_t* __restrict__ kabs, uint16_t* __restrict__ krem,
+    uint16_t* __restrict__ vt, RopeFreqs fr) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * (PF_D + 8)];
+  const int r0 = blockIdx.x * 64;
+  if (r0 >= hdr[2]) return;
+  const int b = seq_of_padded_row(seqs, B, r0);
+  const SeqInfo sq = seqs[b];
+  const int tid = threadIdx.x;
+  // keys: thread = (row, pair group of 8); two passes of 32 rows
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = pass * 32 + (tid >> 3);
+    const int c = tid & 7;
+    const int r = r0 + i;
+    const int trel = r - sq.pad_off;
+    const bool valid = trel < sq.len;
+    float ca[8], sa[8], cr[8], sr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      rope_cs((double)trel, fr.w(8 * c + j), ca[j], sa[j]);
+      if (need_rem) rope_cs((double)(trel / sq.G), fr.w(8 * c + j), cr[j], sr[j]);
+    }
+    for (int g = 0; g < Hkv; ++g) {
+      uint4 av = make_uint4(0, 0, 0, 0), bv = av;
+      if (valid) {
+        const uint16_t* src = xk + ((int64_t)(sq.start + trel) * Hkv + g) * PF_D;
+        av = *(const uint4*)(src + 8 * c);
+        bv = *(const uint4*)(src + 64 + 8 * c);
+      }
+      const uint16_t* ap = (const uint16_t*)&av;
+      const uint16_t* bp = (const uint16_t*)&bv;
+      uint16_t oa[8], ob[8], ra[8], rb[8], ka[8], kb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x0 = bf16_bits_to_f32(ap[j]), x1 = bf16_bits_to_f32(bp[j]);
+        const float y0 = x0 * ca[j] - x1 * sa[j], y1 = x0 * sa[j] + x1 * ca[j];
+        oa[j] = f32_to_f16_bits(y0);
+        ob[j] = f32_to_f16_bits(y1);
+        ka[j] = f32_to_bf16_bits(y0);
+        kb[j] = f32_to_bf16_bits(y1);
+        if (need_rem) {
+          ra[j] = f32_to_f16_bits(x0 * cr[j] - x1 * sr[j]);
+          rb[j] = f32_to_f16_bits(x0 * sr[j] + x1 * cr[j]);
+        }
+      }
+      uint16_t* da = kabs + ((int64_t)g * R + r) * PF_D;
+      *(uint4*)(da + 8 * c) = *(const uint4*)oa;
+      *(uint4*)(da + 64 + 8 * c) = *(const uint4*)ob;
+      if (need_rem) {
+        uint16_t* dr = krem + ((int64_t)g * R + r) * PF_D;
+        *(uint4*)(dr + 8 * c) = *(const uint4*)ra;
+        *(uint4*)(dr + 64 + 8 * c) = *(const uint4*)rb;
+      }
+      if (kcache && valid) {
+        uint16_t* dc = kcache + ((int64_t)(sq.start + trel) * Hkv + g) * PF_D;
+        *(uint4*)(dc + 8 * c) = *(const uint4*)ka;
+        *(uint4*)(dc + 64 + 8 * c) = *(const uint4*)kb;
+      }
+    }
+  }
+  // values: transpose 64 rows x 128 per KV head through LDS
+  for (int g = 0; g < Hkv; ++g) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = (tid >> 4) + 16 * k, c = tid & 15;
+      const int trel = r0 + i - sq.pad_off;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (trel < sq.len) val = *(const uint4*)(v + ((int64_t)(sq.start + trel) * Hkv + g) * PF_D + 8 * c);
+      *(uint4*)(tile + i * (PF_D + 8) + 8 * c) = val;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int dd = (tid >> 3) + 32 * k, kc = tid & 7;
+      uint16_t out[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = tile[(8 * kc + e) * (PF_D + 8) + dd];
+      *(uint4*)(vt + ((int64_t)g * PF_D + dd) * R + r0 + 8 * kc) = *(const uint4*)out;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_prefill_prep_bf16(const void* xk, const void* v, void* kcache_out, int64_t T,
+                                    int B, int Hkv, int need_rem, const RopeFreqs& fr, void* ws,
+                                    const PrefillLayout& lay, hipStream_t st) {
+  char* w = (char*)ws;
+  const int blocks = (int)(lay.R / 64);
+  hipLaunchKernelGGL(prefill_prep_bf16_kernel, dim3(blocks), dim3(256), 0, st,
+                     (const uint16_t*)xk, (const uint16_t*)v, (uint16_t*)kcache_out,
+                     (const SeqInfo*)(w + lay.seqs), (const int*)(w + lay.hdr), B, Hkv,
+                     (int)lay.R, need_rem, (uint16_t*)(w + lay.kabs), (uint16_t*)(w + lay.krem),
+                     (uint16_t*)(w + lay.vt), fr);
+  (void)T;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Attention pass.
+// ---------------------------------------------------------------------------
+struct PfArgs {
+  const uint16_t* xq;    // raw bf16 [T, Hq, D]
+  const uint16_t* kabs;  // fp16 [Hkv, R, D]
+  const uint16_t* krem;  // fp16 [Hkv, R, D]
+  const uint16_t* vt;    // bf16 [Hkv, D, R]
+  void* o;               // bf16 [T, Hq, D] (fp32 for the inclusion-exclusion passes)
+  float* lse;            // [Hq, T] or null
+  const SeqInfo* seqs;
+  const int* hdr;
+  const int* order;
+  const int* tact;
+  const int* tbase;
+  int T, R, Hq, Hkv, w0;
+  float scale_log2;
+  RopeFreqs fr;
+};
+
+__device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Phases of the key loop. Key tiles come in distance order: all-remote tiles
+// first, then the few boundary tiles, then local / diagonal tiles, so only
+// one rotated query operand is live outside the boundary phase.
+enum Phase : int { PH_REMOTE = 0, PH_BOUNDARY = 1, PH_LOCAL = 2 };
+
+template <int PASS>
+__global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][PF_BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][PF_D * VS];
+  __shared__ double w2pi_s[PF_D / 2];  // omega_i / (2 pi)
+  if (threadIdx.x < PF_D / 2) w2pi_s[threadIdx.x] = a.fr.w(threadIdx.x) * kInvTwoPi;
+
+  // ---- work item: (schedule slot, query head); XCD-aware head grouping
+  int slot, head;
+  {
+    const int w = blockIdx.x;
+    if ((a.Hq & 7) == 0) {
+      const int hpx = a.Hq >> 3, k = w >> 3;
+      slot = k / hpx;
+      head = (w & 7) * hpx + k % hpx;
+    } else {
+      slot = w / a.Hq;
+      head = w % a.Hq;
+    }
+  }
+  if (slot >= a.hdr[0]) return;
+  int t;
+  {
+    int lo = 0, hi = a.hdr[1] - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.tbase[mid] <= slot) hi = mid; else lo = mid + 1;
+    }
+    t = lo;
+  }
+  const SeqInfo sq = a.seqs[a.order[slot - a.tbase[t]]];
+  const int g = head / (a.Hq / a.Hkv);
+  const int q0 = t * PF_BM;
+  const int q1 = min(q0 + PF_BM, sq.len) - 1;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int myq = q0 + wave * 32 + l32;
+  const bool qvalid = myq < sq.len;
+  constexpr bool kWindow = PASS == PASS_IE_A || PASS == PASS_IE_C;
+
+  // ---- rotated query operand: RoPE(x_q, p) for p = q or f(q), as fp16.
+  // The lane holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs
+  // (d, d+64) are (c, c+4), both in this lane.
+  auto rotate_q = [&](int p, h8v* out) {
+    __syncthreads();  // w2pi_s written (first call); harmless later
+    uint4 raw[8];
+    const uint16_t* qp = a.xq + ((int64_t)(sq.start + (qvalid ? myq : 0)) * a.Hq + head) * PF_D;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      raw[c] = qvalid ? *(const uint4*)(qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint16_t* x0p = (const uint16_t*)&raw[c];
+      const uint16_t* x1p = (const uint16_t*)&raw[c + 4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x0 = bf16_bits_to_f32(x0p[j]), x1 = bf16_bits_to_f32(x1p[j]);
+        float cs, sn;
+        rope_cs_turns((double)p, w2pi_s[16 * c + 8 * hh + j], cs, sn);
+        out[c][j] = (_Float16)(x0 * cs - x1 * sn);
+        out[c + 4][j] = (_Float16)(x0 * sn + x1 * cs);
+      }
+    }
+  };
+
+  // ---- key-tile ranges (distance only; the per-tile class is recomputed below)
+  const int nkt = q1 / PF_BN + 1;
+  // first tile that is not all-remote, first tile that is all-local
+  const int j_nr = q0 > a.w0 ? (q0 - a.w0) / PF_BN : 0;
+  const int j_loc = q1 > a.w0 ? min(nkt, (q1 - a.w0 + PF_BN - 1) / PF_BN) : 0;
+
+  const uint16_t* kabs_g = a.kabs + ((int64_t)g * a.R + sq.pad_off) * PF_D;
+  const uint16_t* krem_g = a.krem + ((int64_t)g * a.R + sq.pad_off) * PF_D;
+  const uint16_t* vt_g = a.vt + (int64_t)g * PF_D * a.R + sq.pad_off;
+
+  auto tile_cls = [&](int j) {
+    const int k0 = j * PF_BN;
+    return tile_class(q0, q1, k0, min(k0 + PF_BN, sq.len) - 1, a.w0);
+  };
+  // which rotation the LDS key tile j holds
+  auto k_source = [&](int j) -> const uint16_t* {
+    bool rem;
+    if (PASS == PASS_FUSED) rem = (tile_cls(j) & 3) == TC_REMOTE;
+    else rem = PASS == PASS_IE_B || PASS == PASS_IE_C;
+    return (rem ? krem_g : kabs_g) + (int64_t)j * PF_BN * PF_D;
+  };
+
+  uint4 kreg[4], vreg[4];
+  auto gload = [&](int j) {
+    const uint16_t* ks = k_source(j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 4) + 16 * i, ch = tid & 15;
+      kreg[i] = *(const uint4*)(ks + row * PF_D + 8 * ch);
+    }
+    const uint16_t* vs = vt_g + j * PF_BN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int dd = (tid >> 3) + 32 * i, ch = tid & 7;
+      vreg[i] = *(const uint4*)(vs + (int64_t)dd * a.R + 8 * ch);
+    }
+  };
+  auto lstore = [&](int stg) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 4) + 16 * i, ch = tid & 15;
+      *(uint4*)(&Ks[stg][row * KS + 8 * ch]) = kreg[i];
+    }
+    // key order inside each 16-key group is stored as {0-3, 8-11, 4-7, 12-15}
+    // so a lane half reads its 8 PV operand keys as one 16-byte vector.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int dd = (tid >> 3) + 32 * i, ch = tid & 7;
+      const int base = dd * VS + 16 * (ch >> 1) + 4 * (ch & 1);
+      *(uint2*)(&Vs[stg][base]) = make_uint2(vreg[i].x, vreg[i].y);
+      *(uint2*)(&Vs[stg][base + 8]) = make_uint2(vreg[i].z, vreg[i].w);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  // One key tile: S^T = K Q^T (two 32-key blocks), masks, online softmax,
+  // O^T += V^T P^T. `qop` is the query operand for the LDS key tile; on a
+  // boundary tile of the fused pass `qrem` scores the remapped keys read
+  // straight from global memory and each element takes the branch of Eq. 1.
+  auto tile_body = [&](int j, int stg, const h8v* qop, const h8v* qrem, bool boundary_select) {
+    const int k0 = j * PF_BN;
+    const int cls = tile_cls(j);
+    f32x16 s[2];
+    const uint16_t* kst = &Ks[stg][0];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[bk][r] = 0.f;
+      const uint16_t* krow = kst + (32 * bk + l32) * KS + 8 * hh;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * c), qop[c], s[bk],
+                                                       0, 0, 0);
+    }
+    if (boundary_select) {
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        f32x16 s2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s2[r] = 0.f;
+        const uint16_t* krow = krem_g + (int64_t)(k0 + 32 * bk + l32) * PF_D + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * c), qrem[c], s2,
+                                                      0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = k0 + 32 * bk + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (myq - kk > a.w0) s[bk][r] = s2[r];
+        }
+      }
+    }
+    // scale (log2 domain) and masks
+    const bool causal = (cls & TC_DIAG) || j == nkt - 1;
+    const bool window = kWindow && (cls & 3) == TC_BOUNDARY;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[bk][r] * a.scale_log2;
+        const int kk = k0 + 32 * bk + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (causal && kk > myq) x = -INFINITY;
+        if (window && myq - kk > a.w0) x = -INFINITY;
+        s[bk][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, xor32(mt));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+    b8v pb[4];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[bk][r] - m_use);
+        psum += p;
+        pb[2 * bk + (r >> 3)][r & 7] = (__bf16)p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+    const uint16_t* vst = &Vs[stg][0];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const uint16_t* vrow = vst + (32 * db + l32) * VS + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const b8v*)(vrow + 16 * ks), pb[ks],
+                                                          acc[db], 0, 0, 0);
+    }
+  };
+
+  // Double-buffered walk over key tiles [j0, j1) with operand `qop`.
+  int stg = 0;
+  auto walk = [&](int j0, int j1, const h8v* qop, const h8v* qrem, bool boundary_select) {
+    for (int j = j0; j < j1; ++j) {
+      if (j + 1 < nkt) gload(j + 1);
+      tile_body(j, stg, qop, qrem, boundary_select);
+      if (j + 1 < nkt) lstore(stg ^ 1);
+      __syncthreads();
+      stg ^= 1;
+    }
+  };
+
+  // Boundary tiles (a few per query tile) hold both query operands, so they
+  // load the next tile only after the current one is consumed instead of
+  // keeping prefetch registers live.
+  auto walk_sync = [&](int j0, int j1, const h8v* qop, const h8v* qrem) {
+    for (int j = j0; j < j1; ++j) {
+      tile_body(j, stg, qop, qrem, true);
+      __syncthreads();
+      if (j + 1 < nkt) {
+        gload(j + 1);
+        lstore(stg ^ 1);
+      }
+      __syncthreads();
+      stg ^= 1;
+    }
+  };
+
+  const int jstart = kWindow ? j_nr : 0;  // window passes skip all-remote tiles
+  if (jstart < nkt) {
+    gload(jstart);
+    lstore(0);
+  }
+  __syncthreads();
+
+  if (PASS == PASS_FUSED) {
+    h8v qop[8], qalt[8];
+    rotate_q(myq / sq.G, qop);                       // remote phase: f(q)
+    walk(0, j_nr, qop, qop, false);
+    if (j_nr < j_loc) {                              // boundary phase: both
+      rotate_q(myq, qalt);
+      walk_sync(j_nr, j_loc, qalt, qop);
+    }
+    rotate_q(myq, qop);                              // local phase: q
+    walk(max(j_nr, j_loc), nkt, qop, qop, false);
+  } else {
+    h8v qop[8];
+    const bool rem = PASS == PASS_IE_B || PASS == PASS_IE_C;
+    rotate_q(rem ? myq / sq.G : myq, qop);
+    walk(jstart, nkt, qop, qop, false);
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!qvalid) return;
+  const int64_t row = (int64_t)(sq.start + myq);
+  if (PASS == PASS_IE_A || PASS == PASS_IE_B || PASS == PASS_IE_C) {
+    float* op = (float*)a.o + (row * a.Hq + head) * PF_D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(float4*)(op + 32 * db + 8 * r4 + 4 * hh) =
+            make_float4(acc[db][4 * r4] * inv, acc[db][4 * r4 + 1] * inv,
+                        acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv);
+  } else {
+    uint16_t* op = (uint16_t*)a.o + (row * a.Hq + head) * PF_D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint16_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = f32_to_bf16_bits(acc[db][4 * r4 + e] * inv);
+        *(uint2*)(op + 32 * db + 8 * r4 + 4 * hh) = *(const uint2*)pk;
+      }
+  }
+  if (a.lse && hh == 0) {
+    const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    a.lse[(int64_t)head * a.T + row] = lse;
+  }
+}
+
+hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, int64_t T, int B,
+                               int Hq, int Hkv, int64_t w0, float scale, const RopeFreqs& fr,
+                               void* ws, const PrefillLayout& lay, hipStream_t st) {
+  char* w = (char*)ws;
+  PfArgs a;
+  a.xq = (const uint16_t*)xq;
+  a.kabs = (const uint16_t*)(w + lay.kabs);
+  a.krem = (const uint16_t*)(w + lay.krem);
+  a.vt = (const uint16_t*)(w + lay.vt);
+  a.o = o;
+  a.lse = lse;
+  a.seqs = (const SeqInfo*)(w + lay.seqs);
+  a.hdr = (const int*)(w + lay.hdr);
+  a.order = (const int*)(w + lay.tiles);
+  a.tact = a.order + B;
+  a.tbase = a.tact + (lay.max_tiles + 1);
+  a.T = (int)T;
+  a.R = (int)lay.R;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.w0 = (int)w0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.fr = fr;
+  const int64_t blocks = lay.max_tiles * Hq;
+  switch (pass) {
+    case PASS_FUSED:
+      hipLaunchKernelGGL(prefill_bf16_kernel<PASS_FUSED>, dim3(blocks), dim3(256), 0, st, a);
+      break;
+    case PASS_PLAIN:
+      hipLaunchKernelGGL(prefill_bf16_kernel<PASS_PLAIN>, dim3(blocks), dim3(256), 0, st, a);
+      break;
+    case PASS_IE_A:
+      hipLaunchKernelGGL(prefill_bf16_kernel<PASS_IE_A>, dim3(blocks), dim3(256), 0, st, a);
+      break;
+    case PASS_IE_B:
+      hipLaunchKernelGGL(prefill_bf16_kernel<PASS_IE_B>, dim3(blocks), dim3(256), 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL(prefill_bf16_kernel<PASS_IE_C>, dim3(blocks), dim3(256), 0, st, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Device tile-class dump (same classifier and tile shape as the kernel).
+// ---------------------------------------------------------------------------
+__global__ void tile_dump_kernel(int L, int w0, int nq, int nk, int8_t* out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)nq * nk) return;
+  const int i = (int)(idx / nk), j = (int)(idx % nk);
+  const int q0 = i * PF_BM, q1 = min(q0 + PF_BM, L) - 1;
+  const int k0 = j * PF_BN, k1 = min(k0 + PF_BN, L) - 1;
+  out[idx] = (int8_t)tile_class(q0, q1, k0, k1, w0);
+}
+
+hipError_t launch_tile_dump(int64_t L, int64_t w0, int8_t* out, hipStream_t st) {
+  const int nq = (int)((L + PF_BM - 1) / PF_BM), nk = (int)((L + PF_BN - 1) / PF_BN);
+  const int64_t n = (int64_t)nq * nk;
+  const int w0c = w0 > (int64_t)INT32_MAX ? INT32_MAX : (int)w0;
+  hipLaunchKernelGGL(tile_dump_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     (int)L, w0c, nq, nk, out);
+  return hipGetLastError();
+}
+
+}  // namespace jl

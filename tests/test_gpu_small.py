@@ -1,0 +1,277 @@
+"""GPU parity at sizes the oracle finishes in seconds: several tiles, ragged
+tails, and the degenerate cases (one token, w0 = 0, w0 beyond L, G = 1, an
+empty sequence in a packed batch). Every comparison is element by element
+against the float64 oracle on the same seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import rope_context_extension_jl_amd as jl
+from oracle import (bifocal_attention, bifocal_varlen, decode_row, group_size, rope,
+                    tile_class, tile_class_map)
+from synth_inputs import make_qkv
+from tests._gpu_common import (BF16_LSE_ABS, FP32_LSE_ABS, assert_bf16_close, assert_f32_close,
+                               errs, note, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+BIG = 10 ** 9  # a window wider than any sequence: plain causal RoPE attention
+
+
+# ------------------------------------------------------------------ RoPE
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("T,H,d,pos_offset,lens", [
+    (1000, 3, 128, 0, None), (777, 2, 64, 12345, None), (1300, 4, 128, 0, [5, 0, 700, 595]),
+    (64, 1, 256, 131000, None)])
+def test_rope_apply(dtype, T, H, d, pos_offset, lens):
+    theta = 1e6
+    x, _, _, _ = make_qkv(7, T, H, 1, d, dtype=dtype)
+    cu = None
+    pos = np.arange(T) + pos_offset
+    if lens is not None:
+        cuv = np.cumsum([0] + lens)
+        cu = torch.tensor(cuv, dtype=torch.int32, device="cuda")
+        pos = np.concatenate([np.arange(n) for n in lens]) + pos_offset
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    note(f"rope_apply {dtype} T={T} H={H} d={d} off={pos_offset} varlen={lens is not None}")
+    xt = to_dev(x, tdt)
+    jl.rope_apply(xt, theta, cu_seqlens=cu, pos_offset=pos_offset)
+    torch.cuda.synchronize()
+    ref = rope(x, pos, theta)
+    got = to_host(xt)
+    if dtype == "bf16":  # one rounding of an fp32 result to bf16
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+    else:
+        assert np.abs(got - ref).max() <= 2e-6 * max(1.0, np.abs(ref).max())
+
+
+# ------------------------------------------------------------------ tile classes
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 127, 128, 129, 1000, 4113])
+@pytest.mark.parametrize("w0", [0, 1, 63, 64, 100, 4096])
+def test_device_tile_classes_bitexact(L, w0):
+    bm, bn = jl.prefill_tile_shape()
+    note(f"tile dump L={L} w0={w0}")
+    dev = jl.debug_tile_classes(L, w0).cpu().numpy()
+    ref = tile_class_map(L, bm, bn, w0)
+    assert dev.shape == ref.shape
+    np.testing.assert_array_equal(dev, ref)
+
+
+def test_device_tile_classes_128k_sampled():
+    L, w0 = 131072, 4096
+    bm, bn = jl.prefill_tile_shape()
+    note("tile dump 128K")
+    dev = jl.debug_tile_classes(L, w0).cpu().numpy()
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, 31, 32, 33, 500, 1022, 1023]) | set(rng.integers(0, 1024, 24).tolist()))
+    for i in rows:
+        q0, q1 = i * bm, min(L, (i + 1) * bm) - 1
+        cols = set(range(max(0, (q0 - w0) // bn - 3), min(dev.shape[1], q1 // bn + 3)))
+        cols |= set(rng.integers(0, dev.shape[1], 40).tolist()) | {0, dev.shape[1] - 1}
+        for j in sorted(cols):
+            k0, k1 = j * bn, min(L, (j + 1) * bn) - 1
+            assert dev[i, j] == tile_class(q0, q1, k0, k1, w0), (i, j)
+    # class mix of the 128K workload (causal tiles only)
+    live = dev[dev > 0] & 3
+    frac = {c: float(np.mean(live == c)) for c in (1, 2, 3)}
+    note(f"128K tile mix local {frac[1]:.4f} remote {frac[2]:.4f} boundary {frac[3]:.4f}")
+    assert frac[2] > 0.9 and frac[3] < 0.01
+
+
+# ------------------------------------------------------------------ prefill, fp32
+def _oracle(xq, xk, v, w0, w_pre, theta, rows=None):
+    return bifocal_attention(xq, xk, v, w0, w_pre, theta, rows=rows)
+
+
+@pytest.mark.parametrize("L", [256, 64])
+@pytest.mark.parametrize("mode", ["fused", "ie", "plain"])
+def test_prefill_fp32_tiny(L, mode):
+    """Tiny fp32 workload: 1/1 heads, d = 64, w_pre = 64 (G = 4 at L = 256,
+    G = 1 at L = 64), w0 = 16, theta = 1e4, N(0,1)."""
+    xq, xk, v, _ = make_qkv(1001, 256, 1, 1, 64, dtype="fp32")
+    xq, xk, v = xq[:L], xk[:L], v[:L]
+    w0, w_pre, theta = 16, 64, 1e4
+    note(f"prefill fp32 L={L} mode={mode}")
+    o, lse = jl.bifocal_prefill(to_dev(xq, torch.float32), to_dev(xk, torch.float32),
+                                to_dev(v, torch.float32), w0, w_pre, theta, mode=mode)
+    torch.cuda.synchronize()
+    O, LSE = _oracle(xq, xk, v, BIG if mode == "plain" else w0, w_pre, theta)
+    assert_f32_close(to_host(o), O, f"fp32 L={L} {mode} O")
+    assert_f32_close(to_host(lse), LSE, f"fp32 L={L} {mode} LSE", tol=FP32_LSE_ABS)
+
+
+def test_prefill_fp32_short_context_is_plain_rope_attention():
+    """L <= w_pre gives G = 1 and the bifocal result equals plain RoPE attention."""
+    xq, xk, v, _ = make_qkv(1001, 256, 1, 1, 64, dtype="fp32")
+    xq, xk, v = (to_dev(a[:64], torch.float32) for a in (xq, xk, v))
+    o1, l1 = jl.bifocal_prefill(xq, xk, v, 16, 64, 1e4, mode="fused")
+    o2, l2 = jl.bifocal_prefill(xq, xk, v, 16, 64, 1e4, mode="plain")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ prefill, bf16
+SMALL_CASES = [
+    # L, Hq, Hkv, w0, w_pre
+    (1, 4, 2, 0, 1),
+    (37, 4, 2, 5, 8),          # G = 5, one partial tile
+    (200, 8, 2, 16, 64),       # G = 4, ragged second query tile
+    (777, 4, 4, 100, 256),     # G = 4
+    (1500, 8, 2, 300, 1000),   # G = 2
+    (1024, 4, 1, 0, 128),      # w0 = 0, G = 8
+    (640, 4, 2, 63, 64),       # window edge one short of a key tile
+    (640, 4, 2, 64, 64),       # window edge on a key tile
+    (2048, 2, 2, 4096, 512),   # w0 beyond L: every pair local
+    (513, 16, 2, 127, 100),    # GQA 8:1, G = 6
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[f"L{c[0]}-h{c[1]}x{c[2]}-w{c[3]}-p{c[4]}"
+                                                    for c in SMALL_CASES])
+@pytest.mark.parametrize("mode", ["fused", "ie", "plain"])
+def test_prefill_bf16_small(case, mode):
+    L, Hq, Hkv, w0, w_pre = case
+    theta = 1e6
+    xq, xk, v, _ = make_qkv(2000 + L, L, Hq, Hkv, 128)
+    note(f"prefill bf16 L={L} Hq={Hq} Hkv={Hkv} w0={w0} w_pre={w_pre} G={group_size(L, w_pre)} "
+         f"mode={mode}")
+    o, lse = jl.bifocal_prefill(to_dev(xq), to_dev(xk), to_dev(v), w0, w_pre, theta, mode=mode)
+    torch.cuda.synchronize()
+    O, LSE = _oracle(xq, xk, v, BIG if mode == "plain" else w0, w_pre, theta)
+    assert_bf16_close(to_host(o), O, f"{case} {mode} O")
+    mx, _ = errs(to_host(lse), LSE)
+    assert mx <= BF16_LSE_ABS, ("LSE", mx)
+
+
+def test_prefill_bf16_peaked_small():
+    """1% of key rows x8 (peaked softmax), G = 4: the hardest numerics case."""
+    L, Hq, Hkv, w0, w_pre, theta = 4096, 8, 2, 256, 1024, 1e6
+    xq, xk, v, _ = make_qkv(3001, L, Hq, Hkv, 128, peaked_frac=0.01, peaked_gain=8.0)
+    for mode in ("fused", "ie"):
+        note(f"peaked prefill mode={mode}")
+        o, lse = jl.bifocal_prefill(to_dev(xq), to_dev(xk), to_dev(v), w0, w_pre, theta, mode=mode)
+        torch.cuda.synchronize()
+        rows = np.arange(0, L, 3)
+        O, LSE = _oracle(xq, xk, v, w0, w_pre, theta, rows=rows)
+        assert_bf16_close(to_host(o)[rows], O, f"peaked {mode} O")
+        assert errs(to_host(lse)[:, rows], LSE)[0] <= BF16_LSE_ABS
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_prefill_varlen_small(dtype):
+    lens = [5, 0, 300, 129, 1000, 64]
+    Hq, Hkv, w0, w_pre, theta = 4, 2, 40, 128, 1e6
+    d = 128 if dtype == "bf16" else 64
+    T = sum(lens)
+    xq, xk, v, _ = make_qkv(4001, T, Hq, Hkv, d, dtype=dtype)
+    cu = torch.tensor(np.cumsum([0] + lens), dtype=torch.int32, device="cuda")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ref = bifocal_varlen(xq, xk, v, np.cumsum([0] + lens), w0, w_pre, theta)
+    for mode in ("fused", "ie", "plain"):
+        note(f"varlen {dtype} mode={mode} lens={lens}")
+        o, lse = jl.bifocal_prefill(to_dev(xq, tdt), to_dev(xk, tdt), to_dev(v, tdt), w0, w_pre,
+                                    theta, mode=mode, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        oh, lh = to_host(o), to_host(lse)
+        if mode == "plain":
+            ref = bifocal_varlen(xq, xk, v, np.cumsum([0] + lens), BIG, w_pre, theta)
+        s = 0
+        for b, (rows, O, LSE) in enumerate(ref):
+            n = lens[b]
+            if n:
+                if dtype == "bf16":
+                    assert_bf16_close(oh[s:s + n], O, f"varlen seq {b} {mode}")
+                else:
+                    assert_f32_close(oh[s:s + n], O, f"varlen seq {b} {mode}")
+                assert errs(lh[:, s:s + n], LSE)[0] <= (BF16_LSE_ABS if dtype == "bf16"
+                                                         else FP32_LSE_ABS)
+            s += n
+
+
+def test_kcache_out_equals_rope_apply_and_inputs_untouched():
+    L, Hq, Hkv, theta = 1000, 4, 2, 1e6
+    xq, xk, v, _ = make_qkv(5001, L, Hq, Hkv, 128)
+    q, k, vv = to_dev(xq), to_dev(xk), to_dev(v)
+    k0, q0, v0 = k.clone(), q.clone(), vv.clone()
+    kc = torch.empty_like(k)
+    note("kcache_out")
+    jl.bifocal_prefill(q, k, vv, 64, 256, theta, kcache_out=kc)
+    k2 = k.clone()
+    jl.rope_apply(k2, theta)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k2)
+    assert torch.equal(k, k0) and torch.equal(q, q0) and torch.equal(vv, v0)
+
+
+def test_prefill_is_deterministic():
+    L, Hq, Hkv = 3000, 8, 2
+    xq, xk, v, _ = make_qkv(6001, L, Hq, Hkv, 128)
+    q, k, vv = to_dev(xq), to_dev(xk), to_dev(v)
+    note("determinism")
+    a = jl.bifocal_prefill(q, k, vv, 100, 512, 1e6)
+    b = jl.bifocal_prefill(q, k, vv, 100, 512, 1e6)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ decode
+def _decode_setup(dtype, C=3000, Hq=8, Hkv=2, d=128, seed=7001):
+    xq, xk, v, _ = make_qkv(seed, C, Hq, Hkv, d, dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = to_dev(xk, tdt)
+    jl.rope_apply(kc, 1e6)  # the absolute cache
+    return xq, xk, v, kc, to_dev(v, tdt), tdt
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_small_positions(dtype):
+    w0, w_pre, theta = 100, 512, 1e6
+    d = 128 if dtype == "bf16" else 64
+    xq, xk, v, kc, vc, tdt = _decode_setup(dtype, d=d)
+    k_before = kc.clone()
+    for pos in (0, 1, 100, 101, 511, 512, 513, 1023, 1024, 1500, 2999):
+        for mode in ("fused", "plain"):
+            note(f"decode {dtype} pos={pos} G={group_size(pos + 1, w_pre)} mode={mode}")
+            o, lse = jl.bifocal_decode(to_dev(xq[pos], tdt), kc, vc, pos, w0, w_pre, theta,
+                                       mode=mode)
+            torch.cuda.synchronize()
+            ro, rl = decode_row(xq[pos], xk, v, pos, BIG if mode == "plain" else w0, w_pre, theta)
+            if dtype == "bf16":
+                assert_bf16_close(to_host(o), ro, f"decode pos={pos} {mode}")
+                assert errs(to_host(lse), rl)[0] <= BF16_LSE_ABS
+            else:
+                assert_f32_close(to_host(o), ro, f"decode pos={pos} {mode}")
+                assert errs(to_host(lse), rl)[0] <= FP32_LSE_ABS
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k_before), "decode wrote the cache"
+
+
+def test_decode_split_count_invariance():
+    w0, w_pre, theta, pos = 100, 512, 1e6, 2500
+    xq, xk, v, kc, vc, tdt = _decode_setup("bf16")
+    ro, _ = decode_row(xq[pos], xk, v, pos, w0, w_pre, theta)
+    outs = []
+    for s in (1, 2, 7, 40, 47):
+        note(f"decode splits={s}")
+        o, _ = jl.bifocal_decode(to_dev(xq[pos]), kc, vc, pos, w0, w_pre, theta, num_splits=s)
+        torch.cuda.synchronize()
+        outs.append(to_host(o))
+        assert_bf16_close(outs[-1], ro, f"splits={s}")
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 8e-3
+
+
+def test_decode_matches_prefill_last_row():
+    """decode(p) equals row p of a prefill of length p + 1 (both on the GPU)."""
+    w0, w_pre, theta = 100, 512, 1e6
+    xq, xk, v, kc, vc, tdt = _decode_setup("bf16")
+    for pos in (700, 1024, 2047):
+        note(f"decode vs prefill pos={pos}")
+        L = pos + 1
+        o_p, l_p = jl.bifocal_prefill(to_dev(xq[:L]), to_dev(xk[:L]), to_dev(v[:L]), w0, w_pre,
+                                      theta)
+        o_d, l_d = jl.bifocal_decode(to_dev(xq[pos]), kc, vc, pos, w0, w_pre, theta)
+        torch.cuda.synchronize()
+        assert np.abs(to_host(o_p)[pos] - to_host(o_d)).max() <= 1.6e-2
+        assert np.abs(to_host(l_p)[:, pos] - to_host(l_d)).max() <= 1.6e-2

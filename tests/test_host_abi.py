@@ -1,0 +1,191 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, its host-side logic (Eq. 2 group size, tile classes) is bit-exact
+against the oracle's independent definitions, and bad arguments come back as
+status codes before any launch. No kernel runs here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rope_context_extension_jl_amd as jl
+from oracle import group_size as oracle_group_size
+from oracle import tile_class as oracle_tile_class
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bifocal.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(jl.LIB_PATH),
+                                reason="libbifocal.so not built (run __graft_entry__.build())")
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = _declared_symbols()
+    for name in ("jl_group_size", "jl_rope_apply", "jl_bifocal_prefill", "jl_bifocal_decode",
+                 "jl_tile_class", "jl_debug_tile_classes"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(jl.LIB_PATH)
+    missing = [s for s in _declared_symbols() if not hasattr(lib, s)]
+    assert not missing, missing
+    # and the binding declares a signature for each of them
+    assert set(_declared_symbols()) == set(jl._SIGS)
+
+
+def test_group_size_matches_oracle_exhaustive_small():
+    for w_pre in (1, 2, 3, 7, 64, 32768):
+        for L in range(1, 3000):
+            assert jl.group_size(L, w_pre) == oracle_group_size(L, w_pre)
+
+
+def test_group_size_matches_oracle_large():
+    rng = np.random.default_rng(0)
+    for L in list(rng.integers(1, 2 ** 40, 2000)) + [2 ** 31 - 1, 2 ** 31, 2 ** 40]:
+        for w_pre in (1, 4096, 32768, 131072, 2 ** 31 - 1):
+            assert jl.group_size(int(L), w_pre) == oracle_group_size(int(L), w_pre)
+
+
+def test_group_size_rejects_bad_arguments():
+    assert jl.lib().jl_group_size(0, 4) == -1
+    assert jl.lib().jl_group_size(5, 0) == -1
+    assert jl.lib().jl_group_size(-3, 4) == -1
+
+
+def test_tile_class_matches_oracle_bruteforce_exhaustive():
+    """Every tile of every small shape against the pairwise definition."""
+    for w0 in (0, 1, 2, 5, 9):
+        for q0 in range(0, 14):
+            for q1 in range(q0, min(q0 + 6, 14)):
+                for k0 in range(0, 14):
+                    for k1 in range(k0, min(k0 + 6, 14)):
+                        assert jl.tile_class(q0, q1, k0, k1, w0) == \
+                            oracle_tile_class(q0, q1, k0, k1, w0), (q0, q1, k0, k1, w0)
+
+
+def test_tile_class_matches_oracle_at_kernel_tile_shape():
+    bm, bn = jl.prefill_tile_shape()
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        w0 = int(rng.choice([0, 1, 63, 64, 65, 127, 2048, 4096]))
+        i = int(rng.integers(0, 70))
+        j = int(rng.integers(0, 2 * i + 3))
+        L = int(rng.integers(max(1, i * bm + 1), (i + 1) * bm + 300))
+        q0, q1 = i * bm, min(L, (i + 1) * bm) - 1
+        k0 = j * bn
+        if k0 > L - 1:
+            continue
+        k1 = min(L, k0 + bn) - 1
+        assert jl.tile_class(q0, q1, k0, k1, w0) == oracle_tile_class(q0, q1, k0, k1, w0)
+
+
+def test_tile_class_rejects_bad_arguments():
+    f = jl.lib().jl_tile_class
+    assert f(5, 4, 0, 0, 1) == -1
+    assert f(0, 0, 3, 2, 1) == -1
+    assert f(-1, 0, 0, 0, 1) == -1
+    assert f(0, 0, 0, 0, -1) == -1
+
+
+def test_tile_shapes():
+    assert jl.prefill_tile_shape() == (128, 64)
+    with pytest.raises(jl.BifocalError):
+        jl.prefill_tile_shape(d=96)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -99):
+        assert jl.status_string(code)
+
+
+def test_workspace_sizes_are_monotone_and_positive():
+    a = jl.prefill_workspace_size(1000, 1, 8, 2, 128)
+    b = jl.prefill_workspace_size(2000, 1, 8, 2, 128)
+    c = jl.prefill_workspace_size(2000, 1, 8, 2, 128, mode="ie")
+    assert 0 < a < b < c
+    assert jl.decode_workspace_size(131072, 32, 128) >= 32 * 1024 * 130 * 4
+
+
+# --- argument validation: every failing call returns before any HIP call ----
+P = ctypes.c_void_p(16)  # non-null dummy: validation fails before it is touched
+
+
+def _prefill(**kw):
+    args = dict(xq=P, xk=P, v=P, o=P, lse=None, kc=None, cu=None, B=1, T=256, Hq=4, Hkv=2, d=128,
+                w0=16, w_pre=64, theta=1e4, scale=0.0, dt=0, mode=0, ws=P, ws_bytes=1 << 40,
+                stream=None)
+    args.update(kw)
+    return jl.lib().jl_bifocal_prefill(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=3, Hkv=2), -1), (dict(Hkv=0), -1), (dict(T=-1), -1), (dict(w0=-1), -1),
+    (dict(w_pre=0), -1), (dict(theta=1.0), -1), (dict(B=2), -1), (dict(d=96), -2),
+    (dict(d=64), -2), (dict(dt=1, d=96), -2), (dict(mode=7), -1), (dict(xq=None), -1),
+    (dict(ws=None), -4), (dict(ws_bytes=10), -4), (dict(ws=ctypes.c_void_p(16 + 8)), -1),
+    (dict(B=5000, cu=P), -1), (dict(dt=5), -1),
+])
+def test_prefill_argument_errors(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_prefill_empty_is_noop():
+    assert _prefill(T=0, xq=None, xk=None, v=None, o=None, ws=None, ws_bytes=0) == 0
+
+
+def _decode(**kw):
+    args = dict(xq=P, kc=P, vc=P, o=P, lse=None, pos=100, cap=1000, Hq=8, Hkv=2, d=128, w0=16,
+                w_pre=64, theta=1e4, scale=0.0, dt=0, mode=0, splits=0, ws=P, ws_bytes=1 << 40,
+                stream=None)
+    args.update(kw)
+    return jl.lib().jl_bifocal_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pos=-1), -1), (dict(pos=1000), -1), (dict(cap=0), -1), (dict(Hq=6, Hkv=4), -1),
+    (dict(w0=-2), -1), (dict(w_pre=0), -1), (dict(splits=-1), -1), (dict(mode=1), -2),
+    (dict(mode=9), -1), (dict(d=96), -2), (dict(Hq=12, Hkv=4), -2), (dict(Hq=32, Hkv=2), -2),
+    (dict(kc=None), -1), (dict(ws=None), -4), (dict(ws_bytes=100), -4),
+    (dict(splits=5000), -1), (dict(theta=0.5), -1),
+])
+def test_decode_argument_errors(kw, code):
+    assert _decode(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), -1), (dict(H=0), -1), (dict(d=7), -1), (dict(d=40), -2), (dict(d=512), -1),
+    (dict(pos=-1), -1), (dict(theta=1.0), -1), (dict(x=None), -1), (dict(B=0, cu=P), -1),
+])
+def test_rope_argument_errors(kw, code):
+    args = dict(x=P, T=10, H=2, d=128, cu=None, B=1, pos=0, theta=1e4, dt=0, stream=None)
+    args.update(kw)
+    assert jl.lib().jl_rope_apply(*args.values()) == code
+
+
+def test_rope_empty_is_noop():
+    assert jl.lib().jl_rope_apply(None, 0, 2, 128, None, 1, 0, 1e4, 0, None) == 0
+
+
+def test_debug_dump_argument_errors():
+    f = jl.lib().jl_debug_tile_classes
+    assert f(0, 0, P, None) == -1
+    assert f(10, -1, P, None) == -1
+    assert f(10, 0, None, None) == -1
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        jl.rope_apply(x, 1e4)
+    with pytest.raises(ValueError):
+        jl.bifocal_prefill(x, x[:, :1].contiguous(), x[:, :1].contiguous(), 1, 4, 1e4,
+                           workspace=torch.zeros(1, dtype=torch.uint8))

@@ -213,6 +213,10 @@ def bifocal_varlen(xq, xk, v, cu_seqlens, w0, w_pre, theta, scale=None, rows_per
     for b in range(len(cu) - 1):
         s, e = cu[b], cu[b + 1]
         rows = None if rows_per_seq is None else rows_per_seq[b]
+        if e == s:  # an empty sequence has no query rows
+            Hq, d = np.asarray(xq).shape[1:]
+            out.append((np.zeros(0, dtype=np.int64), np.zeros((0, Hq, d)), np.zeros((Hq, 0))))
+            continue
         O, LSE = bifocal_attention(xq[s:e], xk[s:e], v[s:e], w0, w_pre, theta, scale=scale,
                                    rows=rows, heads=heads)
         out.append((np.arange(e - s) if rows is None else np.asarray(rows), O, LSE))

@@ -4,11 +4,12 @@
 //   W_X = exp(l_X - M), M = max(l_A, l_B, l_C).
 // Pass A: window keys, absolute RoPE; B: every causal key, remapped RoPE;
 // C: window keys, remapped RoPE. B minus C is the remote key set.
-// Numerics: the weights are formed after the max shift, the subtraction is
-// done in linear space in fp32, and the denominator is taken as
-// W_A + max(W_B - W_C, 0) (exactly W_A + W_B - W_C in real arithmetic, where
-// W_B >= W_C). The per-row cancellation ratio (W_B + W_C) / denominator is
-// stored so callers can see how much the subtraction amplifies rounding.
+// Numerics: the weights are formed after the max shift and the subtraction
+// is done in linear space, in float64 here (the pass outputs themselves carry
+// fp32 rounding); the denominator is taken as W_A + max(W_B - W_C, 0)
+// (exactly W_A + W_B - W_C in real arithmetic, where W_B >= W_C). The
+// per-row cancellation ratio (W_B + W_C) / denominator is stored so callers
+// can see how much the subtraction amplifies the passes' rounding.
 #include "jl_internal.hpp"
 
 namespace jl {
@@ -28,17 +29,19 @@ __global__ void __launch_bounds__(256) ie_merge_kernel(const float* __restrict__
   const int64_t t = th / Hq;
   const int64_t on = (int64_t)T * Hq * D, ln = (int64_t)T * Hq;
   const int64_t li = (int64_t)h * T + t;
-  const float la = lb[li], lbb = lb[ln + li], lc = lb[2 * ln + li];
-  const float M = fmaxf(fmaxf(la, lbb), lc);
-  const float wa = expf(la - M), wb = expf(lbb - M), wc = expf(lc - M);
-  const float den = wa + fmaxf(wb - wc, 0.f);
-  const float inv = 1.f / den;
+  const double la = lb[li], lbb = lb[ln + li], lc = lb[2 * ln + li];
+  const double M = fmax(fmax(la, lbb), lc);
+  const double wa = exp(la - M), wb = exp(lbb - M), wc = exp(lc - M);
+  const double den = wa + fmax(wb - wc, 0.0);
+  const double inv = 1.0 / den;
   const int64_t oi = th * D + 4 * c;
   const float4 A = *(const float4*)(ob + oi);
   const float4 Bv = *(const float4*)(ob + on + oi);
   const float4 C = *(const float4*)(ob + 2 * on + oi);
-  float r[4] = {(wa * A.x + wb * Bv.x - wc * C.x) * inv, (wa * A.y + wb * Bv.y - wc * C.y) * inv,
-                (wa * A.z + wb * Bv.z - wc * C.z) * inv, (wa * A.w + wb * Bv.w - wc * C.w) * inv};
+  const float r[4] = {(float)((wa * A.x + wb * Bv.x - wc * C.x) * inv),
+                      (float)((wa * A.y + wb * Bv.y - wc * C.y) * inv),
+                      (float)((wa * A.z + wb * Bv.z - wc * C.z) * inv),
+                      (float)((wa * A.w + wb * Bv.w - wc * C.w) * inv)};
   if (OUT_F32) {
     *(float4*)((float*)o + oi) = make_float4(r[0], r[1], r[2], r[3]);
   } else {
@@ -47,8 +50,8 @@ __global__ void __launch_bounds__(256) ie_merge_kernel(const float* __restrict__
     *(uint2*)((uint16_t*)o + oi) = *(const uint2*)pk;
   }
   if (c == 0) {
-    if (lse) lse[li] = M + logf(den);
-    ratio[li] = (wb + wc) / den;
+    if (lse) lse[li] = (float)(M + log(den));
+    ratio[li] = (float)((wb + wc) / den);
   }
 }
 

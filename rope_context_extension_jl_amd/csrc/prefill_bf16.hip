@@ -290,6 +290,7 @@ struct PfArgs {
   const int* tact;
   const int* tbase;
   int T, R, Hq, Hkv, w0;
+  int ie_remote;  // pass B of Eq. 7 (1) or pass C (0)
   float scale_log2;
   RopeFreqs fr;
 };
@@ -299,7 +300,7 @@ __device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
 // Phases of the key loop. Key tiles come in distance order: all-remote tiles
 // first, then the few boundary tiles, then local / diagonal tiles, so only
 // one rotated query operand is live outside the boundary phase.
-enum Phase : int { PH_REMOTE = 0, PH_BOUNDARY = 1, PH_LOCAL = 2 };
+enum MaskMode : int { MASK_NONE = 0, MASK_WINDOW = 1, MASK_REMOTE = 2 };
 
 template <int PASS>
 __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
@@ -339,7 +340,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int myq = q0 + wave * 32 + l32;
   const bool qvalid = myq < sq.len;
-  constexpr bool kWindow = PASS == PASS_IE_A || PASS == PASS_IE_C;
+  constexpr bool kWindow = PASS == PASS_IE_A || PASS == PASS_IE_B;  // B runs as C + remote keys
 
   // ---- rotated query operand: RoPE(x_q, p) for p = q or f(q), as fp16.
   // The lane holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs
@@ -384,7 +385,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   auto k_source = [&](int j) -> const uint16_t* {
     bool rem;
     if (PASS == PASS_FUSED) rem = (tile_cls(j) & 3) == TC_REMOTE;
-    else rem = PASS == PASS_IE_B || PASS == PASS_IE_C;
+    else rem = PASS == PASS_IE_B;
     return (rem ? krem_g : kabs_g) + (int64_t)j * PF_BN * PF_D;
   };
 
@@ -431,7 +432,8 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   // O^T += V^T P^T. `qop` is the query operand for the LDS key tile; on a
   // boundary tile of the fused pass `qrem` scores the remapped keys read
   // straight from global memory and each element takes the branch of Eq. 1.
-  auto tile_body = [&](int j, int stg, const h8v* qop, const h8v* qrem, bool boundary_select) {
+  auto tile_body = [&](int j, int stg, const h8v* qop, const h8v* qrem, bool boundary_select,
+                       int mask_mode) {
     const int k0 = j * PF_BN;
     const int cls = tile_cls(j);
     f32x16 s[2];
@@ -466,7 +468,9 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     }
     // scale (log2 domain) and masks
     const bool causal = (cls & TC_DIAG) || j == nkt - 1;
-    const bool window = kWindow && (cls & 3) == TC_BOUNDARY;
+    const bool bnd = (cls & 3) == TC_BOUNDARY;
+    const bool window = bnd && mask_mode == MASK_WINDOW;       // keep q - k <= w0
+    const bool remote_only = bnd && mask_mode == MASK_REMOTE;  // keep q - k >  w0
     float mt = -INFINITY;
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
@@ -476,6 +480,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
         const int kk = k0 + 32 * bk + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (causal && kk > myq) x = -INFINITY;
         if (window && myq - kk > a.w0) x = -INFINITY;
+        if (remote_only && myq - kk <= a.w0) x = -INFINITY;
         s[bk][r] = x;
         mt = fmaxf(mt, x);
       }
@@ -510,27 +515,30 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     }
   };
 
-  // Double-buffered walk over key tiles [j0, j1) with operand `qop`.
+  // Double-buffered walk over key tiles [j0, j1); `next_after` is the tile to
+  // prefetch after the last one (-1: none), so segments can chain in any order.
   int stg = 0;
-  auto walk = [&](int j0, int j1, const h8v* qop, const h8v* qrem, bool boundary_select) {
+  auto walk = [&](int j0, int j1, const h8v* qop, const h8v* qrem, bool boundary_select,
+                  int mask_mode, int next_after) {
     for (int j = j0; j < j1; ++j) {
-      if (j + 1 < nkt) gload(j + 1);
-      tile_body(j, stg, qop, qrem, boundary_select);
-      if (j + 1 < nkt) lstore(stg ^ 1);
+      const int nxt = j + 1 < j1 ? j + 1 : next_after;
+      if (nxt >= 0) gload(nxt);
+      tile_body(j, stg, qop, qrem, boundary_select, mask_mode);
+      if (nxt >= 0) lstore(stg ^ 1);
       __syncthreads();
       stg ^= 1;
     }
   };
-
   // Boundary tiles (a few per query tile) hold both query operands, so they
   // load the next tile only after the current one is consumed instead of
   // keeping prefetch registers live.
-  auto walk_sync = [&](int j0, int j1, const h8v* qop, const h8v* qrem) {
+  auto walk_sync = [&](int j0, int j1, const h8v* qop, const h8v* qrem, int next_after) {
     for (int j = j0; j < j1; ++j) {
-      tile_body(j, stg, qop, qrem, true);
+      const int nxt = j + 1 < j1 ? j + 1 : next_after;
+      tile_body(j, stg, qop, qrem, true, MASK_NONE);
       __syncthreads();
-      if (j + 1 < nkt) {
-        gload(j + 1);
+      if (nxt >= 0) {
+        gload(nxt);
         lstore(stg ^ 1);
       }
       __syncthreads();
@@ -538,7 +546,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     }
   };
 
-  const int jstart = kWindow ? j_nr : 0;  // window passes skip all-remote tiles
+  const int jstart = kWindow ? j_nr : 0;  // window segments skip all-remote tiles
   if (jstart < nkt) {
     gload(jstart);
     lstore(0);
@@ -547,19 +555,37 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
 
   if (PASS == PASS_FUSED) {
     h8v qop[8], qalt[8];
+    const int jl0 = max(j_nr, j_loc);
     rotate_q(myq / sq.G, qop);                       // remote phase: f(q)
-    walk(0, j_nr, qop, qop, false);
+    walk(0, j_nr, qop, qop, false, MASK_NONE, j_nr < nkt ? j_nr : -1);
     if (j_nr < j_loc) {                              // boundary phase: both
       rotate_q(myq, qalt);
-      walk_sync(j_nr, j_loc, qalt, qop);
+      walk_sync(j_nr, j_loc, qalt, qop, jl0 < nkt ? jl0 : -1);
     }
     rotate_q(myq, qop);                              // local phase: q
-    walk(max(j_nr, j_loc), nkt, qop, qop, false);
-  } else {
+    walk(jl0, nkt, qop, qop, false, MASK_NONE, -1);
+  } else if (PASS == PASS_PLAIN) {
     h8v qop[8];
-    const bool rem = PASS == PASS_IE_B || PASS == PASS_IE_C;
-    rotate_q(rem ? myq / sq.G : myq, qop);
-    walk(jstart, nkt, qop, qop, false);
+    rotate_q(myq, qop);
+    walk(0, nkt, qop, qop, false, MASK_NONE, -1);
+  } else if (PASS == PASS_IE_A) {
+    h8v qop[8];
+    rotate_q(myq, qop);
+    walk(j_nr, nkt, qop, qop, false, MASK_WINDOW, -1);
+  } else {
+    // Passes C and B of Eq. 7 run this same code: the window keys first, in
+    // the same order and with the same masks, so pass C's softmax state is a
+    // bitwise prefix of pass B's; pass B (ie_remote = 1) then adds the remote
+    // keys of the boundary tiles and the all-remote tiles. The shared window
+    // part then cancels exactly in W_B O_B - W_C O_C up to fp32 rounding.
+    h8v qop[8];
+    rotate_q(myq / sq.G, qop);
+    const int seg2 = j_nr < j_loc ? j_nr : (j_nr > 0 ? 0 : -1);
+    walk(j_nr, nkt, qop, qop, false, MASK_WINDOW, a.ie_remote ? seg2 : -1);
+    if (a.ie_remote) {
+      walk(j_nr, j_loc, qop, qop, false, MASK_REMOTE, j_nr > 0 ? 0 : -1);
+      walk(0, j_nr, qop, qop, false, MASK_NONE, -1);
+    }
   }
 
   // ---- epilogue
@@ -567,7 +593,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!qvalid) return;
   const int64_t row = (int64_t)(sq.start + myq);
-  if (PASS == PASS_IE_A || PASS == PASS_IE_B || PASS == PASS_IE_C) {
+  if (PASS == PASS_IE_A || PASS == PASS_IE_B) {
     float* op = (float*)a.o + (row * a.Hq + head) * PF_D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -615,6 +641,7 @@ hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, in
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.w0 = (int)w0;
+  a.ie_remote = pass == PASS_IE_B;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.fr = fr;
   const int64_t blocks = lay.max_tiles * Hq;
@@ -628,11 +655,8 @@ hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, in
     case PASS_IE_A:
       hipLaunchKernelGGL(prefill_bf16_kernel<PASS_IE_A>, dim3(blocks), dim3(256), 0, st, a);
       break;
-    case PASS_IE_B:
+    default:  // passes B and C share one instantiation (see the kernel)
       hipLaunchKernelGGL(prefill_bf16_kernel<PASS_IE_B>, dim3(blocks), dim3(256), 0, st, a);
-      break;
-    default:
-      hipLaunchKernelGGL(prefill_bf16_kernel<PASS_IE_C>, dim3(blocks), dim3(256), 0, st, a);
       break;
   }
   return hipGetLastError();

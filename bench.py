@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the bifocal RoPE attention hot path on one MI355X.
+
+Timed step (the whole prefill hot path of the 128K workload): one
+jl_bifocal_prefill call in fused mode on raw bf16 Q/K/V, L = 131072,
+Hq/Hkv = 32/8, d = 128, w_pretrained = 32768 (G = 4), w0 = 4096, 1% of key
+rows x8; it rotates the keys, writes the absolute bf16 key cache, rotates the
+queries and runs the fused attention pass. Inputs are resident in HBM before
+the timed region. value = causal-attention FLOPs 2 L^2 d Hq per step / step
+time (effective TFLOP/s).
+
+Also reported (not part of the timed step): the attention kernel alone (live
+HIP events around it, for the roofline), the library's plain causal RoPE
+attention at the same shape (overhead ratio), the Eq. 7 inclusion-exclusion
+alternative, the 64K and packed-varlen workloads, decode latency at positions
+32767 .. 131071 of a 131072-key cache with L2 / MALL flushed before every
+step, and the float64 CPU oracle on a bounded sample of rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("bifocal prefill TFLOP/s + tok/s at 128K (% MFMA peak); decode µs/token "
+          "(% HBM BW)")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_128k_fused_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rope_context_extension_jl_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-iters", type=int, default=100)
+    ap.add_argument("--cpu-rows", type=int, default=16, help="oracle rows for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the timed prefill steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(1)
+
+    import torch
+
+    import rope_context_extension_jl_amd as jl
+    from synth_inputs import WORKLOADS, make_qkv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    jl.lib()  # fail loudly if the library is missing
+
+    def up(a):
+        return torch.from_numpy(a).to(torch.bfloat16).to(dev).contiguous()
+
+    c = WORKLOADS["prefill_128k"]
+    L, Hq, Hkv, d = c["lengths"][0], c["Hq"], c["Hkv"], c["d"]
+    w0, w_pre, theta = c["w0"], c["w_pre"], c["theta"]
+    G = jl.group_size(L, w_pre)
+    flops = 2.0 * L * L * d * Hq
+    log(f"generating prefill_128k inputs (L={L}, Hq={Hq}, Hkv={Hkv}, G={G})")
+    xq, xk, v, _ = make_qkv(c["seed"], L, Hq, Hkv, d, c["std"], c["dtype"], c["peaked_frac"],
+                            c["peaked_gain"])
+    q, k, vv = up(xq), up(xk), up(v)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, L), dtype=torch.float32, device=dev)
+    kcache = torch.empty_like(k)
+    ws = torch.empty(jl.prefill_workspace_size(L, 1, Hq, Hkv, d, mode="fused"), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def prefill(mode="fused", events=None, workspace=ws):
+        jl.bifocal_prefill(q, k, vv, w0, w_pre, theta, mode=mode, out=o, lse=lse,
+                           kcache_out=kcache, workspace=workspace, events=events)
+
+    # ---------------------------------------------------------- timed steps
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        prefill()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} step(s)")
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        prefill(events=ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    kern_ms = [b.elapsed_time(e) for b, e in ev]
+    kern_avg = float(np.mean(kern_ms))
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_avg * 1e-3) / 1e12
+    log(f"prefill_128k fused: {ms_per_step:.3f} ms/step ({value:.1f} TFLOP/s), attention kernel "
+        f"{kern_avg:.3f} ms ({achieved:.1f} TFLOP/s, {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of "
+        "peak)")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_128k", "seq_len": L, "batch": 1, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "w_pretrained": w_pre, "G": G, "w0": w0,
+                   "theta": theta, "peaked_key_rows": c["peaked_frac"]},
+        "tok_per_s": round(L / (ms_per_step * 1e-3), 1),
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<FUSED>",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(kern_avg, 4),
+                     "kernel_ms_min": round(min(kern_ms), 4)},
+    }
+    del ev
+
+    if not args.no_extras:
+        extras = {}
+        # ---------------------------------------------------- plain baseline
+        log("plain causal RoPE attention at the same shape")
+        ws_plain = torch.empty(jl.prefill_workspace_size(L, 1, Hq, Hkv, d, mode="plain"),
+                               dtype=torch.uint8, device=dev)
+        pe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        prefill("plain", workspace=ws_plain)
+        torch.cuda.synchronize()
+        pk = []
+        for _ in range(3):
+            prefill("plain", events=pe, workspace=ws_plain)
+            torch.cuda.synchronize()
+            pk.append(pe[0].elapsed_time(pe[1]))
+        del ws_plain
+        plain_ms = float(np.median(pk))
+        extras["plain_128k"] = {"kernel_ms": round(plain_ms, 4),
+                                "tflops": round(flops / plain_ms / 1e9, 2),
+                                "overhead_ratio_kernel": round(kern_avg / plain_ms, 4)}
+        # ---------------------------------------------------- IE alternative
+        log("inclusion-exclusion alternative")
+        ws_ie = torch.empty(jl.prefill_workspace_size(L, 1, Hq, Hkv, d, mode="ie"),
+                            dtype=torch.uint8, device=dev)
+        prefill("ie", workspace=ws_ie)
+        torch.cuda.synchronize()
+        ik = []
+        for _ in range(2):
+            prefill("ie", events=pe, workspace=ws_ie)
+            torch.cuda.synchronize()
+            ik.append(pe[0].elapsed_time(pe[1]))
+        ratio = jl.ie_ratio_view(ws_ie, L, 1, Hq, Hkv, d)
+        extras["ie_128k"] = {"kernels_ms": round(float(np.median(ik)), 4),
+                             "vs_fused": round(float(np.median(ik)) / kern_avg, 4),
+                             "worst_cancellation_ratio": float(ratio.max()),
+                             "rows_ratio_over_1e3": float((ratio > 1e3).float().mean())}
+        del ws_ie, ratio
+        torch.cuda.empty_cache()
+
+        # ---------------------------------------------------- decode
+        log("decode on the 131072-key absolute cache (L2/MALL flushed per step)")
+        cdec = WORKLOADS["decode_128k"]
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        wsd = torch.empty(jl.decode_workspace_size(L, Hq, d), dtype=torch.uint8, device=dev)
+        od = torch.empty((Hq, d), dtype=torch.bfloat16, device=dev)
+        ld = torch.empty((Hq,), dtype=torch.float32, device=dev)
+        de = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        dec = {}
+        for pos in cdec["decode_positions"]:
+            qd = q[pos].contiguous()
+            row = {}
+            for mode in ("fused", "plain"):
+                ts = []
+                for it in range(args.decode_iters + 3):
+                    flush.zero_()
+                    jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta, mode=mode, out=od,
+                                      lse=ld, workspace=wsd, events=de)
+                    torch.cuda.synchronize()
+                    if it >= 3:
+                        ts.append(de[0].elapsed_time(de[1]) * 1e3)  # us
+                nbytes = 4.0 * (pos + 1) * Hkv * d
+                med = float(np.median(ts))
+                row[mode] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
+                             "us_p90": round(pct(ts, 90), 2),
+                             "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                             "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 /
+                                                   PEAK_HBM_GBS, 2)}
+            row["G"] = jl.group_size(pos + 1, w_pre)
+            row["overhead_ratio"] = round(row["fused"]["us_median"] / row["plain"]["us_median"],
+                                          4)
+            dec[str(pos)] = row
+            log(f"decode pos={pos}: {row['fused']['us_median']} us "
+                f"({row['fused']['pct_hbm_peak']}% HBM), plain {row['plain']['us_median']} us")
+        result["decode"] = dec
+        del flush, wsd
+        torch.cuda.empty_cache()
+
+        # ---------------------------------------------------- other workloads
+        for name in ("prefill_64k", "varlen_4seq"):
+            cw = WORKLOADS[name]
+            lens = cw["lengths"]
+            T = sum(lens)
+            log(f"{name}")
+            a, b_, cc, _ = make_qkv(cw["seed"], T, cw["Hq"], cw["Hkv"], cw["d"], cw["std"],
+                                    cw["dtype"])
+            qa, ka, va = up(a), up(b_), up(cc)
+            cu = None
+            if len(lens) > 1:
+                cu = torch.tensor(np.cumsum([0] + lens), dtype=torch.int32, device=dev)
+            wsw = torch.empty(jl.prefill_workspace_size(T, len(lens), cw["Hq"], cw["Hkv"], cw["d"]),
+                              dtype=torch.uint8, device=dev)
+            ow = torch.empty_like(qa)
+            fw = sum(2.0 * n * n * cw["d"] * cw["Hq"] for n in lens)
+            jl.bifocal_prefill(qa, ka, va, cw["w0"], cw["w_pre"], cw["theta"], cu_seqlens=cu,
+                               out=ow, workspace=wsw, want_lse=False)
+            torch.cuda.synchronize()
+            ks = []
+            for _ in range(3):
+                jl.bifocal_prefill(qa, ka, va, cw["w0"], cw["w_pre"], cw["theta"], cu_seqlens=cu,
+                                   out=ow, workspace=wsw, want_lse=False, events=pe)
+                torch.cuda.synchronize()
+                ks.append(pe[0].elapsed_time(pe[1]))
+            km = float(np.median(ks))
+            extras[name] = {"kernel_ms": round(km, 4), "tflops": round(fw / km / 1e9, 2),
+                            "pct_mfma_peak": round(100 * fw / km / 1e9 / PEAK_BF16_TFLOPS, 2)}
+            del qa, ka, va, wsw, ow, a, b_, cc
+            torch.cuda.empty_cache()
+        result["extras"] = extras
+
+    if args.copy_calibration:
+        log("1 GiB device copy (counter calibration)")
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------------------------------------------------- CPU oracle
+    if not args.no_cpu_baseline:
+        from oracle import bifocal_attention
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([p.get("num_threads", 0) for p in threadpool_info()] or [0])
+        except Exception:  # noqa: BLE001
+            blas_threads = None
+        rng = np.random.default_rng(99)
+        rows = np.sort(rng.choice(L, args.cpu_rows, replace=False))
+        log(f"CPU oracle on {len(rows)} rows x {Hq} heads of prefill_128k")
+        t0 = time.perf_counter()
+        bifocal_attention(xq, xk, v, w0, w_pre, theta, rows=rows)
+        dt = time.perf_counter() - t0
+        fl = float(sum(4.0 * (r + 1) * d * Hq for r in rows))
+        result["cpu_baseline"] = {
+            "value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": blas_threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{len(rows)} seeded query rows x {Hq} heads of prefill_128k (all keys "
+                      "of each row, float64 NumPy), FLOPs 4 (q+1) d per row and head"}
+        log(f"CPU oracle: {dt:.2f} s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

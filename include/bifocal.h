@@ -128,6 +128,19 @@ int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, f
                        int Hkv, int d, int64_t w0, int64_t w_pre, double theta, float scale,
                        jl_dtype dt, jl_mode mode, void* workspace, size_t ws_bytes, void* stream);
 
+/* jl_bifocal_prefill plus timing: ev_begin / ev_end (hipEvent_t created by the
+ * caller, or NULL) are recorded on `stream` immediately before the first and
+ * after the last attention kernel (FUSED / PLAIN: the attention pass; IE: the
+ * three passes and the Eq. 7 merge), excluding the schedule and the key/value
+ * pre-pass, so a caller can time the dominant kernel alone. Same arguments,
+ * errors and results as jl_bifocal_prefill; no events are recorded when the
+ * call returns an error before launching. */
+int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void* o, float* lse,
+                             void* kcache_out, const int32_t* cu_seqlens, int B, int64_t T,
+                             int Hq, int Hkv, int d, int64_t w0, int64_t w_pre, double theta,
+                             float scale, jl_dtype dt, jl_mode mode, void* workspace,
+                             size_t ws_bytes, void* stream, void* ev_begin, void* ev_end);
+
 /* Bytes of device workspace jl_bifocal_decode needs (for any pos < capacity
  * and any num_splits it would choose or accept). */
 size_t jl_decode_workspace_size(int64_t capacity, int Hq, int d);
@@ -153,6 +166,14 @@ int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, vo
                       int64_t pos, int64_t capacity, int Hq, int Hkv, int d, int64_t w0,
                       int64_t w_pre, double theta, float scale, jl_dtype dt, jl_mode mode,
                       int num_splits, void* workspace, size_t ws_bytes, void* stream);
+
+/* jl_bifocal_decode plus timing: ev_begin / ev_end (caller-created hipEvent_t,
+ * or NULL) bracket the split and merge kernels on `stream`. */
+int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcache, void* o,
+                            float* lse, int64_t pos, int64_t capacity, int Hq, int Hkv, int d,
+                            int64_t w0, int64_t w_pre, double theta, float scale, jl_dtype dt,
+                            jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
+                            void* stream, void* ev_begin, void* ev_end);
 
 /* Device-side tile classifier dump: out_dev[i * nk + j] (int8, device) gets
  * the class the prefill kernels compute for query tile i and key tile j of a

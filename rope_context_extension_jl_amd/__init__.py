@@ -39,10 +39,16 @@ _SIGS = {
     "jl_bifocal_prefill": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_i64,
                                     _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_dbl, _c_flt,
                                     _c_int, _c_int, _c_p, _c_sz, _c_p]),
+    "jl_bifocal_prefill_timed": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int,
+                                          _c_i64, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_dbl,
+                                          _c_flt, _c_int, _c_int, _c_p, _c_sz, _c_p, _c_p, _c_p]),
     "jl_decode_workspace_size": (_c_sz, [_c_i64, _c_int, _c_int]),
     "jl_bifocal_decode": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_int,
                                    _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int, _c_int, _c_int,
                                    _c_p, _c_sz, _c_p]),
+    "jl_bifocal_decode_timed": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int,
+                                         _c_int, _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int,
+                                         _c_int, _c_int, _c_p, _c_sz, _c_p, _c_p, _c_p]),
     "jl_debug_tile_classes": (_c_int, [_c_i64, _c_i64, _c_p, _c_p]),
     "jl_status_string": (ctypes.c_char_p, [_c_int]),
     "jl_last_hip_error": (_c_int, []),
@@ -109,6 +115,18 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _events(events):
+    """(begin, end) torch.cuda.Event pair -> raw hipEvent_t handles (or NULLs)."""
+    if events is None:
+        return None, None
+    out = []
+    for ev in events:
+        if ev.cuda_event == 0:  # torch creates the HIP event lazily on first record
+            ev.record()
+        out.append(ctypes.c_void_p(ev.cuda_event))
+    return tuple(out)
+
+
 # ---------------------------------------------------------------- host-only calls
 def group_size(L: int, w_pre: int) -> int:
     g = lib().jl_group_size(int(L), int(w_pre))
@@ -159,8 +177,11 @@ def bifocal_prefill(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, w0: int
                     theta: float, scale: float = 0.0, mode: str = "fused",
                     cu_seqlens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, kcache_out: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, want_lse: bool = True):
-    """Causal bifocal attention; xq/xk/v are RAW [T, H, d]. Returns (o, lse)."""
+                    workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                    events=None):
+    """Causal bifocal attention; xq/xk/v are RAW [T, H, d]. Returns (o, lse).
+    events: optional (begin, end) torch.cuda.Event pair, recorded around the
+    attention kernels only (jl_bifocal_prefill_timed)."""
     T, Hq, d = xq.shape
     Hkv = xk.shape[1]
     B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -171,11 +192,11 @@ def bifocal_prefill(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, w0: int
     need = prefill_workspace_size(T, B, Hq, Hkv, d, xq.dtype, mode)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
-    st = lib().jl_bifocal_prefill(
+    st = lib().jl_bifocal_prefill_timed(
         _dev(xq, "xq"), _dev(xk, "xk"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
         _dev(kcache_out, "kcache_out"), _dev(cu_seqlens, "cu_seqlens"), B, T, Hq, Hkv, d,
         int(w0), int(w_pre), float(theta), float(scale), _dtype_code(xq), MODES[mode],
-        _dev(workspace, "workspace"), workspace.numel(), _stream(xq.device))
+        _dev(workspace, "workspace"), workspace.numel(), _stream(xq.device), *_events(events))
     _check("jl_bifocal_prefill", st)
     return out, lse
 
@@ -192,7 +213,7 @@ def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                    w0: int, w_pre: int, theta: float, scale: float = 0.0, mode: str = "fused",
                    num_splits: int = 0, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   want_lse: bool = True):
+                   want_lse: bool = True, events=None):
     """One decode step at `pos` with a RAW query xq [Hq, d] against the absolute
     cache [capacity, Hkv, d]. Returns (o [Hq, d], lse [Hq])."""
     Hq, d = xq.shape
@@ -204,11 +225,11 @@ def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(decode_workspace_size(C, Hq, d), dtype=torch.uint8,
                                 device=xq.device)
-    st = lib().jl_bifocal_decode(
+    st = lib().jl_bifocal_decode_timed(
         _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
         _dev(lse, "lse"), int(pos), C, Hq, Hkv, d, int(w0), int(w_pre), float(theta),
         float(scale), _dtype_code(xq), MODES[mode], int(num_splits), _dev(workspace, "workspace"),
-        workspace.numel(), _stream(xq.device))
+        workspace.numel(), _stream(xq.device), *_events(events))
     _check("jl_bifocal_decode", st)
     return out, lse
 

@@ -122,11 +122,11 @@ size_t jl_prefill_ie_ratio_offset(int64_t T, int B, int Hq, int Hkv, int d, jl_d
   return prefill_layout(T, B, Hq, Hkv, d, dt, JL_MODE_IE).ie_ratio;
 }
 
-int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, float* lse,
-                       void* kcache_out, const int32_t* cu_seqlens, int B, int64_t T, int Hq,
-                       int Hkv, int d, int64_t w0, int64_t w_pre, double theta, float scale,
-                       jl_dtype dt, jl_mode mode, void* workspace, size_t ws_bytes,
-                       void* stream) {
+int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void* o, float* lse,
+                             void* kcache_out, const int32_t* cu_seqlens, int B, int64_t T,
+                             int Hq, int Hkv, int d, int64_t w0, int64_t w_pre, double theta,
+                             float scale, jl_dtype dt, jl_mode mode, void* workspace,
+                             size_t ws_bytes, void* stream, void* ev_begin, void* ev_end) {
   if (!cu_seqlens && B != 1) return JL_EINVAL;
   if (!prefill_shape_ok(T, B, Hq, Hkv, d, dt, mode)) return JL_EINVAL;
   if (w0 < 0 || w_pre < 1 || !(theta > 1.0) || !(scale == scale)) return JL_EINVAL;
@@ -149,6 +149,8 @@ int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, f
   if (dt == JL_BF16) {
     e = launch_prefill_prep_bf16(xk, v, kcache_out, T, B, Hkv, need_rem, fr, workspace, lay, st);
     if (e != hipSuccess) return hip_status(e);
+    if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
+      return hip_status(e);
     if (mode == JL_MODE_IE) {
       float* base_o = (float*)((char*)workspace + lay.ie_o);
       float* base_l = (float*)((char*)workspace + lay.ie_lse);
@@ -167,6 +169,8 @@ int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, f
   } else {
     e = launch_prefill_prep_f32(xk, kcache_out, T, B, Hkv, d, need_rem, fr, workspace, lay, st);
     if (e != hipSuccess) return hip_status(e);
+    if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
+      return hip_status(e);
     if (mode == JL_MODE_IE) {
       float* base_o = (float*)((char*)workspace + lay.ie_o);
       float* base_l = (float*)((char*)workspace + lay.ie_lse);
@@ -183,7 +187,18 @@ int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, f
                              Hq, Hkv, d, w0, sc, fr, workspace, lay, st);
     }
   }
+  if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
   return hip_status(e);
+}
+
+int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, float* lse,
+                       void* kcache_out, const int32_t* cu_seqlens, int B, int64_t T, int Hq,
+                       int Hkv, int d, int64_t w0, int64_t w_pre, double theta, float scale,
+                       jl_dtype dt, jl_mode mode, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  return jl_bifocal_prefill_timed(xq, xk, v, o, lse, kcache_out, cu_seqlens, B, T, Hq, Hkv, d, w0,
+                                  w_pre, theta, scale, dt, mode, workspace, ws_bytes, stream,
+                                  nullptr, nullptr);
 }
 
 static int decode_max_splits(int64_t capacity) {
@@ -196,10 +211,11 @@ size_t jl_decode_workspace_size(int64_t capacity, int Hq, int d) {
   return align256((size_t)Hq * decode_max_splits(capacity) * (d + 2) * sizeof(float));
 }
 
-int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, void* o, float* lse,
-                      int64_t pos, int64_t capacity, int Hq, int Hkv, int d, int64_t w0,
-                      int64_t w_pre, double theta, float scale, jl_dtype dt, jl_mode mode,
-                      int num_splits, void* workspace, size_t ws_bytes, void* stream) {
+int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcache, void* o,
+                            float* lse, int64_t pos, int64_t capacity, int Hq, int Hkv, int d,
+                            int64_t w0, int64_t w_pre, double theta, float scale, jl_dtype dt,
+                            jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
+                            void* stream, void* ev_begin, void* ev_end) {
   if (pos < 0 || capacity < 1 || pos >= capacity || capacity > (int64_t)INT32_MAX) return JL_EINVAL;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 0 || w_pre < 1 || !(theta > 1.0)) return JL_EINVAL;
   if (num_splits < 0 || !(scale == scale)) return JL_EINVAL;
@@ -231,10 +247,24 @@ int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, vo
   RopeFreqs fr;
   make_freqs(fr, d, theta);
   const int64_t G = jl::group_size(pos + 1, w_pre);
-  return hip_status(launch_decode(xq, kcache, vcache, o, lse, pos, Hq, Hkv, d,
-                                  w0 > (int64_t)INT32_MAX ? INT32_MAX : w0, G, sc, fr,
-                                  mode == JL_MODE_PLAIN, dt == JL_FP32, S, workspace,
-                                  (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
+    return hip_status(e);
+  e = launch_decode(xq, kcache, vcache, o, lse, pos, Hq, Hkv, d,
+                    w0 > (int64_t)INT32_MAX ? INT32_MAX : w0, G, sc, fr, mode == JL_MODE_PLAIN,
+                    dt == JL_FP32, S, workspace, st);
+  if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
+  return hip_status(e);
+}
+
+int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, void* o, float* lse,
+                      int64_t pos, int64_t capacity, int Hq, int Hkv, int d, int64_t w0,
+                      int64_t w_pre, double theta, float scale, jl_dtype dt, jl_mode mode,
+                      int num_splits, void* workspace, size_t ws_bytes, void* stream) {
+  return jl_bifocal_decode_timed(xq, kcache, vcache, o, lse, pos, capacity, Hq, Hkv, d, w0, w_pre,
+                                 theta, scale, dt, mode, num_splits, workspace, ws_bytes, stream,
+                                 nullptr, nullptr);
 }
 
 int jl_debug_tile_classes(int64_t L, int64_t w0, int8_t* out_dev, void* stream) {

@@ -61,7 +61,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-iters", type=int, default=100)
-    ap.add_argument("--cpu-rows", type=int, default=16, help="oracle rows for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=128, help="oracle rows for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the timed prefill steps")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -134,6 +134,13 @@ __device__ inline void rope_cs_turns(double p, double w2pi, float& c, float& s) 
 __device__ inline float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
+// Element j (0..7) of eight bf16 values packed in a 16-byte vector, as float.
+typedef uint32_t jl_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float bf16_lane(const jl_u32x4& v, int j) {
+  const uint32_t w = v[j >> 1];
+  return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
 __device__ inline uint16_t f32_to_bf16_bits(float x) {
   __bf16 h = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
   return __builtin_bit_cast(uint16_t, h);

@@ -37,6 +37,9 @@ namespace jl {
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef __bf16 b8v __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// native 16-byte vector (HIP's uint4 is a struct with a union, which keeps
+// arrays of it out of registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KS = PF_D + 8;   // LDS row stride (elements) of a key tile: 272 B, conflict-free b128 reads
 constexpr int VS = PF_BN + 8;  // LDS row stride of a transposed value tile: 144 B
@@ -297,325 +300,386 @@ struct PfArgs {
 
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
 
-// Phases of the key loop. Key tiles come in distance order: all-remote tiles
-// first, then the few boundary tiles, then local / diagonal tiles, so only
-// one rotated query operand is live outside the boundary phase.
 enum MaskMode : int { MASK_NONE = 0, MASK_WINDOW = 1, MASK_REMOTE = 2 };
+
+// Per-workgroup constants of the attention pass. Everything the key loop
+// needs is copied here from the kernel arguments so that no pointer to the
+// argument block is taken (which would force it, and every pointer loaded
+// from it, into generic/private memory).
+struct Tctx {
+  const uint16_t* kabs;  // this sequence's KV head, row 0 of the padded layout
+  const uint16_t* krem;
+  const uint16_t* vt;    // column 0 of the sequence in the transposed values
+  int R;                 // padded row stride of vt
+  int q0, q1, len, nkt, w0;
+  int tid, hh, l32, myq;
+  float scale_log2;
+};
+
+// Running softmax state of one lane's query row.
+struct RowState {
+  f32x16 acc[4];  // O^T accumulator: d = 32*db + 8*(r/4) + 4*hh + r%4
+  float m, l;     // running max (log2 domain) and this lane's partial sum
+};
+
+__device__ __forceinline__ int tile_cls_of(const Tctx& c, int j) {
+  const int k0 = j * PF_BN;
+  return tile_class(c.q0, c.q1, k0, min(k0 + PF_BN, c.len) - 1, c.w0);
+}
+
+// Global -> registers: key tile j (64 x 128 fp16) and value tile j
+// (transposed: 128 rows x 64 keys, bf16), 4 x 16 bytes per thread each.
+__device__ __forceinline__ void tile_gload(const Tctx& c, int j, bool rem, u32x4 (&kreg)[4],
+                                           u32x4 (&vreg)[4]) {
+  const uint16_t* ks = (rem ? c.krem : c.kabs) + (int64_t)j * PF_BN * PF_D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (c.tid >> 4) + 16 * i, ch = c.tid & 15;
+    kreg[i] = *(const u32x4*)(ks + row * PF_D + 8 * ch);
+  }
+  const uint16_t* vs = c.vt + j * PF_BN;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int dd = (c.tid >> 3) + 32 * i, ch = c.tid & 7;
+    vreg[i] = *(const u32x4*)(vs + (int64_t)dd * c.R + 8 * ch);
+  }
+}
+
+// Registers -> LDS stage. Inside each 16-key group the value columns are
+// stored in the order {0-3, 8-11, 4-7, 12-15}, so a lane half reads the 8
+// keys of its PV operand (see tile_compute) as one 16-byte vector.
+__device__ __forceinline__ void tile_lstore(const Tctx& c, uint16_t* ks, uint16_t* vs,
+                                            const u32x4 (&kreg)[4], const u32x4 (&vreg)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (c.tid >> 4) + 16 * i, ch = c.tid & 15;
+    *(u32x4*)(ks + row * KS + 8 * ch) = kreg[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int dd = (c.tid >> 3) + 32 * i, ch = c.tid & 7;
+    const int base = dd * VS + 16 * (ch >> 1) + 4 * (ch & 1);
+    *(uint2*)(vs + base) = make_uint2(vreg[i].x, vreg[i].y);
+    *(uint2*)(vs + base + 8) = make_uint2(vreg[i].z, vreg[i].w);
+  }
+}
+
+// S^T (two 32-key blocks) = K Q^T for the key tile in LDS. The A operand is a
+// key row slice d = 16c + 8hh .. +8, the B operand the same slice of the
+// lane's query row; the MFMA's k-index mapping is the same for both.
+__device__ __forceinline__ void qk_lds(const Tctx& c, const uint16_t* ks, const h8v (&q)[8],
+                                       f32x16 (&s)[2]) {
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[bk][r] = 0.f;
+    const uint16_t* krow = ks + (32 * bk + c.l32) * KS + 8 * c.hh;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * cc), q[cc], s[bk],
+                                                     0, 0, 0);
+  }
+}
+
+// Boundary tile of the fused pass: remapped scores from the global key tile,
+// element-wise select by the route of Eq. 1.
+__device__ __forceinline__ void boundary_select(const Tctx& c, int j, const h8v (&qr)[8],
+                                                f32x16 (&s)[2]) {
+  const int k0 = j * PF_BN;
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    f32x16 s2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s2[r] = 0.f;
+    const uint16_t* krow = c.krem + (int64_t)(k0 + 32 * bk + c.l32) * PF_D + 8 * c.hh;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * cc), qr[cc], s2, 0, 0,
+                                                  0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = k0 + 32 * bk + 8 * (r >> 2) + 4 * c.hh + (r & 3);
+      if (c.myq - kk > c.w0) s[bk][r] = s2[r];
+    }
+  }
+}
+
+// Masks, online softmax and O^T += V^T P^T for one tile whose scores are in s.
+__device__ __forceinline__ void softmax_pv(const Tctx& c, int j, int mask_mode,
+                                           const uint16_t* vs, f32x16 (&s)[2], RowState& st) {
+  const int k0 = j * PF_BN;
+  const int cls = tile_cls_of(c, j);
+  const bool causal = (cls & TC_DIAG) || j == c.nkt - 1;
+  const bool bnd = (cls & 3) == TC_BOUNDARY;
+  const bool window = bnd && mask_mode == MASK_WINDOW;       // keep q - k <= w0
+  const bool remote_only = bnd && mask_mode == MASK_REMOTE;  // keep q - k >  w0
+  float mt = -INFINITY;
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[bk][r] * c.scale_log2;
+      const int kk = k0 + 32 * bk + 8 * (r >> 2) + 4 * c.hh + (r & 3);
+      if (causal && kk > c.myq) x = -INFINITY;
+      if (window && c.myq - kk > c.w0) x = -INFINITY;
+      if (remote_only && c.myq - kk <= c.w0) x = -INFINITY;
+      s[bk][r] = x;
+      mt = fmaxf(mt, x);
+    }
+  mt = fmaxf(mt, xor32(mt));
+  const float m_new = fmaxf(st.m, mt);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+  float psum = 0.f;
+  b8v pb[4];
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[bk][r] - m_use);
+      psum += p;
+      pb[2 * bk + (r >> 3)][r & 7] = (__bf16)p;
+    }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.acc[i][r] *= alpha;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const uint16_t* vrow = vs + (32 * db + c.l32) * VS + 8 * c.hh;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const b8v*)(vrow + 16 * ks), pb[ks],
+                                                           st.acc[db], 0, 0, 0);
+  }
+}
+
+// Double-buffered walk over key tiles [j0, j1) whose LDS key tiles hold the
+// rotation `rem_src` (remote tiles: remapped keys). `next_after` is the tile
+// to prefetch after the last one (-1: none) and `next_rem` its rotation, so
+// segments chain in any order. `stg` is the LDS stage holding tile j0.
+__device__ __forceinline__ void walk(const Tctx& c, int j0, int j1, bool rem_src, int next_after,
+                                     bool next_rem, int mask_mode, const h8v (&q)[8],
+                                     uint16_t (&Ks)[2][PF_BN * KS], uint16_t (&Vs)[2][PF_D * VS],
+                                     int& stg, RowState& st) {
+  u32x4 kreg[4], vreg[4];
+  for (int j = j0; j < j1; ++j) {
+    const int nxt = j + 1 < j1 ? j + 1 : next_after;
+    if (nxt >= 0) tile_gload(c, nxt, j + 1 < j1 ? rem_src : next_rem, kreg, vreg);
+    f32x16 s[2];
+    qk_lds(c, Ks[stg], q, s);
+    softmax_pv(c, j, mask_mode, Vs[stg], s, st);
+    if (nxt >= 0) tile_lstore(c, Ks[stg ^ 1], Vs[stg ^ 1], kreg, vreg);
+    __syncthreads();
+    stg ^= 1;
+  }
+}
+
+// Boundary tiles of the fused pass: both query operands are live, so the
+// next tile is loaded only after this one is consumed (no prefetch
+// registers). The LDS key tile holds the absolute keys.
+__device__ __forceinline__ void walk_boundary(const Tctx& c, int j0, int j1, int next_after,
+                                              const h8v (&qa)[8], const h8v (&qr)[8],
+                                              uint16_t (&Ks)[2][PF_BN * KS],
+                                              uint16_t (&Vs)[2][PF_D * VS], int& stg,
+                                              RowState& st) {
+  u32x4 kreg[4], vreg[4];
+  for (int j = j0; j < j1; ++j) {
+    const int nxt = j + 1 < j1 ? j + 1 : next_after;
+    f32x16 s[2];
+    qk_lds(c, Ks[stg], qa, s);
+    boundary_select(c, j, qr, s);
+    softmax_pv(c, j, MASK_NONE, Vs[stg], s, st);
+    __syncthreads();
+    if (nxt >= 0) {
+      tile_gload(c, nxt, false, kreg, vreg);
+      tile_lstore(c, Ks[stg ^ 1], Vs[stg ^ 1], kreg, vreg);
+    }
+    __syncthreads();
+    stg ^= 1;
+  }
+}
+
+// RoPE(x_q, p) of the lane's raw query row as the fp16 QK^T operand. The lane
+// holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs (d, d+64)
+// are chunks (c, c+4) of the same lane. w2pi: omega_i / (2 pi) in LDS.
+__device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], int p, int hh,
+                                             const double* w2pi, h8v (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x0 = bf16_lane(raw[c], j), x1 = bf16_lane(raw[c + 4], j);
+      float cs, sn;
+      rope_cs_turns((double)p, w2pi[16 * c + 8 * hh + j], cs, sn);
+      out[c][j] = (_Float16)(x0 * cs - x1 * sn);
+      out[c + 4][j] = (_Float16)(x0 * sn + x1 * cs);
+    }
+  }
+}
 
 template <int PASS>
 __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][PF_BN * KS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][PF_D * VS];
   __shared__ double w2pi_s[PF_D / 2];  // omega_i / (2 pi)
-  if (threadIdx.x < PF_D / 2) w2pi_s[threadIdx.x] = a.fr.w(threadIdx.x) * kInvTwoPi;
 
+  const int Hq = a.Hq, Hkv = a.Hkv;
   // ---- work item: (schedule slot, query head); XCD-aware head grouping
   int slot, head;
   {
     const int w = blockIdx.x;
-    if ((a.Hq & 7) == 0) {
-      const int hpx = a.Hq >> 3, k = w >> 3;
+    if ((Hq & 7) == 0) {
+      const int hpx = Hq >> 3, k = w >> 3;
       slot = k / hpx;
       head = (w & 7) * hpx + k % hpx;
     } else {
-      slot = w / a.Hq;
-      head = w % a.Hq;
+      slot = w / Hq;
+      head = w % Hq;
     }
   }
-  if (slot >= a.hdr[0]) return;
+  const int* __restrict__ hdr = a.hdr;
+  if (slot >= hdr[0]) return;
+  if (threadIdx.x < PF_D / 2) w2pi_s[threadIdx.x] = a.fr.w(threadIdx.x) * kInvTwoPi;
+  const int* __restrict__ tbase = a.tbase;
   int t;
   {
-    int lo = 0, hi = a.hdr[1] - 1;
+    int lo = 0, hi = hdr[1] - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (a.tbase[mid] <= slot) hi = mid; else lo = mid + 1;
+      if (tbase[mid] <= slot) hi = mid; else lo = mid + 1;
     }
     t = lo;
   }
-  const SeqInfo sq = a.seqs[a.order[slot - a.tbase[t]]];
-  const int g = head / (a.Hq / a.Hkv);
-  const int q0 = t * PF_BM;
-  const int q1 = min(q0 + PF_BM, sq.len) - 1;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
-  const int myq = q0 + wave * 32 + l32;
-  const bool qvalid = myq < sq.len;
-  constexpr bool kWindow = PASS == PASS_IE_A || PASS == PASS_IE_B;  // B runs as C + remote keys
+  const SeqInfo sq = a.seqs[a.order[slot - tbase[t]]];
+  const int g = head / (Hq / Hkv);
+  const int R = a.R;
 
-  // ---- rotated query operand: RoPE(x_q, p) for p = q or f(q), as fp16.
-  // The lane holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs
-  // (d, d+64) are (c, c+4), both in this lane.
-  auto rotate_q = [&](int p, h8v* out) {
-    __syncthreads();  // w2pi_s written (first call); harmless later
-    uint4 raw[8];
-    const uint16_t* qp = a.xq + ((int64_t)(sq.start + (qvalid ? myq : 0)) * a.Hq + head) * PF_D;
+  Tctx c;
+  c.tid = threadIdx.x;
+  c.hh = (c.tid & 63) >> 5;
+  c.l32 = c.tid & 31;
+  c.q0 = t * PF_BM;
+  c.q1 = min(c.q0 + PF_BM, sq.len) - 1;
+  c.len = sq.len;
+  c.myq = c.q0 + (c.tid >> 6) * 32 + c.l32;
+  c.nkt = c.q1 / PF_BN + 1;
+  c.w0 = a.w0;
+  c.R = R;
+  c.scale_log2 = a.scale_log2;
+  c.kabs = a.kabs + ((int64_t)g * R + sq.pad_off) * PF_D;
+  c.krem = a.krem + ((int64_t)g * R + sq.pad_off) * PF_D;
+  c.vt = a.vt + (int64_t)g * PF_D * R + sq.pad_off;
+  const bool qvalid = c.myq < sq.len;
+
+  // raw query row slice of this lane (zeros past the sequence end); re-read
+  // before each rotation rather than kept live across the key loops
+  const uint16_t* qp =
+      a.xq + ((int64_t)(sq.start + (qvalid ? c.myq : 0)) * Hq + head) * PF_D + 8 * c.hh;
+  auto rotq = [&](int p, h8v (&out)[8]) __attribute__((always_inline)) {
+    u32x4 raw[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      raw[c] = qvalid ? *(const uint4*)(qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint16_t* x0p = (const uint16_t*)&raw[c];
-      const uint16_t* x1p = (const uint16_t*)&raw[c + 4];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x0 = bf16_bits_to_f32(x0p[j]), x1 = bf16_bits_to_f32(x1p[j]);
-        float cs, sn;
-        rope_cs_turns((double)p, w2pi_s[16 * c + 8 * hh + j], cs, sn);
-        out[c][j] = (_Float16)(x0 * cs - x1 * sn);
-        out[c + 4][j] = (_Float16)(x0 * sn + x1 * cs);
-      }
-    }
+    for (int cc = 0; cc < 8; ++cc)
+      raw[cc] = qvalid ? *(const u32x4*)(qp + 16 * cc) : u32x4{0, 0, 0, 0};
+    rotate_query(raw, p, c.hh, w2pi_s, out);
   };
 
-  // ---- key-tile ranges (distance only; the per-tile class is recomputed below)
-  const int nkt = q1 / PF_BN + 1;
   // first tile that is not all-remote, first tile that is all-local
-  const int j_nr = q0 > a.w0 ? (q0 - a.w0) / PF_BN : 0;
-  const int j_loc = q1 > a.w0 ? min(nkt, (q1 - a.w0 + PF_BN - 1) / PF_BN) : 0;
+  const int j_nr = c.q0 > c.w0 ? (c.q0 - c.w0) / PF_BN : 0;
+  const int j_loc = c.q1 > c.w0 ? min(c.nkt, (c.q1 - c.w0 + PF_BN - 1) / PF_BN) : 0;
+  constexpr bool kWin = PASS == PASS_IE_A || PASS == PASS_IE_B;  // B runs as C + remote keys
+  const int jstart = kWin ? j_nr : 0;
 
-  const uint16_t* kabs_g = a.kabs + ((int64_t)g * a.R + sq.pad_off) * PF_D;
-  const uint16_t* krem_g = a.krem + ((int64_t)g * a.R + sq.pad_off) * PF_D;
-  const uint16_t* vt_g = a.vt + (int64_t)g * PF_D * a.R + sq.pad_off;
-
-  auto tile_cls = [&](int j) {
-    const int k0 = j * PF_BN;
-    return tile_class(q0, q1, k0, min(k0 + PF_BN, sq.len) - 1, a.w0);
-  };
-  // which rotation the LDS key tile j holds
-  auto k_source = [&](int j) -> const uint16_t* {
-    bool rem;
-    if (PASS == PASS_FUSED) rem = (tile_cls(j) & 3) == TC_REMOTE;
-    else rem = PASS == PASS_IE_B;
-    return (rem ? krem_g : kabs_g) + (int64_t)j * PF_BN * PF_D;
-  };
-
-  uint4 kreg[4], vreg[4];
-  auto gload = [&](int j) {
-    const uint16_t* ks = k_source(j);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 4) + 16 * i, ch = tid & 15;
-      kreg[i] = *(const uint4*)(ks + row * PF_D + 8 * ch);
-    }
-    const uint16_t* vs = vt_g + j * PF_BN;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int dd = (tid >> 3) + 32 * i, ch = tid & 7;
-      vreg[i] = *(const uint4*)(vs + (int64_t)dd * a.R + 8 * ch);
-    }
-  };
-  auto lstore = [&](int stg) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 4) + 16 * i, ch = tid & 15;
-      *(uint4*)(&Ks[stg][row * KS + 8 * ch]) = kreg[i];
-    }
-    // key order inside each 16-key group is stored as {0-3, 8-11, 4-7, 12-15}
-    // so a lane half reads its 8 PV operand keys as one 16-byte vector.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int dd = (tid >> 3) + 32 * i, ch = tid & 7;
-      const int base = dd * VS + 16 * (ch >> 1) + 4 * (ch & 1);
-      *(uint2*)(&Vs[stg][base]) = make_uint2(vreg[i].x, vreg[i].y);
-      *(uint2*)(&Vs[stg][base + 8]) = make_uint2(vreg[i].z, vreg[i].w);
-    }
-  };
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 acc[4];
+  RowState st;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-  // One key tile: S^T = K Q^T (two 32-key blocks), masks, online softmax,
-  // O^T += V^T P^T. `qop` is the query operand for the LDS key tile; on a
-  // boundary tile of the fused pass `qrem` scores the remapped keys read
-  // straight from global memory and each element takes the branch of Eq. 1.
-  auto tile_body = [&](int j, int stg, const h8v* qop, const h8v* qrem, bool boundary_select,
-                       int mask_mode) {
-    const int k0 = j * PF_BN;
-    const int cls = tile_cls(j);
-    f32x16 s[2];
-    const uint16_t* kst = &Ks[stg][0];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[bk][r] = 0.f;
-      const uint16_t* krow = kst + (32 * bk + l32) * KS + 8 * hh;
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * c), qop[c], s[bk],
-                                                       0, 0, 0);
-    }
-    if (boundary_select) {
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
-        f32x16 s2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s2[r] = 0.f;
-        const uint16_t* krow = krem_g + (int64_t)(k0 + 32 * bk + l32) * PF_D + 8 * hh;
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * c), qrem[c], s2,
-                                                      0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = k0 + 32 * bk + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (myq - kk > a.w0) s[bk][r] = s2[r];
-        }
-      }
-    }
-    // scale (log2 domain) and masks
-    const bool causal = (cls & TC_DIAG) || j == nkt - 1;
-    const bool bnd = (cls & 3) == TC_BOUNDARY;
-    const bool window = bnd && mask_mode == MASK_WINDOW;       // keep q - k <= w0
-    const bool remote_only = bnd && mask_mode == MASK_REMOTE;  // keep q - k >  w0
-    float mt = -INFINITY;
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[bk][r] * a.scale_log2;
-        const int kk = k0 + 32 * bk + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (causal && kk > myq) x = -INFINITY;
-        if (window && myq - kk > a.w0) x = -INFINITY;
-        if (remote_only && myq - kk <= a.w0) x = -INFINITY;
-        s[bk][r] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, xor32(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.f;
-    b8v pb[4];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[bk][r] - m_use);
-        psum += p;
-        pb[2 * bk + (r >> 3)][r & 7] = (__bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
-    const uint16_t* vst = &Vs[stg][0];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const uint16_t* vrow = vst + (32 * db + l32) * VS + 8 * hh;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const b8v*)(vrow + 16 * ks), pb[ks],
-                                                          acc[db], 0, 0, 0);
-    }
-  };
-
-  // Double-buffered walk over key tiles [j0, j1); `next_after` is the tile to
-  // prefetch after the last one (-1: none), so segments can chain in any order.
+    for (int r = 0; r < 16; ++r) st.acc[i][r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
   int stg = 0;
-  auto walk = [&](int j0, int j1, const h8v* qop, const h8v* qrem, bool boundary_select,
-                  int mask_mode, int next_after) {
-    for (int j = j0; j < j1; ++j) {
-      const int nxt = j + 1 < j1 ? j + 1 : next_after;
-      if (nxt >= 0) gload(nxt);
-      tile_body(j, stg, qop, qrem, boundary_select, mask_mode);
-      if (nxt >= 0) lstore(stg ^ 1);
-      __syncthreads();
-      stg ^= 1;
-    }
-  };
-  // Boundary tiles (a few per query tile) hold both query operands, so they
-  // load the next tile only after the current one is consumed instead of
-  // keeping prefetch registers live.
-  auto walk_sync = [&](int j0, int j1, const h8v* qop, const h8v* qrem, int next_after) {
-    for (int j = j0; j < j1; ++j) {
-      const int nxt = j + 1 < j1 ? j + 1 : next_after;
-      tile_body(j, stg, qop, qrem, true, MASK_NONE);
-      __syncthreads();
-      if (nxt >= 0) {
-        gload(nxt);
-        lstore(stg ^ 1);
-      }
-      __syncthreads();
-      stg ^= 1;
-    }
-  };
-
-  const int jstart = kWindow ? j_nr : 0;  // window segments skip all-remote tiles
-  if (jstart < nkt) {
-    gload(jstart);
-    lstore(0);
+  {
+    // the first key tile: remapped keys for the remote phase of the fused
+    // pass and for passes B/C, absolute otherwise
+    const bool rem0 = (PASS == PASS_FUSED && jstart < j_nr) || PASS == PASS_IE_B;
+    u32x4 kreg[4], vreg[4];
+    tile_gload(c, jstart, rem0, kreg, vreg);
+    tile_lstore(c, Ks[0], Vs[0], kreg, vreg);
   }
-  __syncthreads();
+  __syncthreads();  // also publishes w2pi_s
 
   if (PASS == PASS_FUSED) {
-    h8v qop[8], qalt[8];
     const int jl0 = max(j_nr, j_loc);
-    rotate_q(myq / sq.G, qop);                       // remote phase: f(q)
-    walk(0, j_nr, qop, qop, false, MASK_NONE, j_nr < nkt ? j_nr : -1);
-    if (j_nr < j_loc) {                              // boundary phase: both
-      rotate_q(myq, qalt);
-      walk_sync(j_nr, j_loc, qalt, qop, jl0 < nkt ? jl0 : -1);
+    {
+      h8v qr[8];
+      rotq(c.myq / sq.G, qr);
+      // remote phase: remapped query against remapped key tiles
+      walk(c, 0, j_nr, true, j_nr < c.nkt ? j_nr : -1, false, MASK_NONE, qr, Ks, Vs, stg, st);
+      if (j_nr < j_loc) {  // boundary phase: both routes, element-wise select
+        h8v qa[8];
+        rotq(c.myq, qa);
+        walk_boundary(c, j_nr, j_loc, jl0 < c.nkt ? jl0 : -1, qa, qr, Ks, Vs, stg, st);
+      }
     }
-    rotate_q(myq, qop);                              // local phase: q
-    walk(jl0, nkt, qop, qop, false, MASK_NONE, -1);
+    h8v qa[8];
+    rotq(c.myq, qa);
+    // local phase: absolute query against absolute key tiles
+    walk(c, jl0, c.nkt, false, -1, false, MASK_NONE, qa, Ks, Vs, stg, st);
   } else if (PASS == PASS_PLAIN) {
-    h8v qop[8];
-    rotate_q(myq, qop);
-    walk(0, nkt, qop, qop, false, MASK_NONE, -1);
+    h8v qa[8];
+    rotq(c.myq, qa);
+    walk(c, 0, c.nkt, false, -1, false, MASK_NONE, qa, Ks, Vs, stg, st);
   } else if (PASS == PASS_IE_A) {
-    h8v qop[8];
-    rotate_q(myq, qop);
-    walk(j_nr, nkt, qop, qop, false, MASK_WINDOW, -1);
+    h8v qa[8];
+    rotq(c.myq, qa);
+    walk(c, j_nr, c.nkt, false, -1, false, MASK_WINDOW, qa, Ks, Vs, stg, st);
   } else {
     // Passes C and B of Eq. 7 run this same code: the window keys first, in
     // the same order and with the same masks, so pass C's softmax state is a
     // bitwise prefix of pass B's; pass B (ie_remote = 1) then adds the remote
     // keys of the boundary tiles and the all-remote tiles. The shared window
-    // part then cancels exactly in W_B O_B - W_C O_C up to fp32 rounding.
-    h8v qop[8];
-    rotate_q(myq / sq.G, qop);
+    // part then cancels in W_B O_B - W_C O_C up to fp32 rounding.
+    h8v qr[8];
+    rotq(c.myq / sq.G, qr);
     const int seg2 = j_nr < j_loc ? j_nr : (j_nr > 0 ? 0 : -1);
-    walk(j_nr, nkt, qop, qop, false, MASK_WINDOW, a.ie_remote ? seg2 : -1);
+    walk(c, j_nr, c.nkt, true, a.ie_remote ? seg2 : -1, true, MASK_WINDOW, qr, Ks, Vs, stg, st);
     if (a.ie_remote) {
-      walk(j_nr, j_loc, qop, qop, false, MASK_REMOTE, j_nr > 0 ? 0 : -1);
-      walk(0, j_nr, qop, qop, false, MASK_NONE, -1);
+      walk(c, j_nr, j_loc, true, j_nr > 0 ? 0 : -1, true, MASK_REMOTE, qr, Ks, Vs, stg, st);
+      walk(c, 0, j_nr, true, -1, true, MASK_NONE, qr, Ks, Vs, stg, st);
     }
   }
 
   // ---- epilogue
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = st.l + xor32(st.l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!qvalid) return;
-  const int64_t row = (int64_t)(sq.start + myq);
+  const int64_t row = (int64_t)(sq.start + c.myq);
   if (PASS == PASS_IE_A || PASS == PASS_IE_B) {
-    float* op = (float*)a.o + (row * a.Hq + head) * PF_D;
+    float* op = (float*)a.o + (row * Hq + head) * PF_D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        *(float4*)(op + 32 * db + 8 * r4 + 4 * hh) =
-            make_float4(acc[db][4 * r4] * inv, acc[db][4 * r4 + 1] * inv,
-                        acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv);
+        *(float4*)(op + 32 * db + 8 * r4 + 4 * c.hh) =
+            make_float4(st.acc[db][4 * r4] * inv, st.acc[db][4 * r4 + 1] * inv,
+                        st.acc[db][4 * r4 + 2] * inv, st.acc[db][4 * r4 + 3] * inv);
   } else {
-    uint16_t* op = (uint16_t*)a.o + (row * a.Hq + head) * PF_D;
+    uint16_t* op = (uint16_t*)a.o + (row * Hq + head) * PF_D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        uint16_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = f32_to_bf16_bits(acc[db][4 * r4 + e] * inv);
-        *(uint2*)(op + 32 * db + 8 * r4 + 4 * hh) = *(const uint2*)pk;
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 2] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 3] * inv) << 16);
+        *(uint2*)(op + 32 * db + 8 * r4 + 4 * c.hh) = make_uint2(lo, hi);
       }
   }
-  if (a.lse && hh == 0) {
-    const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+  if (a.lse && c.hh == 0) {
+    const float lse = l_tot > 0.f ? (st.m + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
     a.lse[(int64_t)head * a.T + row] = lse;
   }
 }

@@ -404,48 +404,77 @@ __device__ __forceinline__ void boundary_select(const Tctx& c, int j, const h8v 
   }
 }
 
-// Masks, online softmax and O^T += V^T P^T for one tile whose scores are in s.
-__device__ __forceinline__ void softmax_pv(const Tctx& c, int j, int mask_mode,
-                                           const uint16_t* vs, f32x16 (&s)[2], RowState& st) {
+// Masks, online softmax and O^T += V^T P^T for one tile whose raw scores are
+// in s. The running reference max m only moves when a row's max grows by more
+// than 2^kLazy (in the log2 domain): probabilities are then bounded by
+// 2^kLazy instead of 1, and since the final division uses the same reference
+// the result is unchanged, while the rescale of the 64 accumulator registers
+// (and its exp) is skipped on almost every tile. MASKED selects the path for
+// the few tiles that need the causal or window masks.
+constexpr float kLazy = 8.f;
+
+// Causal / window masks on the raw scores of a tile that needs them.
+__device__ __forceinline__ void mask_scores(const Tctx& c, int j, int cls, int mask_mode,
+                                            f32x16 (&s)[2]) {
   const int k0 = j * PF_BN;
-  const int cls = tile_cls_of(c, j);
   const bool causal = (cls & TC_DIAG) || j == c.nkt - 1;
   const bool bnd = (cls & 3) == TC_BOUNDARY;
   const bool window = bnd && mask_mode == MASK_WINDOW;       // keep q - k <= w0
   const bool remote_only = bnd && mask_mode == MASK_REMOTE;  // keep q - k >  w0
-  float mt = -INFINITY;
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = s[bk][r] * c.scale_log2;
       const int kk = k0 + 32 * bk + 8 * (r >> 2) + 4 * c.hh + (r & 3);
-      if (causal && kk > c.myq) x = -INFINITY;
-      if (window && c.myq - kk > c.w0) x = -INFINITY;
-      if (remote_only && c.myq - kk <= c.w0) x = -INFINITY;
-      s[bk][r] = x;
-      mt = fmaxf(mt, x);
+      const int dist = c.myq - kk;
+      const bool drop = (causal && dist < 0) || (window && dist > c.w0) ||
+                        (remote_only && dist <= c.w0);
+      if (drop) s[bk][r] = -INFINITY;
     }
-  mt = fmaxf(mt, xor32(mt));
-  const float m_new = fmaxf(st.m, mt);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+}
+
+// Does tile j need masks?
+__device__ __forceinline__ bool tile_needs_mask(const Tctx& c, int j, int cls, int mask_mode) {
+  return (cls & TC_DIAG) || j == c.nkt - 1 ||
+         ((cls & 3) == TC_BOUNDARY && mask_mode != MASK_NONE);
+}
+
+__device__ __forceinline__ void softmax_pv_any(const Tctx& c, int j, int mask_mode,
+                                               const uint16_t* vs, f32x16 (&s)[2],
+                                               RowState& st) {
+  const int cls = tile_cls_of(c, j);
+  if (tile_needs_mask(c, j, cls, mask_mode)) mask_scores(c, j, cls, mask_mode, s);
+  float mt = -INFINITY;
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[bk][r]);
+  mt = fmaxf(mt, xor32(mt)) * c.scale_log2;  // scale > 0 commutes with max
+  // lazy reference update (the same decision in both lanes of a row)
+  const bool grow = mt > st.m + kLazy || (st.m == -INFINITY && mt > -INFINITY);
+  if (__any(grow)) {
+    const float m_new = grow ? mt : st.m;
+    const float alpha = grow ? (st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new))
+                             : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[i][r] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = st.m == -INFINITY ? 0.f : st.m;
   float psum = 0.f;
   b8v pb[4];
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[bk][r] - m_use);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bk][r], c.scale_log2, -m_use));
       psum += p;
       pb[2 * bk + (r >> 3)][r & 7] = (__bf16)p;
     }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.acc[i][r] *= alpha;
+  st.l += psum;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const uint16_t* vrow = vs + (32 * db + c.l32) * VS + 8 * c.hh;
@@ -470,7 +499,7 @@ __device__ __forceinline__ void walk(const Tctx& c, int j0, int j1, bool rem_src
     if (nxt >= 0) tile_gload(c, nxt, j + 1 < j1 ? rem_src : next_rem, kreg, vreg);
     f32x16 s[2];
     qk_lds(c, Ks[stg], q, s);
-    softmax_pv(c, j, mask_mode, Vs[stg], s, st);
+    softmax_pv_any(c, j, mask_mode, Vs[stg], s, st);
     if (nxt >= 0) tile_lstore(c, Ks[stg ^ 1], Vs[stg ^ 1], kreg, vreg);
     __syncthreads();
     stg ^= 1;
@@ -491,7 +520,7 @@ __device__ __forceinline__ void walk_boundary(const Tctx& c, int j0, int j1, int
     f32x16 s[2];
     qk_lds(c, Ks[stg], qa, s);
     boundary_select(c, j, qr, s);
-    softmax_pv(c, j, MASK_NONE, Vs[stg], s, st);
+    softmax_pv_any(c, j, MASK_NONE, Vs[stg], s, st);
     __syncthreads();
     if (nxt >= 0) {
       tile_gload(c, nxt, false, kreg, vreg);

@@ -64,7 +64,9 @@ def test_device_tile_classes_128k_sampled():
     note("tile dump 128K")
     dev = jl.debug_tile_classes(L, w0).cpu().numpy()
     rng = np.random.default_rng(3)
-    rows = sorted(set([0, 1, 31, 32, 33, 500, 1022, 1023]) | set(rng.integers(0, 1024, 24).tolist()))
+    nq = dev.shape[0]
+    rows = sorted({0, 1, nq // 32, nq // 32 + 1, nq // 2, nq - 2, nq - 1} |
+                  set(rng.integers(0, nq, 24).tolist()))
     for i in rows:
         q0, q1 = i * bm, min(L, (i + 1) * bm) - 1
         cols = set(range(max(0, (q0 - w0) // bn - 3), min(dev.shape[1], q1 // bn + 3)))

@@ -36,6 +36,7 @@ namespace jl {
 
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef __bf16 b8v __attribute__((ext_vector_type(8)));
+typedef __bf16 b2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 // native 16-byte vector (HIP's uint4 is a struct with a union, which keeps
 // arrays of it out of registers)
@@ -316,10 +317,15 @@ struct Tctx {
   float scale_log2;
 };
 
-// Running softmax state of one lane's query row.
+// Running softmax state of one lane's query row. Scores are produced in the
+// log2 domain already shifted by the reference: the query operand carries
+// scale * log2(e), and the QK^T accumulator starts at -m, so each MFMA
+// output is s' = scale * log2(e) * (q . k) - m and p = exp2(s') directly.
 struct RowState {
   f32x16 acc[4];  // O^T accumulator: d = 32*db + 8*(r/4) + 4*hh + r%4
-  float m, l;     // running max (log2 domain) and this lane's partial sum
+  f32x16 negm;    // -m in every register: the QK^T accumulator's start value
+  float m, l;     // reference (log2 domain; -inf until the row has a score)
+                  // and this lane's partial sum
 };
 
 __device__ __forceinline__ int tile_cls_of(const Tctx& c, int j) {
@@ -368,14 +374,13 @@ __device__ __forceinline__ void tile_lstore(const Tctx& c, uint16_t* ks, uint16_
 // key row slice d = 16c + 8hh .. +8, the B operand the same slice of the
 // lane's query row; the MFMA's k-index mapping is the same for both.
 __device__ __forceinline__ void qk_lds(const Tctx& c, const uint16_t* ks, const h8v (&q)[8],
-                                       f32x16 (&s)[2]) {
+                                       const f32x16& negm, f32x16 (&s)[2]) {
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[bk][r] = 0.f;
     const uint16_t* krow = ks + (32 * bk + c.l32) * KS + 8 * c.hh;
+    s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)krow, q[0], negm, 0, 0, 0);
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
+    for (int cc = 1; cc < 8; ++cc)
       s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * cc), q[cc], s[bk],
                                                      0, 0, 0);
   }
@@ -384,16 +389,14 @@ __device__ __forceinline__ void qk_lds(const Tctx& c, const uint16_t* ks, const 
 // Boundary tile of the fused pass: remapped scores from the global key tile,
 // element-wise select by the route of Eq. 1.
 __device__ __forceinline__ void boundary_select(const Tctx& c, int j, const h8v (&qr)[8],
-                                                f32x16 (&s)[2]) {
+                                                const f32x16& negm, f32x16 (&s)[2]) {
   const int k0 = j * PF_BN;
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
-    f32x16 s2;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s2[r] = 0.f;
     const uint16_t* krow = c.krem + (int64_t)(k0 + 32 * bk + c.l32) * PF_D + 8 * c.hh;
+    f32x16 s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)krow, qr[0], negm, 0, 0, 0);
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
+    for (int cc = 1; cc < 8; ++cc)
       s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * cc), qr[cc], s2, 0, 0,
                                                   0);
 #pragma unroll
@@ -404,14 +407,17 @@ __device__ __forceinline__ void boundary_select(const Tctx& c, int j, const h8v 
   }
 }
 
-// Masks, online softmax and O^T += V^T P^T for one tile whose raw scores are
-// in s. The running reference max m only moves when a row's max grows by more
-// than 2^kLazy (in the log2 domain): probabilities are then bounded by
-// 2^kLazy instead of 1, and since the final division uses the same reference
-// the result is unchanged, while the rescale of the 64 accumulator registers
-// (and its exp) is skipped on almost every tile. MASKED selects the path for
-// the few tiles that need the causal or window masks.
-constexpr float kLazy = 8.f;
+// Masks, online softmax and O^T += V^T P^T for one tile whose shifted
+// scores s' = s - m are in s. The reference m does not follow every new row
+// maximum: it moves only when the tile's probabilities p = exp2(s') summed
+// over a lane's 32 keys exceed 2^8 (or the row has no reference yet), so
+// every p stays below 2^8 and the sum check replaces the per-tile row max.
+// Since the final division uses the same reference, the result does not
+// depend on where the reference sits; the rescale of the 64 accumulator
+// registers, the row max and the cross-lane exchange are skipped on almost
+// every tile. The tile sum is taken over the bf16-rounded p, the same values
+// the PV product weights, so numerator and denominator see identical p.
+constexpr float kSumMax = 256.f;
 
 // Causal / window masks on the raw scores of a tile that needs them.
 __device__ __forceinline__ void mask_scores(const Tctx& c, int j, int cls, int mask_mode,
@@ -439,41 +445,72 @@ __device__ __forceinline__ bool tile_needs_mask(const Tctx& c, int j, int cls, i
          ((cls & 3) == TC_BOUNDARY && mask_mode != MASK_NONE);
 }
 
+// p = exp2(s') packed to bf16 as the PV operand; returns the lane's sum of
+// the rounded p (bf16 pair dot products with ones, fp32 accumulation).
+__device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], b8v (&pb)[4]) {
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pb[2 * bk + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(s[bk][r]);
+  const b2v one = {(__bf16)1.f, (__bf16)1.f};
+  float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks], pb[ks], 0, 1), one, ps0,
+                                          false);
+    ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks], pb[ks], 2, 3), one, ps1,
+                                          false);
+    ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks], pb[ks], 4, 5), one, ps0,
+                                          false);
+    ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks], pb[ks], 6, 7), one, ps1,
+                                          false);
+  }
+  return ps0 + ps1;
+}
+
+// Partner lane (l ^ 32) exchange as one VALU op: after the swap the two
+// results hold this lane's and the partner's value, in lane-half order.
+__device__ __forceinline__ float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ void softmax_pv_any(const Tctx& c, int j, int mask_mode,
                                                const uint16_t* vs, f32x16 (&s)[2],
                                                RowState& st) {
   const int cls = tile_cls_of(c, j);
   if (tile_needs_mask(c, j, cls, mask_mode)) mask_scores(c, j, cls, mask_mode, s);
-  float mt = -INFINITY;
+  b8v pb[4];
+  float psum = exp_pack(s, pb);
+  const bool need = !(psum <= kSumMax) || st.m == -INFINITY;
+  if (__any(need)) {
+    // Rare: move the reference of the rows that need it to their tile max.
+    // Both lanes of a row take the same decision from exchanged values.
+    float mt = -INFINITY;
 #pragma unroll
-  for (int bk = 0; bk < 2; ++bk)
+    for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[bk][r]);
-  mt = fmaxf(mt, xor32(mt)) * c.scale_log2;  // scale > 0 commutes with max
-  // lazy reference update (the same decision in both lanes of a row)
-  const bool grow = mt > st.m + kLazy || (st.m == -INFINITY && mt > -INFINITY);
-  if (__any(grow)) {
-    const float m_new = grow ? mt : st.m;
-    const float alpha = grow ? (st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new))
-                             : 1.f;
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[bk][r]);
+    mt = max_with_partner(mt);
+    const bool grow = max_with_partner(need ? 1.f : 0.f) > 0.f && mt > -INFINITY;
+    const float delta = grow ? mt : 0.f;
+    const float alpha = grow ? (st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-mt)) : 1.f;
     st.l *= alpha;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.acc[i][r] *= alpha;
-    st.m = m_new;
+    if (grow) st.m = (st.m == -INFINITY ? 0.f : st.m) + mt;
+    const float nm = st.m == -INFINITY ? 0.f : -st.m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.negm[r] = nm;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[bk][r] -= delta;
+    psum = exp_pack(s, pb);
   }
-  const float m_use = st.m == -INFINITY ? 0.f : st.m;
-  float psum = 0.f;
-  b8v pb[4];
-#pragma unroll
-  for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bk][r], c.scale_log2, -m_use));
-      psum += p;
-      pb[2 * bk + (r >> 3)][r & 7] = (__bf16)p;
-    }
   st.l += psum;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
@@ -498,7 +535,7 @@ __device__ __forceinline__ void walk(const Tctx& c, int j0, int j1, bool rem_src
     const int nxt = j + 1 < j1 ? j + 1 : next_after;
     if (nxt >= 0) tile_gload(c, nxt, j + 1 < j1 ? rem_src : next_rem, kreg, vreg);
     f32x16 s[2];
-    qk_lds(c, Ks[stg], q, s);
+    qk_lds(c, Ks[stg], q, st.negm, s);
     softmax_pv_any(c, j, mask_mode, Vs[stg], s, st);
     if (nxt >= 0) tile_lstore(c, Ks[stg ^ 1], Vs[stg ^ 1], kreg, vreg);
     __syncthreads();
@@ -518,8 +555,8 @@ __device__ __forceinline__ void walk_boundary(const Tctx& c, int j0, int j1, int
   for (int j = j0; j < j1; ++j) {
     const int nxt = j + 1 < j1 ? j + 1 : next_after;
     f32x16 s[2];
-    qk_lds(c, Ks[stg], qa, s);
-    boundary_select(c, j, qr, s);
+    qk_lds(c, Ks[stg], qa, st.negm, s);
+    boundary_select(c, j, qr, st.negm, s);
     softmax_pv_any(c, j, MASK_NONE, Vs[stg], s, st);
     __syncthreads();
     if (nxt >= 0) {
@@ -533,9 +570,10 @@ __device__ __forceinline__ void walk_boundary(const Tctx& c, int j0, int j1, int
 
 // RoPE(x_q, p) of the lane's raw query row as the fp16 QK^T operand. The lane
 // holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs (d, d+64)
-// are chunks (c, c+4) of the same lane. w2pi: omega_i / (2 pi) in LDS.
+// are chunks (c, c+4) of the same lane. w2pi: omega_i / (2 pi) in LDS. The
+// operand carries the score scale qs = scale * log2(e).
 __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], int p, int hh,
-                                             const double* w2pi, h8v (&out)[8]) {
+                                             const double* w2pi, float qs, h8v (&out)[8]) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -543,8 +581,8 @@ __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], int p, int h
       const float x0 = bf16_lane(raw[c], j), x1 = bf16_lane(raw[c + 4], j);
       float cs, sn;
       rope_cs_turns((double)p, w2pi[16 * c + 8 * hh + j], cs, sn);
-      out[c][j] = (_Float16)(x0 * cs - x1 * sn);
-      out[c + 4][j] = (_Float16)(x0 * sn + x1 * cs);
+      out[c][j] = (_Float16)((x0 * cs - x1 * sn) * qs);
+      out[c + 4][j] = (_Float16)((x0 * sn + x1 * cs) * qs);
     }
   }
 }
@@ -612,7 +650,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
       raw[cc] = qvalid ? *(const u32x4*)(qp + 16 * cc) : u32x4{0, 0, 0, 0};
-    rotate_query(raw, p, c.hh, w2pi_s, out);
+    rotate_query(raw, p, c.hh, w2pi_s, c.scale_log2, out);
   };
 
   // first tile that is not all-remote, first tile that is all-local
@@ -626,6 +664,8 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.acc[i][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) st.negm[r] = 0.f;
   st.m = -INFINITY;
   st.l = 0.f;
   int stg = 0;

@@ -232,8 +232,9 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
   const int64_t keys = pos + 1;
   int S = num_splits;
   if (S == 0) {
-    // ~4 workgroups per CU over the KV heads, at least 64 keys per split.
-    int64_t want = (1024 + Hkv - 1) / Hkv;
+    // bf16: one wave per split, ~8 waves per CU over the KV heads; float32:
+    // one workgroup per split, ~4 per CU. At least 64 keys per split.
+    int64_t want = ((dt == JL_BF16 ? 2048 : 1024) + Hkv - 1) / Hkv;
     int64_t by_keys = (keys + 63) / 64;
     S = (int)(want < by_keys ? want : by_keys);
   }

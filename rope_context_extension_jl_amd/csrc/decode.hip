@@ -203,34 +203,362 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path: one wave per split, both products on the matrix cores.
+//
+// Per 64-key chunk a wave loads K (as the A operand of S^T = K Q^T, fp16,
+// 16x16x32 MFMAs: lane = one key, 8 consecutive dims) and V (row-major into a
+// wave-private LDS region). Remote keys are corrected in-lane: the pairs
+// (i, i + D/2) of a key sit in d-steps ds and ds + D/64 of the same lane. The
+// S^T tile gives each lane one query (lane % 16) and four keys per 16-key
+// block, which is exactly the A operand of O = P V for two consecutive
+// blocks; the V operand (8 keys at one dim per lane) comes from LDS with the
+// transpose read ds_read_b64_tr_b16: within 16 lanes, lane i receives element
+// i % 4 of the 8-byte rows addressed by lanes i / 4 + 4t, t = 0..3, so lanes
+// pointing at V[key_t][4c .. 4c + 3] deliver V[key_t][own dim] for 4 keys.
+// Query heads are padded to the 16 MFMA columns with zeros.
+//
+// Softmax: the query operand carries scale * log2(e) and the score
+// accumulator starts at -m, m a per-split reference that moves only when a
+// lane's sum of bf16-rounded p over the chunk exceeds 2^8 (or on the first
+// scores), so the common chunk needs no row max and no cross-lane exchange.
+// ---------------------------------------------------------------------------
+typedef _Float16 dh8v __attribute__((ext_vector_type(8)));
+typedef __bf16 db8v __attribute__((ext_vector_type(8)));
+typedef __bf16 db2v __attribute__((ext_vector_type(2)));
+typedef short ds4v __attribute__((ext_vector_type(4)));
+typedef float df32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t du32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int DEC_CHUNK = 64;
+constexpr float kDecSumMax = 256.f;
+
+template <int D>
+struct DecGeom {
+  static constexpr int NDS = D / 32;        // 32-dim steps of the QK product
+  static constexpr int NDB = D / 16;        // 16-dim output blocks of the PV product
+  static constexpr int VROW = 2 * D + 32;   // LDS bytes per key row (padding: conflict-free reads)
+  static constexpr int VLD = D / 8;         // 16-byte V loads per lane per chunk
+  static constexpr int VLPR = 2 * D / 16;   // lanes per V row
+};
+
+template <int D>
+__device__ __forceinline__ void dec_qk(const dh8v (&kf)[D / 32], const dh8v (&q)[D / 32],
+                                       const df32x4& c, df32x4& out) {
+  out = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[0], q[0], c, 0, 0, 0);
+#pragma unroll
+  for (int ds = 1; ds < D / 32; ++ds)
+    out = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ds], q[ds], out, 0, 0, 0);
+}
+
+// bf16 pairs of a 16-byte vector -> 8 fp16 (exact for normal bf16 values in
+// fp16 range), optionally rotated by the remote correction first.
+__device__ __forceinline__ dh8v dec_to_f16(const du32x4& v) {
+  dh8v r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (_Float16)bf16_lane(v, j);
+  return r;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
+  using G = DecGeom<D>;
+  constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[4][DEC_CHUNK * VROW];
+  __shared__ double w2pi_s[D / 2];
+  // the wave index is uniform per wave: say so, so that every split-derived
+  // value (key range, route of a key block) lives in scalar registers and the
+  // route branches are scalar jumps; matrix instructions then never run under
+  // a partial or empty EXEC mask
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g16 = lane >> 4, r16 = lane & 15;
+  if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
+  __syncthreads();
+  const int s = blockIdx.x * 4 + wave, kvh = blockIdx.y;
+  if (s >= a.S) return;
+  const int R = a.Hq / a.Hkv, h0 = kvh * R;
+  const uint16_t* xq = (const uint16_t*)a.xq;
+  const uint16_t* kc = (const uint16_t*)a.kc;
+  const uint16_t* vc = (const uint16_t*)a.vc;
+  uint8_t* vb = vbuf[wave];
+
+  // query operands (B of S^T = K Q^T): lane holds dims 32 ds + 8 g16 + j of
+  // query head r16, rotated at pos (qa) and at f(pos) (qr), times scale*log2 e
+  dh8v qa[NDS], qr[NDS];
+  {
+    const bool qv = r16 < R;
+    const uint16_t* qp = xq + (int64_t)(h0 + (qv ? r16 : 0)) * D;
+    const int fpos = a.pos / a.G;
+#pragma unroll
+    for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * ds + 8 * g16 + j;
+        const float x0 = qv ? bf16_bits_to_f32(qp[i]) : 0.f;
+        const float x1 = qv ? bf16_bits_to_f32(qp[i + D / 2]) : 0.f;
+        float c, sn;
+        rope_cs_turns((double)a.pos, w2pi_s[i], c, sn);
+        qa[ds][j] = (_Float16)((x0 * c - x1 * sn) * a.scale_log2);
+        qa[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * c) * a.scale_log2);
+        rope_cs_turns((double)fpos, w2pi_s[i], c, sn);
+        qr[ds][j] = (_Float16)((x0 * c - x1 * sn) * a.scale_log2);
+        qr[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * c) * a.scale_log2);
+      }
+  }
+  const int k_lo = s * a.kps;
+  const int k_hi = min(k_lo + a.kps, a.pos + 1);
+  const int64_t rstride = (int64_t)a.Hkv * D;  // elements between consecutive keys
+  const uint16_t* kbase = kc + (int64_t)kvh * D + 8 * g16;
+  const uint16_t* vbase = vc + (int64_t)kvh * D;
+  const bool correct = !a.plain && a.G > 1;
+
+  df32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = df32x4{0.f, 0.f, 0.f, 0.f};
+  df32x4 negm = {0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
+  for (int k0 = k_lo; k0 < k_hi; k0 += DEC_CHUNK) {
+    asm volatile("" ::: "memory");  // previous chunk's LDS reads stay before these stores
+    // ---- loads: K fragments (key k0 + 16 kb + r16) and the V chunk
+    du32x4 kr[4][NDS], vr[G::VLD];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = k0 + 16 * kb + r16;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds)
+        kr[kb][ds] = key < k_hi ? *(const du32x4*)(kbase + key * rstride + 32 * ds)
+                                : du32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < G::VLD; ++i) {
+      const int row = (i * 64 + lane) / G::VLPR, ch = lane % G::VLPR;
+      vr[i] = k0 + row < k_hi ? *(const du32x4*)(vbase + (k0 + row) * rstride + 8 * ch)
+                              : du32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < G::VLD; ++i) {
+      const int row = (i * 64 + lane) / G::VLPR, ch = lane % G::VLPR;
+      *(du32x4*)(vb + row * VROW + 16 * ch) = vr[i];
+    }
+    // ---- S^T = K Q^T per 16-key block, seeded with -m
+    df32x4 st[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int kfirst = k0 + 16 * kb;
+      const int klast = min(kfirst + 15, k_hi - 1);
+      const bool any_rem = !a.plain && a.pos - kfirst > a.w0;
+      const bool any_loc = a.plain || a.pos - klast <= a.w0;
+      const int key = kfirst + r16;
+      dh8v kf[NDS];
+      if (correct && a.pos - key > a.w0) {
+        // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2)
+        const double delta = (double)(key / a.G - key);
+#pragma unroll
+        for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float c, sn;
+            rope_cs_turns(delta, w2pi_s[32 * ds + 8 * g16 + j], c, sn);
+            const float x0 = bf16_lane(kr[kb][ds], j), x1 = bf16_lane(kr[kb][ds + NDS / 2], j);
+            kf[ds][j] = (_Float16)(x0 * c - x1 * sn);
+            kf[ds + NDS / 2][j] = (_Float16)(x0 * sn + x1 * c);
+          }
+      } else {
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) kf[ds] = dec_to_f16(kr[kb][ds]);
+      }
+      if (!any_loc) {
+        dec_qk<D>(kf, qr, negm, st[kb]);
+      } else if (!any_rem) {
+        dec_qk<D>(kf, qa, negm, st[kb]);
+      } else {
+        // block across the window edge: each lane (one key) keeps its
+        // fragment for its own route and zeros it for the other, so one
+        // accumulation chain adds exactly one product per key
+        const bool rem = a.pos - key > a.w0;
+        dh8v kl[NDS], krm[NDS];
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+          const dh8v z = {};
+          kl[ds] = rem ? z : kf[ds];
+          krm[ds] = rem ? kf[ds] : z;
+        }
+        df32x4 t;
+        dec_qk<D>(kl, qa, negm, t);
+        dec_qk<D>(krm, qr, t, st[kb]);
+      }
+      if (klast - kfirst < 15) {  // keys past the split end
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kfirst + 4 * g16 + r >= k_hi) st[kb][r] = -INFINITY;
+      }
+    }
+    // ---- p = exp2(s'), packed as the A operand of O = P V (2 x 32 keys)
+    db8v pb[2];
+    auto expsum = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pb[kb >> 1][4 * (kb & 1) + r] = (__bf16)__builtin_amdgcn_exp2f(st[kb][r]);
+      const db2v one = {(__bf16)1.f, (__bf16)1.f};
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[t], pb[t], 0, 1), one, ps0,
+                                              false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[t], pb[t], 2, 3), one, ps1,
+                                              false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[t], pb[t], 4, 5), one, ps0,
+                                              false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[t], pb[t], 6, 7), one, ps1,
+                                              false);
+      }
+      return ps0 + ps1;
+    };
+    float psum = expsum();
+    const bool need = !(psum <= kDecSumMax) || m == -INFINITY;
+    if (__any(need)) {
+      // move the reference of the queries that need it to their chunk max;
+      // a query's scores live in lanes r16 + 16 g, g = 0..3
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, st[kb][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      float nf = need ? 1.f : 0.f;
+      nf = fmaxf(nf, __shfl_xor(nf, 16));
+      nf = fmaxf(nf, __shfl_xor(nf, 32));
+      const bool grow = nf > 0.f && mt > -INFINITY;
+      const float delta = grow ? mt : 0.f;
+      const float alpha = grow ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-mt)) : 1.f;
+      lsum *= alpha;
+      if (grow) m = (m == -INFINITY ? 0.f : m) + mt;
+      const float nm = m == -INFINITY ? 0.f : -m;
+      negm = df32x4{nm, nm, nm, nm};
+      // output rows of this lane are queries 4 g16 + r, held as r16 by lane 4 g16 + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float al = __shfl(alpha, 4 * g16 + r);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db][r] *= al;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[kb][r] -= delta;
+      psum = expsum();
+    }
+    lsum += psum;
+    // ---- O += P V, the V operand through transpose reads of the LDS chunk
+    // LDS operations of a wave complete in order; keep the compiler from
+    // moving the reads above this wave's stores (other lanes' data)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        ds4v lo, hi;
+        {
+          const int row = 32 * kst + 4 * g16 + (r16 >> 2);
+          const int col = 16 * db + 4 * (r16 & 3);
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) ds4v*)(vb + row * VROW + 2 * col));
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) ds4v*)(vb + (row + 16) * VROW + 2 * col));
+        }
+        const db8v vop = __builtin_bit_cast(db8v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[kst], vop, acc[db], 0, 0, 0);
+      }
+  }
+  // ---- split partial: m (log2 domain), l, unnormalised O for each query head
+  float lt = lsum + __shfl_xor(lsum, 16);
+  lt += __shfl_xor(lt, 32);
+  float* part = a.part;
+  if (g16 == 0 && r16 < R) {
+    float* pp = part + ((int64_t)(h0 + r16) * a.S + s) * (D + 2);
+    pp[0] = m;
+    pp[1] = lt;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int q = 4 * g16 + r;
+    if (q < R) {
+      float* pp = part + ((int64_t)(h0 + q) * a.S + s) * (D + 2) + 2;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) pp[16 * db + r16] = acc[db][r];
+    }
+  }
+}
+
+// Merge of the split partials of one query head with LSE weights: the
+// reference max over splits, one weight per split (in LDS), then each thread
+// sums one output dim over a strided subset of the splits.
 template <bool F32, int D>
-__global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
-  const int h = blockIdx.x, dd = threadIdx.x;
+__global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
+  constexpr int NG = 256 / D;
+  __shared__ float wts[1024];
+  __shared__ float red[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
   const float* pp = a.part + (int64_t)h * a.S * (D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < a.S; ++s) M = fmaxf(M, pp[(int64_t)s * (D + 2)]);
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < a.S; ++s) {
+  for (int s = tid; s < a.S; s += 256) M = fmaxf(M, pp[(int64_t)s * (D + 2)]);
+  red[tid] = M;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  float L = 0.f;
+  for (int s = tid; s < a.S; s += 256) {
     const float ms = pp[(int64_t)s * (D + 2)];
     const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    L += pp[(int64_t)s * (D + 2) + 1] * w;
-    A += pp[(int64_t)s * (D + 2) + 2 + dd] * w;
+    wts[s] = w;
+    L += w * pp[(int64_t)s * (D + 2) + 1];
   }
-  const float out = A / L;
-  if constexpr (F32) ((float*)a.o)[(int64_t)h * D + dd] = out;
-  else ((uint16_t*)a.o)[(int64_t)h * D + dd] = f32_to_bf16_bits(out);
-  if (a.lse && dd == 0) a.lse[h] = (M + __log2f(L)) * 0.69314718055994530942f;
+  red[tid] = L;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  L = red[0];
+  __syncthreads();
+  const int dd = tid % D, grp = tid / D;
+  float A = 0.f;
+#pragma unroll 4
+  for (int s = grp; s < a.S; s += NG) A += wts[s] * pp[(int64_t)s * (D + 2) + 2 + dd];
+  red[tid] = A;
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 1; g < NG; ++g) A += red[tid + g * D];
+    const float out = A / L;
+    if constexpr (F32) ((float*)a.o)[(int64_t)h * D + dd] = out;
+    else ((uint16_t*)a.o)[(int64_t)h * D + dd] = f32_to_bf16_bits(out);
+    if (a.lse && dd == 0) a.lse[h] = (M + __log2f(L)) * 0.69314718055994530942f;
+  }
 }
 
 template <bool F32, int D>
 static void launch_decode_t(int R, dim3 grid, hipStream_t st, const DecArgs& a) {
-  switch (R) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<F32, D, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<F32, D, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<F32, D, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<F32, D, 8>), grid, dim3(256), 0, st, a); break;
+  if constexpr (F32) {
+    switch (R) {
+      case 1: hipLaunchKernelGGL((decode_split_kernel<F32, D, 1>), grid, dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((decode_split_kernel<F32, D, 2>), grid, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((decode_split_kernel<F32, D, 4>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((decode_split_kernel<F32, D, 8>), grid, dim3(256), 0, st, a); break;
+    }
+  } else {
+    const dim3 g2((a.S + 3) / 4, grid.y);
+    hipLaunchKernelGGL((decode_mfma_kernel<D>), g2, dim3(256), 0, st, a);
   }
-  hipLaunchKernelGGL((decode_merge_kernel<F32, D>), dim3(a.Hq), dim3(D), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<F32, D>), dim3(a.Hq), dim3(256), 0, st, a);
 }
 
 hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,

@@ -271,6 +271,26 @@ def test_decode_small_positions(dtype):
     assert torch.equal(kc, k_before), "decode wrote the cache"
 
 
+@pytest.mark.parametrize("Hq,Hkv,d", [(2, 2, 128), (4, 2, 128), (16, 2, 128), (8, 2, 64),
+                                       (8, 8, 64)])
+def test_decode_bf16_head_ratios_and_dims(Hq, Hkv, d):
+    """Every GQA ratio the boundary accepts and both head dims, remote and
+    local keys, a ragged last chunk (pos + 1 not a multiple of 64)."""
+    w0, w_pre, theta = 100, 512, 1e6
+    xq, xk, v, _ = make_qkv(7100 + Hq + d, 1400, Hq, Hkv, d)
+    kc = to_dev(xk)
+    jl.rope_apply(kc, theta)
+    vc = to_dev(v)
+    for pos in (0, 63, 64, 150, 1023, 1399):
+        for mode in ("fused", "plain"):
+            note(f"decode bf16 Hq={Hq} Hkv={Hkv} d={d} pos={pos} {mode}")
+            o, lse = jl.bifocal_decode(to_dev(xq[pos]), kc, vc, pos, w0, w_pre, theta, mode=mode)
+            torch.cuda.synchronize()
+            ro, rl = decode_row(xq[pos], xk, v, pos, BIG if mode == "plain" else w0, w_pre, theta)
+            assert_bf16_close(to_host(o), ro, f"decode pos={pos} {mode}")
+            assert errs(to_host(lse), rl)[0] <= BF16_LSE_ABS
+
+
 def test_decode_split_count_invariance():
     w0, w_pre, theta, pos = 100, 512, 1e6, 2500
     xq, xk, v, kc, vc, tdt = _decode_setup("bf16")

@@ -202,9 +202,12 @@ def main():
         torch.cuda.empty_cache()
 
         # ---------------------------------------------------- decode
-        log("decode on the 131072-key absolute cache (L2/MALL flushed per step)")
+        log("decode on the 131072-key absolute cache (L2/MALL evicted by a clean read per step)")
         cdec = WORKLOADS["decode_128k"]
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # clean 1 GiB read between steps: evicts the cache from L2 and the
+        # memory-side cache without leaving dirty lines behind (a zero-fill
+        # would make the timed step pay for its write-backs)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         wsd = torch.empty(jl.decode_workspace_size(L, Hq, d), dtype=torch.uint8, device=dev)
         od = torch.empty((Hq, d), dtype=torch.bfloat16, device=dev)
         ld = torch.empty((Hq,), dtype=torch.float32, device=dev)
@@ -216,7 +219,7 @@ def main():
             for mode in ("fused", "plain"):
                 ts = []
                 for it in range(args.decode_iters + 3):
-                    flush.zero_()
+                    flush.sum()
                     jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta, mode=mode, out=od,
                                       lse=ld, workspace=wsd, events=de)
                     torch.cuda.synchronize()

@@ -9,11 +9,12 @@
 // against the query rotated at f(pos). Keys inside the window are scored
 // against the query rotated at pos.
 //
-// Split-K: workgroup (split s, KV head g) streams keys [s*n, (s+1)*n) of
-// head g once, for all Hq/Hkv query heads of the group, and leaves a partial
-// (max, sum, unnormalised accumulator) per query head; a second kernel merges
-// the splits with LSE weights. HBM traffic is the K and V rows of keys
-// 0..pos read once.
+// Split-K: each split streams keys [s*n, (s+1)*n) of one KV head once, for
+// all Hq/Hkv query heads of the group, and leaves a partial (max, sum,
+// unnormalised accumulator) per query head; a second kernel merges the splits
+// with LSE weights. HBM traffic is the K and V rows of keys 0..pos read once.
+// The bf16 kernel runs one split per wave (a workgroup covers four KV heads
+// of one key range); the float32 kernel one split per workgroup.
 //
 // Lane layout: D/8 lanes per key; lane dl holds the pairs
 // (4dl .. 4dl+3, D/2 + 4dl .. D/2 + 4dl + 3), so the correction rotation is
@@ -274,8 +275,11 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   const int g16 = lane >> 4, r16 = lane & 15;
   if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
   __syncthreads();
-  const int s = blockIdx.x * 4 + wave, kvh = blockIdx.y;
-  if (s >= a.S) return;
+  // workgroup = one split of four KV heads (wave w: head 4 hg + w), so the
+  // waves running together read neighbouring head slices of the same key rows
+  const int hgroups = (a.Hkv + 3) >> 2;
+  const int s = blockIdx.x / hgroups, kvh = (blockIdx.x % hgroups) * 4 + wave;
+  if (kvh >= a.Hkv) return;
   const int R = a.Hq / a.Hkv, h0 = kvh * R;
   const uint16_t* xq = (const uint16_t*)a.xq;
   const uint16_t* kc = (const uint16_t*)a.kc;
@@ -494,15 +498,15 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   }
 }
 
-// Merge of the split partials of one query head with LSE weights: the
-// reference max over splits, one weight per split (in LDS), then each thread
-// sums one output dim over a strided subset of the splits.
+// Merge of the split partials of one query head with LSE weights.
+// Workgroup (head h, 16 output dims): the reference max over splits and one
+// weight per split (in LDS), then 16 split groups x 16 dims accumulate and
+// reduce through LDS.
 template <bool F32, int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
-  constexpr int NG = 256 / D;
   __shared__ float wts[1024];
   __shared__ float red[256];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int h = blockIdx.x, d0 = 16 * blockIdx.y, tid = threadIdx.x;
   const float* pp = a.part + (int64_t)h * a.S * (D + 2);
   float M = -INFINITY;
   for (int s = tid; s < a.S; s += 256) M = fmaxf(M, pp[(int64_t)s * (D + 2)]);
@@ -529,19 +533,19 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
   }
   L = red[0];
   __syncthreads();
-  const int dd = tid % D, grp = tid / D;
+  const int dd = tid & 15, grp = tid >> 4;
   float A = 0.f;
 #pragma unroll 4
-  for (int s = grp; s < a.S; s += NG) A += wts[s] * pp[(int64_t)s * (D + 2) + 2 + dd];
+  for (int s = grp; s < a.S; s += 16) A += wts[s] * pp[(int64_t)s * (D + 2) + 2 + d0 + dd];
   red[tid] = A;
   __syncthreads();
   if (grp == 0) {
 #pragma unroll
-    for (int g = 1; g < NG; ++g) A += red[tid + g * D];
+    for (int g = 1; g < 16; ++g) A += red[tid + 16 * g];
     const float out = A / L;
-    if constexpr (F32) ((float*)a.o)[(int64_t)h * D + dd] = out;
-    else ((uint16_t*)a.o)[(int64_t)h * D + dd] = f32_to_bf16_bits(out);
-    if (a.lse && dd == 0) a.lse[h] = (M + __log2f(L)) * 0.69314718055994530942f;
+    if constexpr (F32) ((float*)a.o)[(int64_t)h * D + d0 + dd] = out;
+    else ((uint16_t*)a.o)[(int64_t)h * D + d0 + dd] = f32_to_bf16_bits(out);
+    if (a.lse && d0 + dd == 0) a.lse[h] = (M + __log2f(L)) * 0.69314718055994530942f;
   }
 }
 
@@ -555,10 +559,10 @@ static void launch_decode_t(int R, dim3 grid, hipStream_t st, const DecArgs& a) 
       default: hipLaunchKernelGGL((decode_split_kernel<F32, D, 8>), grid, dim3(256), 0, st, a); break;
     }
   } else {
-    const dim3 g2((a.S + 3) / 4, grid.y);
+    const dim3 g2(a.S * ((a.Hkv + 3) / 4));
     hipLaunchKernelGGL((decode_mfma_kernel<D>), g2, dim3(256), 0, st, a);
   }
-  hipLaunchKernelGGL((decode_merge_kernel<F32, D>), dim3(a.Hq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<F32, D>), dim3(a.Hq, D / 16), dim3(256), 0, st, a);
 }
 
 hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,

@@ -232,10 +232,12 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
   const int64_t keys = pos + 1;
   int S = num_splits;
   if (S == 0) {
-    // bf16: one wave per split, ~8 waves per CU over the KV heads; float32:
-    // one workgroup per split, ~4 per CU. At least 64 keys per split.
+    // bf16: one wave per split, up to ~8 waves per CU over the KV heads, at
+    // least 256 keys per split (fewer partials to merge at short contexts);
+    // float32: one workgroup per split, ~4 per CU, at least 64 keys.
+    const int64_t min_keys = dt == JL_BF16 ? 256 : 64;
     int64_t want = ((dt == JL_BF16 ? 2048 : 1024) + Hkv - 1) / Hkv;
-    int64_t by_keys = (keys + 63) / 64;
+    int64_t by_keys = (keys + min_keys - 1) / min_keys;
     S = (int)(want < by_keys ? want : by_keys);
   }
   if (S < 1) S = 1;

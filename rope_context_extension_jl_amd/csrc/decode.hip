@@ -231,16 +231,50 @@ typedef short ds4v __attribute__((ext_vector_type(4)));
 typedef float df32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t du32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int DEC_CHUNK = 64;
+constexpr int DEC_CHUNK = 32;  // keys per chunk; two chunks are in flight per wave
 constexpr float kDecSumMax = 256.f;
 
 template <int D>
 struct DecGeom {
-  static constexpr int NDS = D / 32;        // 32-dim steps of the QK product
-  static constexpr int NDB = D / 16;        // 16-dim output blocks of the PV product
-  static constexpr int VROW = 2 * D + 32;   // LDS bytes per key row (padding: conflict-free reads)
-  static constexpr int VLD = D / 8;         // 16-byte V loads per lane per chunk
-  static constexpr int VLPR = 2 * D / 16;   // lanes per V row
+  static constexpr int NDS = D / 32;                    // 32-dim steps of the QK product
+  static constexpr int NDB = D / 16;                    // 16-dim output blocks of the PV product
+  static constexpr int NC = D / 8;                      // 16-byte chunks per key row
+  static constexpr int VROW = 2 * D;                    // LDS bytes per key row
+  static constexpr int VLD = DEC_CHUNK * 2 * D / 1024;  // 1 KiB V transfers per chunk
+  static constexpr int RPL = 64 / NC;                   // key rows per transfer
+  static constexpr int VBYTES = DEC_CHUNK * VROW;       // one LDS stage
+};
+
+// LDS position of 16-byte chunk ch of key row r in a V stage: rows are
+// packed (the direct-to-LDS transfers write 1 KiB contiguously) and the chunk
+// index is XOR-swizzled by the row so that the transpose reads of the PV
+// operand (4 rows x 32 bytes per 16 lanes) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int dec_vswz(int r) {
+  return (2 * r) & (DecGeom<D>::NC - 1);
+}
+
+// Per-wave constants of the key loop (all wave-uniform except the lane ids).
+struct DecCtx {
+  const uint16_t* kbase;  // this lane's K slice: head, dims 8 * g16 ..
+  const uint16_t* vbase;  // the head's V row 0
+  int64_t rstride;        // elements between consecutive keys
+  int pos, w0, G, plain, correct, k_hi;
+  int lane, g16, r16;
+};
+
+// One chunk's K fragments (key k0 + 16 kb + r16, dims 32 ds + 8 g16 .. + 8);
+// its V rows go straight to an LDS stage.
+template <int D>
+struct DecBuf {
+  du32x4 k[2][D / 32];
+};
+
+template <int D>
+struct DecState {
+  df32x4 acc[D / 16];  // O: lane holds dims 16 db + r16 of queries 4 g16 + r
+  df32x4 negm;         // -m in every element: the QK accumulator's start value
+  float m, lsum;       // reference (log2 domain) of query r16, partial row sum
 };
 
 template <int D>
@@ -262,10 +296,180 @@ __device__ __forceinline__ dh8v dec_to_f16(const du32x4& v) {
 }
 
 template <int D>
+__device__ __forceinline__ void dec_issue_k(const DecCtx& c, int k0, DecBuf<D>& b) {
+  using G = DecGeom<D>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // keys past the split end load the last key (finite data, masked later)
+    const int key = min(k0 + 16 * kb + c.r16, c.k_hi - 1);
+#pragma unroll
+    for (int ds = 0; ds < G::NDS; ++ds)
+      b.k[kb][ds] = *(const du32x4*)(c.kbase + key * c.rstride + 32 * ds);
+  }
+}
+
+// V rows of the chunk, global -> LDS stage without registers: transfer i
+// writes rows RPL i .. RPL i + RPL - 1; lane L fills slot L, i.e. row
+// RPL i + L / NC, swizzled chunk L % NC, so it fetches the row's chunk
+// (L % NC) ^ swz(row).
+template <int D>
+__device__ __forceinline__ void dec_issue_v(const DecCtx& c, int k0, uint8_t* stage) {
+  using G = DecGeom<D>;
+#pragma unroll
+  for (int i = 0; i < G::VLD; ++i) {
+    const int row = G::RPL * i + c.lane / G::NC;
+    const int ch = (c.lane % G::NC) ^ dec_vswz<D>(row);
+    const int key = min(k0 + row, c.k_hi - 1);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(c.vbase + key * c.rstride + 8 * ch),
+        (__attribute__((address_space(3))) void*)(stage + 1024 * i), 16, 0, 0);
+  }
+}
+
+// p = exp2(s') of the chunk's two 16-key blocks, packed as the A operand of
+// O = P V; returns the lane's sum of the rounded p.
+__device__ __forceinline__ float dec_exp(const df32x4 (&st)[2], db8v& pb) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pb[4 * kb + r] = (__bf16)__builtin_amdgcn_exp2f(st[kb][r]);
+  const db2v one = {(__bf16)1.f, (__bf16)1.f};
+  float ps0 =
+      __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one, 0.f, false);
+  float ps1 =
+      __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one, 0.f, false);
+  ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one, ps0, false);
+  ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one, ps1, false);
+  return ps0 + ps1;
+}
+
+template <int D>
+__device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<D>& b,
+                                          const dh8v (&qa)[D / 32], const dh8v (&qr)[D / 32],
+                                          const double* w2pi, const uint8_t* vb,
+                                          DecState<D>& st) {
+  using G = DecGeom<D>;
+  constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
+  // ---- S^T = K Q^T per 16-key block, seeded with -m
+  df32x4 s2[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kfirst = k0 + 16 * kb;
+    const int klast = min(kfirst + 15, c.k_hi - 1);
+    const bool any_rem = !c.plain && c.pos - kfirst > c.w0;
+    const bool any_loc = c.plain || c.pos - klast <= c.w0;
+    const int key = kfirst + c.r16;
+    dh8v kf[NDS];
+    if (c.correct && c.pos - key > c.w0) {
+      // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2)
+      const double delta = (double)(key / c.G - key);
+#pragma unroll
+      for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float cs, sn;
+          rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + j], cs, sn);
+          const float x0 = bf16_lane(b.k[kb][ds], j), x1 = bf16_lane(b.k[kb][ds + NDS / 2], j);
+          kf[ds][j] = (_Float16)(x0 * cs - x1 * sn);
+          kf[ds + NDS / 2][j] = (_Float16)(x0 * sn + x1 * cs);
+        }
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) kf[ds] = dec_to_f16(b.k[kb][ds]);
+    }
+    if (!any_loc) {
+      dec_qk<D>(kf, qr, st.negm, s2[kb]);
+    } else if (!any_rem) {
+      dec_qk<D>(kf, qa, st.negm, s2[kb]);
+    } else {
+      // block across the window edge: each lane (one key) keeps its fragment
+      // for its own route and zeros it for the other, so one accumulation
+      // chain adds exactly one product per key
+      const bool rem = c.pos - key > c.w0;
+      dh8v kl[NDS], krm[NDS];
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const dh8v z = {};
+        kl[ds] = rem ? z : kf[ds];
+        krm[ds] = rem ? kf[ds] : z;
+      }
+      df32x4 t;
+      dec_qk<D>(kl, qa, st.negm, t);
+      dec_qk<D>(krm, qr, t, s2[kb]);
+    }
+    if (klast - kfirst < 15) {  // keys past the split end
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kfirst + 4 * c.g16 + r >= c.k_hi) s2[kb][r] = -INFINITY;
+    }
+  }
+  // ---- softmax with the lazy reference
+  db8v pb;
+  float psum = dec_exp(s2, pb);
+  const bool need = !(psum <= kDecSumMax) || st.m == -INFINITY;
+  if (__any(need)) {
+    // move the reference of the queries that need it to their chunk max; a
+    // query's scores live in lanes r16 + 16 g, g = 0..3
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s2[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float nf = need ? 1.f : 0.f;
+    nf = fmaxf(nf, __shfl_xor(nf, 16));
+    nf = fmaxf(nf, __shfl_xor(nf, 32));
+    const bool grow = nf > 0.f && mt > -INFINITY;
+    const float delta = grow ? mt : 0.f;
+    const float alpha = grow ? (st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-mt)) : 1.f;
+    st.lsum *= alpha;
+    if (grow) st.m = (st.m == -INFINITY ? 0.f : st.m) + mt;
+    const float nm = st.m == -INFINITY ? 0.f : -st.m;
+    st.negm = df32x4{nm, nm, nm, nm};
+    // output rows of this lane are queries 4 g16 + r, held as r16 by lane 4 g16 + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float al = __shfl(alpha, 4 * c.g16 + r);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) st.acc[db][r] *= al;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s2[kb][r] -= delta;
+    psum = dec_exp(s2, pb);
+  }
+  st.lsum += psum;
+  // ---- O += P V, the V operand through transpose reads of the LDS stage:
+  // lane (g16, r16) addresses row 4 g16 + r16 / 4 (and + 16), dims
+  // 16 db + 4 (r16 % 4) .. + 3, i.e. byte 8 (r16 & 1) of chunk
+  // 2 db + (r16 & 3) / 2 before the swizzle
+  const int row = 4 * c.g16 + (c.r16 >> 2);
+  const int sub = 8 * (c.r16 & 1);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int ch = 2 * db + ((c.r16 & 3) >> 1);
+    const ds4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) ds4v*)(vb + row * VROW +
+                                                  16 * (ch ^ dec_vswz<D>(row)) + sub));
+    const ds4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) ds4v*)(vb + (row + 16) * VROW +
+                                                  16 * (ch ^ dec_vswz<D>(row + 16)) + sub));
+    const db8v vop =
+        __builtin_bit_cast(db8v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vop, st.acc[db], 0, 0, 0);
+  }
+}
+
+template <int D>
 __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   using G = DecGeom<D>;
   constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
-  __shared__ __attribute__((aligned(16))) uint8_t vbuf[4][DEC_CHUNK * VROW];
+  // two V stages per wave, as separate arrays so that reads of one are known
+  // not to alias the transfers in flight into the other
+  __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
   __shared__ double w2pi_s[D / 2];
   // the wave index is uniform per wave: say so, so that every split-derived
   // value (key range, route of a key block) lives in scalar registers and the
@@ -284,7 +488,6 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   const uint16_t* xq = (const uint16_t*)a.xq;
   const uint16_t* kc = (const uint16_t*)a.kc;
   const uint16_t* vc = (const uint16_t*)a.vc;
-  uint8_t* vb = vbuf[wave];
 
   // query operands (B of S^T = K Q^T): lane holds dims 32 ds + 8 g16 + j of
   // query head r16, rotated at pos (qa) and at f(pos) (qr), times scale*log2 e
@@ -310,174 +513,54 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
       }
   }
   const int k_lo = s * a.kps;
-  const int k_hi = min(k_lo + a.kps, a.pos + 1);
-  const int64_t rstride = (int64_t)a.Hkv * D;  // elements between consecutive keys
-  const uint16_t* kbase = kc + (int64_t)kvh * D + 8 * g16;
-  const uint16_t* vbase = vc + (int64_t)kvh * D;
-  const bool correct = !a.plain && a.G > 1;
+  DecCtx c;
+  c.k_hi = min(k_lo + a.kps, a.pos + 1);
+  c.rstride = (int64_t)a.Hkv * D;
+  c.kbase = kc + (int64_t)kvh * D + 8 * g16;
+  c.vbase = vc + (int64_t)kvh * D;
+  c.pos = a.pos;
+  c.w0 = a.w0;
+  c.G = a.G;
+  c.plain = a.plain;
+  c.correct = !a.plain && a.G > 1;
+  c.lane = lane;
+  c.g16 = g16;
+  c.r16 = r16;
 
-  df32x4 acc[NDB];
+  DecState<D> st;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = df32x4{0.f, 0.f, 0.f, 0.f};
-  df32x4 negm = {0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  for (int db = 0; db < NDB; ++db) st.acc[db] = df32x4{0.f, 0.f, 0.f, 0.f};
+  st.negm = df32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.lsum = 0.f;
 
-  for (int k0 = k_lo; k0 < k_hi; k0 += DEC_CHUNK) {
-    asm volatile("" ::: "memory");  // previous chunk's LDS reads stay before these stores
-    // ---- loads: K fragments (key k0 + 16 kb + r16) and the V chunk
-    du32x4 kr[4][NDS], vr[G::VLD];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = k0 + 16 * kb + r16;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds)
-        kr[kb][ds] = key < k_hi ? *(const du32x4*)(kbase + key * rstride + 32 * ds)
-                                : du32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < G::VLD; ++i) {
-      const int row = (i * 64 + lane) / G::VLPR, ch = lane % G::VLPR;
-      vr[i] = k0 + row < k_hi ? *(const du32x4*)(vbase + (k0 + row) * rstride + 8 * ch)
-                              : du32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < G::VLD; ++i) {
-      const int row = (i * 64 + lane) / G::VLPR, ch = lane % G::VLPR;
-      *(du32x4*)(vb + row * VROW + 16 * ch) = vr[i];
-    }
-    // ---- S^T = K Q^T per 16-key block, seeded with -m
-    df32x4 st[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int kfirst = k0 + 16 * kb;
-      const int klast = min(kfirst + 15, k_hi - 1);
-      const bool any_rem = !a.plain && a.pos - kfirst > a.w0;
-      const bool any_loc = a.plain || a.pos - klast <= a.w0;
-      const int key = kfirst + r16;
-      dh8v kf[NDS];
-      if (correct && a.pos - key > a.w0) {
-        // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2)
-        const double delta = (double)(key / a.G - key);
-#pragma unroll
-        for (int ds = 0; ds < NDS / 2; ++ds)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float c, sn;
-            rope_cs_turns(delta, w2pi_s[32 * ds + 8 * g16 + j], c, sn);
-            const float x0 = bf16_lane(kr[kb][ds], j), x1 = bf16_lane(kr[kb][ds + NDS / 2], j);
-            kf[ds][j] = (_Float16)(x0 * c - x1 * sn);
-            kf[ds + NDS / 2][j] = (_Float16)(x0 * sn + x1 * c);
-          }
-      } else {
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) kf[ds] = dec_to_f16(kr[kb][ds]);
-      }
-      if (!any_loc) {
-        dec_qk<D>(kf, qr, negm, st[kb]);
-      } else if (!any_rem) {
-        dec_qk<D>(kf, qa, negm, st[kb]);
-      } else {
-        // block across the window edge: each lane (one key) keeps its
-        // fragment for its own route and zeros it for the other, so one
-        // accumulation chain adds exactly one product per key
-        const bool rem = a.pos - key > a.w0;
-        dh8v kl[NDS], krm[NDS];
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          const dh8v z = {};
-          kl[ds] = rem ? z : kf[ds];
-          krm[ds] = rem ? kf[ds] : z;
-        }
-        df32x4 t;
-        dec_qk<D>(kl, qa, negm, t);
-        dec_qk<D>(krm, qr, t, st[kb]);
-      }
-      if (klast - kfirst < 15) {  // keys past the split end
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kfirst + 4 * g16 + r >= k_hi) st[kb][r] = -INFINITY;
-      }
-    }
-    // ---- p = exp2(s'), packed as the A operand of O = P V (2 x 32 keys)
-    db8v pb[2];
-    auto expsum = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          pb[kb >> 1][4 * (kb & 1) + r] = (__bf16)__builtin_amdgcn_exp2f(st[kb][r]);
-      const db2v one = {(__bf16)1.f, (__bf16)1.f};
-      float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[t], pb[t], 0, 1), one, ps0,
-                                              false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[t], pb[t], 2, 3), one, ps1,
-                                              false);
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[t], pb[t], 4, 5), one, ps0,
-                                              false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[t], pb[t], 6, 7), one, ps1,
-                                              false);
-      }
-      return ps0 + ps1;
-    };
-    float psum = expsum();
-    const bool need = !(psum <= kDecSumMax) || m == -INFINITY;
-    if (__any(need)) {
-      // move the reference of the queries that need it to their chunk max;
-      // a query's scores live in lanes r16 + 16 g, g = 0..3
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, st[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      float nf = need ? 1.f : 0.f;
-      nf = fmaxf(nf, __shfl_xor(nf, 16));
-      nf = fmaxf(nf, __shfl_xor(nf, 32));
-      const bool grow = nf > 0.f && mt > -INFINITY;
-      const float delta = grow ? mt : 0.f;
-      const float alpha = grow ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-mt)) : 1.f;
-      lsum *= alpha;
-      if (grow) m = (m == -INFINITY ? 0.f : m) + mt;
-      const float nm = m == -INFINITY ? 0.f : -m;
-      negm = df32x4{nm, nm, nm, nm};
-      // output rows of this lane are queries 4 g16 + r, held as r16 by lane 4 g16 + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float al = __shfl(alpha, 4 * g16 + r);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db][r] *= al;
-      }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[kb][r] -= delta;
-      psum = expsum();
-    }
-    lsum += psum;
-    // ---- O += P V, the V operand through transpose reads of the LDS chunk
-    // LDS operations of a wave complete in order; keep the compiler from
-    // moving the reads above this wave's stores (other lanes' data)
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int kst = 0; kst < 2; ++kst)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        ds4v lo, hi;
-        {
-          const int row = 32 * kst + 4 * g16 + (r16 >> 2);
-          const int col = 16 * db + 4 * (r16 & 3);
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) ds4v*)(vb + row * VROW + 2 * col));
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) ds4v*)(vb + (row + 16) * VROW + 2 * col));
-        }
-        const db8v vop = __builtin_bit_cast(db8v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[kst], vop, acc[db], 0, 0, 0);
-      }
+  // chunk i + 1 (K in registers, V in the other LDS stage) is in flight
+  // while chunk i is computed. The next chunk is always issued: its keys are
+  // clamped to the split, so past the end it re-reads the last key (from L2)
+  // and the loads need no branch.
+  DecBuf<D> bA, bB;
+  uint8_t* sA = vstA[wave];
+  uint8_t* sB = vstB[wave];
+  int k0 = k_lo;
+  dec_issue_k<D>(c, k0, bA);
+  dec_issue_v<D>(c, k0, sA);
+  for (;;) {
+    dec_issue_k<D>(c, k0 + DEC_CHUNK, bB);
+    dec_issue_v<D>(c, k0 + DEC_CHUNK, sB);
+    __builtin_amdgcn_sched_barrier(0);  // all of the next chunk's loads go out first
+    dec_chunk<D>(c, k0, bA, qa, qr, w2pi_s, sA, st);
+    if (k0 + DEC_CHUNK >= c.k_hi) break;
+    dec_issue_k<D>(c, k0 + 2 * DEC_CHUNK, bA);
+    dec_issue_v<D>(c, k0 + 2 * DEC_CHUNK, sA);
+    __builtin_amdgcn_sched_barrier(0);
+    dec_chunk<D>(c, k0 + DEC_CHUNK, bB, qa, qr, w2pi_s, sB, st);
+    if (k0 + 2 * DEC_CHUNK >= c.k_hi) break;
+    k0 += 2 * DEC_CHUNK;
   }
+  // no transfer into this workgroup's LDS may outlive it
+  __builtin_amdgcn_s_waitcnt(0);
+  const float m = st.m, lsum = st.lsum;
+  df32x4 (&acc)[NDB] = st.acc;
   // ---- split partial: m (log2 domain), l, unnormalised O for each query head
   float lt = lsum + __shfl_xor(lsum, 16);
   lt += __shfl_xor(lt, 32);
@@ -498,54 +581,52 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   }
 }
 
-// Merge of the split partials of one query head with LSE weights.
-// Workgroup (head h, 16 output dims): the reference max over splits and one
-// weight per split (in LDS), then 16 split groups x 16 dims accumulate and
-// reduce through LDS.
+// Merge of the split partials of one query head with LSE weights, one pass:
+// workgroup (head h, 16 output dims), thread (split group g of 16, dim):
+// each thread folds its splits s = g, g + 16, ... with a running maximum
+// (all loads independent of the arithmetic, so they are in flight together),
+// then the 16 groups are combined through LDS.
 template <bool F32, int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
-  __shared__ float wts[1024];
-  __shared__ float red[256];
+  __shared__ float rm[256], rl[256], ra[256];
   const int h = blockIdx.x, d0 = 16 * blockIdx.y, tid = threadIdx.x;
-  const float* pp = a.part + (int64_t)h * a.S * (D + 2);
-  float M = -INFINITY;
-  for (int s = tid; s < a.S; s += 256) M = fmaxf(M, pp[(int64_t)s * (D + 2)]);
-  red[tid] = M;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
-  float L = 0.f;
-  for (int s = tid; s < a.S; s += 256) {
-    const float ms = pp[(int64_t)s * (D + 2)];
-    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    wts[s] = w;
-    L += w * pp[(int64_t)s * (D + 2) + 1];
-  }
-  red[tid] = L;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  L = red[0];
-  __syncthreads();
   const int dd = tid & 15, grp = tid >> 4;
-  float A = 0.f;
+  const float* pp = a.part + (int64_t)h * a.S * (D + 2);
+  float M = -INFINITY, L = 0.f, A = 0.f;
 #pragma unroll 4
-  for (int s = grp; s < a.S; s += 16) A += wts[s] * pp[(int64_t)s * (D + 2) + 2 + d0 + dd];
-  red[tid] = A;
+  for (int s = grp; s < a.S; s += 16) {
+    const float* q = pp + (int64_t)s * (D + 2);
+    const float ms = q[0], ls = q[1], as = q[2 + d0 + dd];
+    if (ms > M) {  // -inf partials (no keys) never pass
+      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - ms);
+      L *= sc;
+      A *= sc;
+      M = ms;
+    }
+    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    L += w * ls;
+    A += w * as;
+  }
+  rm[tid] = M;
+  rl[tid] = L;
+  ra[tid] = A;
   __syncthreads();
   if (grp == 0) {
+    float Mt = -INFINITY;
 #pragma unroll
-    for (int g = 1; g < 16; ++g) A += red[tid + 16 * g];
-    const float out = A / L;
+    for (int g = 0; g < 16; ++g) Mt = fmaxf(Mt, rm[16 * g + dd]);
+    float Lt = 0.f, At = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const float mg = rm[16 * g + dd];
+      const float w = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg - Mt);
+      Lt += w * rl[16 * g + dd];
+      At += w * ra[16 * g + dd];
+    }
+    const float out = At / Lt;
     if constexpr (F32) ((float*)a.o)[(int64_t)h * D + d0 + dd] = out;
     else ((uint16_t*)a.o)[(int64_t)h * D + d0 + dd] = f32_to_bf16_bits(out);
-    if (a.lse && d0 + dd == 0) a.lse[h] = (M + __log2f(L)) * 0.69314718055994530942f;
+    if (a.lse && d0 + dd == 0) a.lse[h] = (Mt + __log2f(Lt)) * 0.69314718055994530942f;
   }
 }
 

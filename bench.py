@@ -12,9 +12,10 @@ time (effective TFLOP/s).
 Also reported (not part of the timed step): the attention kernel alone (live
 HIP events around it, for the roofline), the library's plain causal RoPE
 attention at the same shape (overhead ratio), the Eq. 7 inclusion-exclusion
-alternative, the 64K and packed-varlen workloads, decode latency at positions
-32767 .. 131071 of a 131072-key cache with L2 / MALL flushed before every
-step, and the float64 CPU oracle on a bounded sample of rows.
+alternative, the 64K and packed-varlen workloads, a window-size sweep, decode latency
+at positions 32767 .. 131071 of a 131072-key cache with L2 / MALL evicted
+before every step, calibrated HBM-read and MFMA ceilings, and the float64 CPU
+oracle on a bounded sample of rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -84,6 +85,28 @@ def main():
 
     def up(a):
         return torch.from_numpy(a).to(torch.bfloat16).to(dev).contiguous()
+
+    # ------------------------------------------------- calibrated ceilings
+    log("calibration: streaming HBM read and pure bf16 MFMA rate")
+    cev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    rbuf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    rts = []
+    for _ in range(6):
+        jl.calib_stream_read(rbuf, events=cev)
+        torch.cuda.synchronize()
+        rts.append(cev[0].elapsed_time(cev[1]))
+    read_gbs = rbuf.numel() * 4 / (float(np.median(rts[1:])) * 1e-3) / 1e9
+    del rbuf
+    mts = []
+    for _ in range(4):
+        mfl = jl.calib_mfma_bf16(512, 20000, events=cev)
+        torch.cuda.synchronize()
+        mts.append(cev[0].elapsed_time(cev[1]))
+    mfma_tflops = mfl / (float(np.median(mts[1:])) * 1e-3) / 1e12
+    calib = {"hbm_read_GBps": round(read_gbs, 1), "mfma_bf16_TFLOPs": round(mfma_tflops, 1),
+             "method": "jl_calib_stream_read over 1 GiB (median of 5); jl_calib_mfma_bf16, "
+                       "2048 waves x 20000 rounds of 4 independent 32x32x16 MFMAs (median of 3)"}
+    log(f"calibrated ceilings: HBM read {read_gbs:.0f} GB/s, bf16 MFMA {mfma_tflops:.0f} TFLOP/s")
 
     c = WORKLOADS["prefill_128k"]
     L, Hq, Hkv, d = c["lengths"][0], c["Hq"], c["Hkv"], c["d"]
@@ -159,7 +182,10 @@ def main():
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kern_avg, 4),
-                     "kernel_ms_min": round(min(kern_ms), 4)},
+                     "kernel_ms_min": round(min(kern_ms), 4),
+                     "calibrated_peak": calib["mfma_bf16_TFLOPs"],
+                     "frac_of_calibrated": round(achieved / calib["mfma_bf16_TFLOPs"], 4)},
+        "calibration": calib,
     }
     del ev
 
@@ -201,12 +227,30 @@ def main():
         del ws_ie, ratio
         torch.cuda.empty_cache()
 
+        # ---------------------------------------------------- w0 sweep
+        log("window sweep at 128K (fused attention kernel)")
+        sweep = {}
+        for w in (0, 512, 1024, 2048, 4096):
+            jl.bifocal_prefill(q, k, vv, w, w_pre, theta, out=o, lse=lse, workspace=ws)
+            torch.cuda.synchronize()
+            wt = []
+            for _ in range(2):
+                jl.bifocal_prefill(q, k, vv, w, w_pre, theta, out=o, lse=lse, workspace=ws,
+                                   events=pe)
+                torch.cuda.synchronize()
+                wt.append(pe[0].elapsed_time(pe[1]))
+            wm = float(np.median(wt))
+            sweep[str(w)] = {"kernel_ms": round(wm, 4), "tflops": round(flops / wm / 1e9, 2),
+                             "vs_plain": round(wm / plain_ms, 4)}
+        extras["w0_sweep_128k"] = sweep
+
         # ---------------------------------------------------- decode
         log("decode on the 131072-key absolute cache (L2/MALL evicted by a clean read per step)")
         cdec = WORKLOADS["decode_128k"]
-        # clean 1 GiB read between steps: evicts the cache from L2 and the
-        # memory-side cache without leaving dirty lines behind (a zero-fill
-        # would make the timed step pay for its write-backs)
+        # Two cache states between steps: a clean 1 GiB read (evicts L2 and the
+        # memory-side cache and leaves no dirty lines) and a 1 GiB zero-fill
+        # (evicts too, but leaves dirty lines whose write-back the timed step
+        # then pays for). The clean read is the headline state.
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         wsd = torch.empty(jl.decode_workspace_size(L, Hq, d), dtype=torch.uint8, device=dev)
         od = torch.empty((Hq, d), dtype=torch.bfloat16, device=dev)
@@ -217,27 +261,35 @@ def main():
             qd = q[pos].contiguous()
             row = {}
             for mode in ("fused", "plain"):
-                ts = []
-                for it in range(args.decode_iters + 3):
-                    flush.sum()
-                    jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta, mode=mode, out=od,
-                                      lse=ld, workspace=wsd, events=de)
-                    torch.cuda.synchronize()
-                    if it >= 3:
-                        ts.append(de[0].elapsed_time(de[1]) * 1e3)  # us
-                nbytes = 4.0 * (pos + 1) * Hkv * d
-                med = float(np.median(ts))
-                row[mode] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
-                             "us_p90": round(pct(ts, 90), 2),
-                             "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
-                             "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 /
-                                                   PEAK_HBM_GBS, 2)}
+                for evict in ("read", "write"):
+                    ts = []
+                    for it in range(args.decode_iters + 3):
+                        if evict == "read":
+                            flush.sum()
+                        else:
+                            flush.zero_()
+                        jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta, mode=mode,
+                                          out=od, lse=ld, workspace=wsd, events=de)
+                        torch.cuda.synchronize()
+                        if it >= 3:
+                            ts.append(de[0].elapsed_time(de[1]) * 1e3)  # us
+                    nbytes = 4.0 * (pos + 1) * Hkv * d
+                    med = float(np.median(ts))
+                    key = mode if evict == "read" else mode + "_after_zero_fill"
+                    row[key] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
+                                "us_p90": round(pct(ts, 90), 2),
+                                "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 /
+                                                      PEAK_HBM_GBS, 2),
+                                "pct_calibrated_read": round(100 * nbytes / (med * 1e-6) / 1e9 /
+                                                             read_gbs, 2)}
             row["G"] = jl.group_size(pos + 1, w_pre)
             row["overhead_ratio"] = round(row["fused"]["us_median"] / row["plain"]["us_median"],
                                           4)
             dec[str(pos)] = row
             log(f"decode pos={pos}: {row['fused']['us_median']} us "
-                f"({row['fused']['pct_hbm_peak']}% HBM), plain {row['plain']['us_median']} us")
+                f"({row['fused']['pct_hbm_peak']}% HBM, {row['fused']['pct_calibrated_read']}% "
+                f"of the calibrated read rate), plain {row['plain']['us_median']} us")
         result["decode"] = dec
         del flush, wsd
         torch.cuda.empty_cache()

@@ -182,6 +182,18 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
  * jl_tile_class and an independent definition. */
 int jl_debug_tile_classes(int64_t L, int64_t w0, int8_t* out_dev, void* stream);
 
+/* Calibration kernels (not part of the method) for the rooflines reported
+ * beside the vendor peaks. jl_calib_stream_read reads `bytes` bytes at `src`
+ * (device, 16-byte aligned, bytes a multiple of 16) once, with `blocks`
+ * workgroups of 256 threads; *sink (device uint32) is left untouched unless
+ * the reads xor to one fixed value. jl_calib_mfma_bf16 runs `iters` rounds of
+ * four independent 32x32x16 bf16 MFMAs per wave in `blocks` workgroups of 256
+ * threads and writes one float per thread to sink (device, blocks * 256
+ * floats); one round is 4 * 32768 FLOP per wave. Both only launch on
+ * `stream`; time them with the caller's events. JL_EINVAL on bad arguments. */
+int jl_calib_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream);
+int jl_calib_mfma_bf16(float* sink, int blocks, int iters, void* stream);
+
 /* Static English text for a status code; never NULL. */
 const char* jl_status_string(int status);
 

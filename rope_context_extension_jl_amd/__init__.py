@@ -17,7 +17,7 @@ __all__ = [
     "LIB_PATH", "BifocalError", "lib", "group_size", "tile_class", "prefill_tile_shape",
     "status_string", "rope_apply", "prefill_workspace_size", "bifocal_prefill",
     "decode_workspace_size", "bifocal_decode", "debug_tile_classes", "ie_ratio_view",
-    "MODES",
+    "calib_stream_read", "calib_mfma_bf16", "MODES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbifocal.so")
@@ -50,6 +50,8 @@ _SIGS = {
                                          _c_int, _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int,
                                          _c_int, _c_int, _c_p, _c_sz, _c_p, _c_p, _c_p]),
     "jl_debug_tile_classes": (_c_int, [_c_i64, _c_i64, _c_p, _c_p]),
+    "jl_calib_stream_read": (_c_int, [_c_p, _c_sz, _c_p, _c_int, _c_p]),
+    "jl_calib_mfma_bf16": (_c_int, [_c_p, _c_int, _c_int, _c_p]),
     "jl_status_string": (ctypes.c_char_p, [_c_int]),
     "jl_last_hip_error": (_c_int, []),
 }
@@ -241,3 +243,29 @@ def debug_tile_classes(L: int, w0: int, device="cuda") -> torch.Tensor:
     _check("jl_debug_tile_classes", lib().jl_debug_tile_classes(int(L), int(w0), _dev(out, "out"),
                                                                 _stream(out.device)))
     return out
+
+
+def calib_stream_read(buf: torch.Tensor, events=None, blocks: int = 2048) -> None:
+    """One streaming read of `buf` (device) by the calibration kernel; the
+    optional (begin, end) events bracket it on the current stream."""
+    sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    s = torch.cuda.current_stream(buf.device)
+    if events is not None:
+        events[0].record(s)
+    _check("jl_calib_stream_read", lib().jl_calib_stream_read(
+        _dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"), int(blocks),
+        _stream(buf.device)))
+    if events is not None:
+        events[1].record(s)
+
+
+def calib_mfma_bf16(blocks: int, iters: int, events=None, device="cuda") -> float:
+    """Runs the MFMA calibration kernel; returns its FLOP count."""
+    sink = torch.empty(int(blocks) * 256, dtype=torch.float32, device=device)
+    if events is not None:
+        events[0].record(torch.cuda.current_stream(sink.device))
+    _check("jl_calib_mfma_bf16", lib().jl_calib_mfma_bf16(_dev(sink, "sink"), int(blocks),
+                                                          int(iters), _stream(sink.device)))
+    if events is not None:
+        events[1].record(torch.cuda.current_stream(sink.device))
+    return 4.0 * 32768.0 * 4 * int(blocks) * int(iters)

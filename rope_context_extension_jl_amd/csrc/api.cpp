@@ -232,13 +232,25 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
   const int64_t keys = pos + 1;
   int S = num_splits;
   if (S == 0) {
-    // bf16: one wave per split, up to ~8 waves per CU over the KV heads, at
-    // least 256 keys per split (fewer partials to merge at short contexts);
-    // float32: one workgroup per split, ~4 per CU, at least 64 keys.
-    const int64_t min_keys = dt == JL_BF16 ? 256 : 64;
-    int64_t want = ((dt == JL_BF16 ? 2048 : 1024) + Hkv - 1) / Hkv;
-    int64_t by_keys = (keys + min_keys - 1) / min_keys;
-    S = (int)(want < by_keys ? want : by_keys);
+    if (dt == JL_BF16) {
+      // one wave per split, four KV heads per workgroup, two workgroups fit a
+      // CU: pick the split count so the workgroups cover the 256 CUs evenly
+      // (two per CU when each split gets >= 256 keys, else one), since a few
+      // CUs holding an extra workgroup would set the kernel's time
+      const int64_t hg = (Hkv + 3) / 4;
+      const int64_t s_full = 512 / hg > 0 ? 512 / hg : 1, s_half = 256 / hg > 0 ? 256 / hg : 1;
+      int64_t want;
+      if (keys >= 256 * s_full) want = s_full;
+      else if (keys >= 128 * s_half) want = s_half;
+      else want = (keys + 127) / 128;
+      S = (int)want;
+    } else {
+      // float32: one workgroup per split, ~4 per CU, at least 64 keys
+      int64_t want = (1024 + Hkv - 1) / Hkv;
+      int64_t by_keys = (keys + 63) / 64;
+      S = (int)(want < by_keys ? want : by_keys);
+    }
+    if (S > maxs) S = maxs;
   }
   if (S < 1) S = 1;
   if (S > maxs) return JL_EINVAL;
@@ -273,6 +285,18 @@ int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, vo
 int jl_debug_tile_classes(int64_t L, int64_t w0, int8_t* out_dev, void* stream) {
   if (L < 1 || L > (int64_t)1 << 24 || w0 < 0 || !out_dev) return JL_EINVAL;
   return hip_status(launch_tile_dump(L, w0, out_dev, (hipStream_t)stream));
+}
+
+int jl_calib_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                         void* stream) {
+  if (!src || !sink || bytes < 16 || (bytes & 15) || (((uintptr_t)src) & 15) || blocks < 1)
+    return JL_EINVAL;
+  return hip_status(launch_calib_read(src, bytes, sink, blocks, (hipStream_t)stream));
+}
+
+int jl_calib_mfma_bf16(float* sink, int blocks, int iters, void* stream) {
+  if (!sink || blocks < 1 || iters < 1) return JL_EINVAL;
+  return hip_status(launch_calib_mfma(sink, blocks, iters, (hipStream_t)stream));
 }
 
 const char* jl_status_string(int status) {

@@ -102,6 +102,10 @@ hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o
 
 hipError_t launch_tile_dump(int64_t L, int64_t w0, int8_t* out, hipStream_t st);
 
+hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                             hipStream_t st);
+hipError_t launch_calib_mfma(float* sink, int blocks, int iters, hipStream_t st);
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------

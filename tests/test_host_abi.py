@@ -189,3 +189,15 @@ def test_python_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         jl.bifocal_prefill(x, x[:, :1].contiguous(), x[:, :1].contiguous(), 1, 4, 1e4,
                            workspace=torch.zeros(1, dtype=torch.uint8))
+
+
+def test_calibration_argument_errors():
+    f, g = jl.lib().jl_calib_stream_read, jl.lib().jl_calib_mfma_bf16
+    assert f(None, 1024, P, 16, None) == -1
+    assert f(P, 1000, P, 16, None) == -1          # not a multiple of 16 bytes
+    assert f(ctypes.c_void_p(24), 1024, P, 16, None) == -1  # not 16-byte aligned
+    assert f(P, 1024, None, 16, None) == -1
+    assert f(P, 1024, P, 0, None) == -1
+    assert g(None, 4, 10, None) == -1
+    assert g(P, 0, 10, None) == -1
+    assert g(P, 4, 0, None) == -1

@@ -44,9 +44,10 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of the sources the fused attention kernel is compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rope_context_extension_jl_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ("jl_internal.hpp", "prefill_bf16.hip"):
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]

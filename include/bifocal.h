@@ -141,6 +141,48 @@ int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void
                              float scale, jl_dtype dt, jl_mode mode, void* workspace,
                              size_t ws_bytes, void* stream, void* ev_begin, void* ev_end);
 
+/* Bytes of device workspace jl_bifocal_prefill_cached needs for a chunk of
+ * Tq query rows starting at position q_off (mode FUSED or PLAIN, d = 128);
+ * 0 for arguments it would reject. */
+size_t jl_prefill_cached_workspace_size(int64_t q_off, int64_t Tq, int Hq, int Hkv, int d,
+                                        jl_mode mode);
+
+/* Prefill continued on an existing absolute cache (chunked prefill): the
+ * Tq query rows at positions q_off .. q_off + Tq - 1 of one sequence attend
+ * causally to keys 0 .. q_off + Tq - 1 held in the cache, with
+ * L = q_off + Tq and G = max(1, ceil(L / w_pre)) (Eq. 1 with the "Dynamic
+ * group size" of the whole sequence so far). The cache keeps keys rotated at
+ * their absolute positions, so a chunk that moves L across a multiple of
+ * w_pre (G changes) needs no re-rotation of the cache: remote keys get
+ * R_{f(k) - k} on the fly ("KV cache invariant" paragraph; Pith ledger
+ * Sec. 3.2 Eqs. 5-6).
+ *   xq      [Tq, Hq, d]        RAW queries of the chunk (bf16)
+ *   kcache  [capacity, Hkv, d] keys rotated at absolute positions, rows
+ *                              0 .. q_off + Tq - 1 filled (the chunk's own
+ *                              keys included, e.g. written by jl_rope_apply
+ *                              with pos_offset = q_off); never written
+ *   vcache  [capacity, Hkv, d] values, same rows; never written
+ *   o       [Tq, Hq, d] bf16; lse [Hq, Tq] float32 (natural log) or NULL.
+ * q_off = 0 is an ordinary single-sequence prefill from the cache; Tq = 1
+ * is one decode step. Supported: bf16, d = 128, JL_MODE_FUSED or
+ * JL_MODE_PLAIN (JL_MODE_IE: JL_EUNSUPPORTED). Errors: JL_EINVAL (q_off < 0,
+ * Tq < 0, q_off + Tq > capacity, bad heads or scalars, NULL pointers),
+ * JL_EUNSUPPORTED, JL_EWORKSPACE, JL_EHIP. Tq = 0 is a no-op. */
+int jl_bifocal_prefill_cached(const void* xq, const void* kcache, const void* vcache, void* o,
+                              float* lse, int64_t q_off, int64_t Tq, int64_t capacity, int Hq,
+                              int Hkv, int d, int64_t w0, int64_t w_pre, double theta, float scale,
+                              jl_dtype dt, jl_mode mode, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* jl_bifocal_prefill_cached plus timing: ev_begin / ev_end (caller-created
+ * hipEvent_t, or NULL) bracket the attention kernel on `stream`. */
+int jl_bifocal_prefill_cached_timed(const void* xq, const void* kcache, const void* vcache,
+                                    void* o, float* lse, int64_t q_off, int64_t Tq,
+                                    int64_t capacity, int Hq, int Hkv, int d, int64_t w0,
+                                    int64_t w_pre, double theta, float scale, jl_dtype dt,
+                                    jl_mode mode, void* workspace, size_t ws_bytes, void* stream,
+                                    void* ev_begin, void* ev_end);
+
 /* Bytes of device workspace jl_bifocal_decode needs (for any pos < capacity
  * and any num_splits it would choose or accept). */
 size_t jl_decode_workspace_size(int64_t capacity, int Hq, int d);

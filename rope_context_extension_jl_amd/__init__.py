@@ -17,6 +17,7 @@ __all__ = [
     "LIB_PATH", "BifocalError", "lib", "group_size", "tile_class", "prefill_tile_shape",
     "status_string", "rope_apply", "prefill_workspace_size", "bifocal_prefill",
     "decode_workspace_size", "bifocal_decode", "debug_tile_classes", "ie_ratio_view",
+    "prefill_cached_workspace_size", "bifocal_prefill_cached",
     "calib_stream_read", "calib_mfma_bf16", "MODES",
 ]
 
@@ -42,6 +43,15 @@ _SIGS = {
     "jl_bifocal_prefill_timed": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int,
                                           _c_i64, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_dbl,
                                           _c_flt, _c_int, _c_int, _c_p, _c_sz, _c_p, _c_p, _c_p]),
+    "jl_prefill_cached_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_int, _c_int, _c_int,
+                                                 _c_int]),
+    "jl_bifocal_prefill_cached": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                           _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_dbl, _c_flt,
+                                           _c_int, _c_int, _c_p, _c_sz, _c_p]),
+    "jl_bifocal_prefill_cached_timed": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64,
+                                                 _c_i64, _c_int, _c_int, _c_int, _c_i64, _c_i64,
+                                                 _c_dbl, _c_flt, _c_int, _c_int, _c_p, _c_sz,
+                                                 _c_p, _c_p, _c_p]),
     "jl_decode_workspace_size": (_c_sz, [_c_i64, _c_int, _c_int]),
     "jl_bifocal_decode": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_int,
                                    _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int, _c_int, _c_int,
@@ -159,6 +169,11 @@ def prefill_workspace_size(T, B, Hq, Hkv, d, dtype=torch.bfloat16, mode="fused")
     return int(n)
 
 
+def prefill_cached_workspace_size(q_off, Tq, Hq, Hkv, d, mode="fused") -> int:
+    return int(lib().jl_prefill_cached_workspace_size(int(q_off), int(Tq), int(Hq), int(Hkv),
+                                                      int(d), MODES[mode]))
+
+
 def decode_workspace_size(capacity, Hq, d) -> int:
     return int(lib().jl_decode_workspace_size(int(capacity), int(Hq), int(d)))
 
@@ -209,6 +224,33 @@ def ie_ratio_view(workspace: torch.Tensor, T, B, Hq, Hkv, d, dtype=torch.bfloat1
     code = JL_BF16 if dtype == torch.bfloat16 else JL_FP32
     off = int(lib().jl_prefill_ie_ratio_offset(T, B, Hq, Hkv, d, code))
     return workspace[off: off + Hq * T * 4].view(torch.float32).view(Hq, T)
+
+
+def bifocal_prefill_cached(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                           q_off: int, w0: int, w_pre: int, theta: float, scale: float = 0.0,
+                           mode: str = "fused", out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                           events=None):
+    """Chunked prefill: RAW queries xq [Tq, Hq, d] at positions q_off .. q_off+Tq-1
+    against the absolute cache [capacity, Hkv, d] (rows up to q_off+Tq-1 filled).
+    Returns (o [Tq, Hq, d], lse [Hq, Tq])."""
+    Tq, Hq, d = xq.shape
+    C, Hkv, _ = kcache.shape
+    if out is None:
+        out = torch.empty_like(xq)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=xq.device)
+    if workspace is None:
+        need = prefill_cached_workspace_size(q_off, Tq, Hq, Hkv, d, mode)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
+    st = lib().jl_bifocal_prefill_cached_timed(
+        _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
+        _dev(lse, "lse"), int(q_off), Tq, C, Hq, Hkv, d, int(w0), int(w_pre), float(theta),
+        float(scale), _dtype_code(xq), MODES[mode], _dev(workspace, "workspace"),
+        workspace.numel(), _stream(xq.device), *_events(events))
+    _check("jl_bifocal_prefill_cached", st)
+    return out, lse
 
 
 def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, pos: int,

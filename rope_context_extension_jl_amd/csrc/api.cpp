@@ -143,11 +143,12 @@ int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void
   make_freqs(fr, d, theta);
   hipStream_t st = (hipStream_t)stream;
   const int bm = dt == JL_BF16 ? PF_BM : PF32_BM;
-  hipError_t e = launch_prefill_plan(cu_seqlens, B, T, w_pre, bm, workspace, lay, st);
+  hipError_t e = launch_prefill_plan(cu_seqlens, B, T, 0, w_pre, bm, workspace, lay, st);
   if (e != hipSuccess) return hip_status(e);
   const int need_rem = mode != JL_MODE_PLAIN;
   if (dt == JL_BF16) {
-    e = launch_prefill_prep_bf16(xk, v, kcache_out, T, B, Hkv, need_rem, fr, workspace, lay, st);
+    e = launch_prefill_prep_bf16(xk, v, kcache_out, T, B, Hkv, need_rem, 0,
+                                 sc * 1.4426950408889634f, fr, workspace, lay, st);
     if (e != hipSuccess) return hip_status(e);
     if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
       return hip_status(e);
@@ -158,13 +159,13 @@ int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void
       const int passes[3] = {PASS_IE_A, PASS_IE_B, PASS_IE_C};
       for (int i = 0; i < 3; ++i) {
         e = launch_prefill_bf16(passes[i], xq, base_o + i * on, base_l + i * ln, T, B, Hq, Hkv,
-                                w0, sc, fr, workspace, lay, st);
+                                w0, 0, sc, fr, workspace, lay, st);
         if (e != hipSuccess) return hip_status(e);
       }
       e = launch_ie_merge(o, lse, 0, T, Hq, d, workspace, lay, st);
     } else {
       e = launch_prefill_bf16(mode == JL_MODE_PLAIN ? PASS_PLAIN : PASS_FUSED, xq, o, lse, T, B,
-                              Hq, Hkv, w0, sc, fr, workspace, lay, st);
+                              Hq, Hkv, w0, 0, sc, fr, workspace, lay, st);
     }
   } else {
     e = launch_prefill_prep_f32(xk, kcache_out, T, B, Hkv, d, need_rem, fr, workspace, lay, st);
@@ -199,6 +200,66 @@ int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, f
   return jl_bifocal_prefill_timed(xq, xk, v, o, lse, kcache_out, cu_seqlens, B, T, Hq, Hkv, d, w0,
                                   w_pre, theta, scale, dt, mode, workspace, ws_bytes, stream,
                                   nullptr, nullptr);
+}
+
+// ---- prefill continued on an existing absolute cache
+static bool cached_shape_ok(int64_t q_off, int64_t Tq, int Hq, int Hkv) {
+  if (q_off < 0 || Tq < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv) return false;
+  return q_off + Tq <= (int64_t)INT32_MAX / 2;
+}
+
+size_t jl_prefill_cached_workspace_size(int64_t q_off, int64_t Tq, int Hq, int Hkv, int d,
+                                        jl_mode mode) {
+  if (!cached_shape_ok(q_off, Tq, Hq, Hkv) || d != PF_D) return 0;
+  if (mode != JL_MODE_FUSED && mode != JL_MODE_PLAIN) return 0;
+  return prefill_layout(q_off + Tq, 1, Hq, Hkv, d, JL_BF16, mode).total;
+}
+
+int jl_bifocal_prefill_cached_timed(const void* xq, const void* kcache, const void* vcache,
+                                    void* o, float* lse, int64_t q_off, int64_t Tq,
+                                    int64_t capacity, int Hq, int Hkv, int d, int64_t w0,
+                                    int64_t w_pre, double theta, float scale, jl_dtype dt,
+                                    jl_mode mode, void* workspace, size_t ws_bytes, void* stream,
+                                    void* ev_begin, void* ev_end) {
+  if (!cached_shape_ok(q_off, Tq, Hq, Hkv)) return JL_EINVAL;
+  if (capacity < 1 || q_off + Tq > capacity) return JL_EINVAL;
+  if (w0 < 0 || w_pre < 1 || !(theta > 1.0) || !(scale == scale)) return JL_EINVAL;
+  if (dt != JL_BF16 && dt != JL_FP32) return JL_EINVAL;
+  if (mode == JL_MODE_IE) return JL_EUNSUPPORTED;
+  if (mode != JL_MODE_FUSED && mode != JL_MODE_PLAIN) return JL_EINVAL;
+  if (dt != JL_BF16 || d != PF_D) return JL_EUNSUPPORTED;
+  if (w0 > (int64_t)INT32_MAX) w0 = INT32_MAX;
+  if (Tq == 0) return JL_OK;
+  if (!xq || !kcache || !vcache || !o) return JL_EINVAL;
+  const int64_t L = q_off + Tq;
+  const PrefillLayout lay = prefill_layout(L, 1, Hq, Hkv, d, dt, mode);
+  if (!workspace || ws_bytes < lay.total) return JL_EWORKSPACE;
+  if (((uintptr_t)workspace) & 255) return JL_EINVAL;
+  const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d));
+  RopeFreqs fr;
+  make_freqs(fr, d, theta);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_prefill_plan(nullptr, 1, L, q_off, w_pre, PF_BM, workspace, lay, st);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_prefill_prep_bf16(kcache, vcache, nullptr, L, 1, Hkv, mode != JL_MODE_PLAIN, 1,
+                               sc * 1.4426950408889634f, fr, workspace, lay, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
+    return hip_status(e);
+  e = launch_prefill_bf16(mode == JL_MODE_PLAIN ? PASS_PLAIN : PASS_FUSED, xq, o, lse, Tq, 1, Hq,
+                          Hkv, w0, q_off, sc, fr, workspace, lay, st);
+  if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
+  return hip_status(e);
+}
+
+int jl_bifocal_prefill_cached(const void* xq, const void* kcache, const void* vcache, void* o,
+                              float* lse, int64_t q_off, int64_t Tq, int64_t capacity, int Hq,
+                              int Hkv, int d, int64_t w0, int64_t w_pre, double theta, float scale,
+                              jl_dtype dt, jl_mode mode, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  return jl_bifocal_prefill_cached_timed(xq, kcache, vcache, o, lse, q_off, Tq, capacity, Hq, Hkv,
+                                         d, w0, w_pre, theta, scale, dt, mode, workspace, ws_bytes,
+                                         stream, nullptr, nullptr);
 }
 
 static int decode_max_splits(int64_t capacity) {

@@ -72,16 +72,22 @@ hipError_t launch_rope_apply(void* x, int64_t T, int H, int d, const int32_t* cu
                              int64_t pos_offset, const RopeFreqs& fr, int is_f32,
                              hipStream_t st);
 
-hipError_t launch_prefill_plan(const int32_t* cu, int B, int64_t T, int64_t w_pre, int bm,
-                               void* ws, const PrefillLayout& lay, hipStream_t st);
+// qoff: position of the first query row of a single sequence (0 = all rows
+// are queries); the query tiles then cover rows qoff .. T-1.
+hipError_t launch_prefill_plan(const int32_t* cu, int B, int64_t T, int64_t qoff, int64_t w_pre,
+                               int bm, void* ws, const PrefillLayout& lay, hipStream_t st);
 
+// from_abs: the keys are already rotated at their absolute positions.
+// kscale multiplies the fp16 key operands (not the bf16 cache written).
 hipError_t launch_prefill_prep_bf16(const void* xk, const void* v, void* kcache_out, int64_t T,
-                                    int B, int Hkv, int need_rem, const RopeFreqs& fr, void* ws,
-                                    const PrefillLayout& lay, hipStream_t st);
+                                    int B, int Hkv, int need_rem, int from_abs, float kscale,
+                                    const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
+                                    hipStream_t st);
 
 hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, int64_t T, int B,
-                               int Hq, int Hkv, int64_t w0, float scale, const RopeFreqs& fr,
-                               void* ws, const PrefillLayout& lay, hipStream_t st);
+                               int Hq, int Hkv, int64_t w0, int64_t qoff, float scale,
+                               const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
+                               hipStream_t st);
 
 hipError_t launch_prefill_prep_f32(const void* xk, void* kcache_out, int64_t T, int B, int Hkv,
                                    int d, int need_rem, const RopeFreqs& fr, void* ws,

@@ -75,7 +75,8 @@ __device__ inline int block_excl_scan(int v, int* sh) {
 }
 
 __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(
-    const int32_t* __restrict__ cu, int B, int T, int64_t w_pre, int bm, int* __restrict__ hdr,
+    const int32_t* __restrict__ cu, int B, int T, int qoff, int64_t w_pre, int bm,
+    int* __restrict__ hdr,
     SeqInfo* __restrict__ seqs, int* __restrict__ order, int* __restrict__ tact,
     int* __restrict__ tbase) {
   // Every value one thread produces for another goes through LDS (B <= 4096).
@@ -92,7 +93,9 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(
     const int e = cu ? cu[b + 1] : T;
     const int len = e > s ? e - s : 0;
     len_s[b] = len;
-    nt_s[b] = (len + bm - 1) / bm;
+    // query tiles: the rows from qoff on (qoff > 0 only for one sequence
+    // continued on an existing cache: its first qoff rows are keys only)
+    nt_s[b] = (len - qoff + bm - 1) / bm;
     atomicMax(&maxnt_s, nt_s[b]);
     seqs[b].start = s;
     seqs[b].len = len;
@@ -156,14 +159,14 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(
   }
 }
 
-hipError_t launch_prefill_plan(const int32_t* cu, int B, int64_t T, int64_t w_pre, int bm,
-                               void* ws, const PrefillLayout& lay, hipStream_t st) {
+hipError_t launch_prefill_plan(const int32_t* cu, int B, int64_t T, int64_t qoff, int64_t w_pre,
+                               int bm, void* ws, const PrefillLayout& lay, hipStream_t st) {
   char* w = (char*)ws;
   int* order = (int*)(w + lay.tiles);
   int* tact = order + B;
   int* tbase = tact + (lay.max_tiles + 1);
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, cu, B, (int)T,
-                     w_pre, bm, (int*)(w + lay.hdr), (SeqInfo*)(w + lay.seqs), order, tact, tbase);
+                     (int)qoff, w_pre, bm, (int*)(w + lay.hdr), (SeqInfo*)(w + lay.seqs), order, tact, tbase);
   return hipGetLastError();
 }
 
@@ -178,12 +181,15 @@ __device__ inline int seq_of_padded_row(const SeqInfo* seqs, int B, int r) {
 
 // ---------------------------------------------------------------------------
 // Pre-pass: 64 padded rows per workgroup (rows of one sequence, or padding).
+// With from_abs the keys are already rotated at their absolute positions (an
+// existing key cache): the absolute operand is the key itself and the
+// remapped one is R_{f(k) - k} applied to it (R_a R_b = R_{a+b}).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
     const uint16_t* __restrict__ xk, const uint16_t* __restrict__ v, uint16_t* __restrict__ kcache,
     const SeqInfo* __restrict__ seqs, const int* __restrict__ hdr, int B, int Hkv, int R,
-    int need_rem, uint16_t* __restrict__ kabs, uint16_t* __restrict__ krem,
-    uint16_t* __restrict__ vt, RopeFreqs fr) {
+    int need_rem, int from_abs, float kscale, uint16_t* __restrict__ kabs,
+    uint16_t* __restrict__ krem, uint16_t* __restrict__ vt, RopeFreqs fr) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * (PF_D + 8)];
   const int r0 = blockIdx.x * 64;
   if (r0 >= hdr[2]) return;
@@ -198,10 +204,12 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
     const int trel = r - sq.pad_off;
     const bool valid = trel < sq.len;
     float ca[8], sa[8], cr[8], sr[8];
+    const double pa = from_abs ? 0.0 : (double)trel;
+    const double pr = from_abs ? (double)(trel / sq.G - trel) : (double)(trel / sq.G);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      rope_cs((double)trel, fr.w(8 * c + j), ca[j], sa[j]);
-      if (need_rem) rope_cs((double)(trel / sq.G), fr.w(8 * c + j), cr[j], sr[j]);
+      rope_cs(pa, fr.w(8 * c + j), ca[j], sa[j]);
+      if (need_rem) rope_cs(pr, fr.w(8 * c + j), cr[j], sr[j]);
     }
     for (int g = 0; g < Hkv; ++g) {
       uint4 av = make_uint4(0, 0, 0, 0), bv = av;
@@ -217,13 +225,13 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
       for (int j = 0; j < 8; ++j) {
         const float x0 = bf16_bits_to_f32(ap[j]), x1 = bf16_bits_to_f32(bp[j]);
         const float y0 = x0 * ca[j] - x1 * sa[j], y1 = x0 * sa[j] + x1 * ca[j];
-        oa[j] = f32_to_f16_bits(y0);
-        ob[j] = f32_to_f16_bits(y1);
+        oa[j] = f32_to_f16_bits(y0 * kscale);
+        ob[j] = f32_to_f16_bits(y1 * kscale);
         ka[j] = f32_to_bf16_bits(y0);
         kb[j] = f32_to_bf16_bits(y1);
         if (need_rem) {
-          ra[j] = f32_to_f16_bits(x0 * cr[j] - x1 * sr[j]);
-          rb[j] = f32_to_f16_bits(x0 * sr[j] + x1 * cr[j]);
+          ra[j] = f32_to_f16_bits((x0 * cr[j] - x1 * sr[j]) * kscale);
+          rb[j] = f32_to_f16_bits((x0 * sr[j] + x1 * cr[j]) * kscale);
         }
       }
       uint16_t* da = kabs + ((int64_t)g * R + r) * PF_D;
@@ -265,15 +273,16 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
 }
 
 hipError_t launch_prefill_prep_bf16(const void* xk, const void* v, void* kcache_out, int64_t T,
-                                    int B, int Hkv, int need_rem, const RopeFreqs& fr, void* ws,
-                                    const PrefillLayout& lay, hipStream_t st) {
+                                    int B, int Hkv, int need_rem, int from_abs, float kscale,
+                                    const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
+                                    hipStream_t st) {
   char* w = (char*)ws;
   const int blocks = (int)(lay.R / 64);
   hipLaunchKernelGGL(prefill_prep_bf16_kernel, dim3(blocks), dim3(256), 0, st,
                      (const uint16_t*)xk, (const uint16_t*)v, (uint16_t*)kcache_out,
                      (const SeqInfo*)(w + lay.seqs), (const int*)(w + lay.hdr), B, Hkv,
-                     (int)lay.R, need_rem, (uint16_t*)(w + lay.kabs), (uint16_t*)(w + lay.krem),
-                     (uint16_t*)(w + lay.vt), fr);
+                     (int)lay.R, need_rem, from_abs, kscale, (uint16_t*)(w + lay.kabs),
+                     (uint16_t*)(w + lay.krem), (uint16_t*)(w + lay.vt), fr);
   (void)T;
   return hipGetLastError();
 }
@@ -294,8 +303,8 @@ struct PfArgs {
   const int* tact;
   const int* tbase;
   int T, R, Hq, Hkv, w0;
+  int qoff;       // position of the first query row (0 unless continuing on a cache)
   int ie_remote;  // pass B of Eq. 7 (1) or pass C (0)
-  float scale_log2;
   RopeFreqs fr;
 };
 
@@ -314,13 +323,14 @@ struct Tctx {
   int R;                 // padded row stride of vt
   int q0, q1, len, nkt, w0;
   int tid, hh, l32, myq;
-  float scale_log2;
 };
 
-// Running softmax state of one lane's query row. Scores are produced in the
-// log2 domain already shifted by the reference: the query operand carries
-// scale * log2(e), and the QK^T accumulator starts at -m, so each MFMA
-// output is s' = scale * log2(e) * (q . k) - m and p = exp2(s') directly.
+// Running softmax state of one lane's query row. Scores come out of the
+// MFMA in the log2 domain, already shifted by the reference: the key
+// operands carry c = scale * log2(e) (applied in the pre-pass before their
+// fp16 rounding) and the QK^T accumulator starts at -m, so each output is
+// s' = c (q . k) - m and p = exp2(s'). The query operand is the rotated query
+// itself.
 struct RowState {
   f32x16 acc[4];  // O^T accumulator: d = 32*db + 8*(r/4) + 4*hh + r%4
   f32x16 negm;    // -m in every register: the QK^T accumulator's start value
@@ -408,8 +418,8 @@ __device__ __forceinline__ void boundary_select(const Tctx& c, int j, const h8v 
 }
 
 // Masks, online softmax and O^T += V^T P^T for one tile whose shifted
-// scores s' = s - m are in s. The reference m does not follow every new row
-// maximum: it moves only when the tile's probabilities p = exp2(s') summed
+// scores s' = c (q . k) - m are in s. The reference m does not follow every new
+// row maximum: it moves only when the tile's probabilities p = exp2(s') summed
 // over a lane's 32 keys exceed 2^8 (or the row has no reference yet), so
 // every p stays below 2^8 and the sum check replaces the per-tile row max.
 // Since the final division uses the same reference, the result does not
@@ -451,7 +461,8 @@ __device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], b8v (&pb)[4]) {
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pb[2 * bk + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(s[bk][r]);
+    for (int r = 0; r < 16; ++r)
+      pb[2 * bk + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(s[bk][r]);
   const b2v one = {(__bf16)1.f, (__bf16)1.f};
   float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -570,10 +581,9 @@ __device__ __forceinline__ void walk_boundary(const Tctx& c, int j0, int j1, int
 
 // RoPE(x_q, p) of the lane's raw query row as the fp16 QK^T operand. The lane
 // holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs (d, d+64)
-// are chunks (c, c+4) of the same lane. w2pi: omega_i / (2 pi) in LDS. The
-// operand carries the score scale qs = scale * log2(e).
+// are chunks (c, c+4) of the same lane. w2pi: omega_i / (2 pi) in LDS.
 __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], int p, int hh,
-                                             const double* w2pi, float qs, h8v (&out)[8]) {
+                                             const double* w2pi, h8v (&out)[8]) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -581,8 +591,8 @@ __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], int p, int h
       const float x0 = bf16_lane(raw[c], j), x1 = bf16_lane(raw[c + 4], j);
       float cs, sn;
       rope_cs_turns((double)p, w2pi[16 * c + 8 * hh + j], cs, sn);
-      out[c][j] = (_Float16)((x0 * cs - x1 * sn) * qs);
-      out[c + 4][j] = (_Float16)((x0 * sn + x1 * cs) * qs);
+      out[c][j] = (_Float16)(x0 * cs - x1 * sn);
+      out[c + 4][j] = (_Float16)(x0 * sn + x1 * cs);
     }
   }
 }
@@ -628,14 +638,13 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   c.tid = threadIdx.x;
   c.hh = (c.tid & 63) >> 5;
   c.l32 = c.tid & 31;
-  c.q0 = t * PF_BM;
+  c.q0 = a.qoff + t * PF_BM;
   c.q1 = min(c.q0 + PF_BM, sq.len) - 1;
   c.len = sq.len;
   c.myq = c.q0 + (c.tid >> 6) * 32 + c.l32;
   c.nkt = c.q1 / PF_BN + 1;
   c.w0 = a.w0;
   c.R = R;
-  c.scale_log2 = a.scale_log2;
   c.kabs = a.kabs + ((int64_t)g * R + sq.pad_off) * PF_D;
   c.krem = a.krem + ((int64_t)g * R + sq.pad_off) * PF_D;
   c.vt = a.vt + (int64_t)g * PF_D * R + sq.pad_off;
@@ -644,13 +653,13 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   // raw query row slice of this lane (zeros past the sequence end); re-read
   // before each rotation rather than kept live across the key loops
   const uint16_t* qp =
-      a.xq + ((int64_t)(sq.start + (qvalid ? c.myq : 0)) * Hq + head) * PF_D + 8 * c.hh;
+      a.xq + ((int64_t)(sq.start + (qvalid ? c.myq - a.qoff : 0)) * Hq + head) * PF_D + 8 * c.hh;
   auto rotq = [&](int p, h8v (&out)[8]) __attribute__((always_inline)) {
     u32x4 raw[8];
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
       raw[cc] = qvalid ? *(const u32x4*)(qp + 16 * cc) : u32x4{0, 0, 0, 0};
-    rotate_query(raw, p, c.hh, w2pi_s, c.scale_log2, out);
+    rotate_query(raw, p, c.hh, w2pi_s, out);
   };
 
   // first tile that is not all-remote, first tile that is all-local
@@ -724,7 +733,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   const float l_tot = st.l + xor32(st.l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!qvalid) return;
-  const int64_t row = (int64_t)(sq.start + c.myq);
+  const int64_t row = (int64_t)(sq.start + c.myq - a.qoff);  // query row of the call
   if (PASS == PASS_IE_A || PASS == PASS_IE_B) {
     float* op = (float*)a.o + (row * Hq + head) * PF_D;
 #pragma unroll
@@ -754,8 +763,9 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
 }
 
 hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, int64_t T, int B,
-                               int Hq, int Hkv, int64_t w0, float scale, const RopeFreqs& fr,
-                               void* ws, const PrefillLayout& lay, hipStream_t st) {
+                               int Hq, int Hkv, int64_t w0, int64_t qoff, float scale,
+                               const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
+                               hipStream_t st) {
   char* w = (char*)ws;
   PfArgs a;
   a.xq = (const uint16_t*)xq;
@@ -774,8 +784,9 @@ hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, in
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.w0 = (int)w0;
+  a.qoff = (int)qoff;
   a.ie_remote = pass == PASS_IE_B;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  (void)scale;  // the score scale is carried by the key operands (pre-pass)
   a.fr = fr;
   const int64_t blocks = lay.max_tiles * Hq;
   switch (pass) {

@@ -319,3 +319,60 @@ def test_decode_matches_prefill_last_row():
         torch.cuda.synchronize()
         assert np.abs(to_host(o_p)[pos] - to_host(o_d)).max() <= 1.6e-2
         assert np.abs(to_host(l_p)[:, pos] - to_host(l_d)).max() <= 1.6e-2
+
+
+# ------------------------------------------------- prefill continued on a cache
+def _cache(seed, C, Hq, Hkv, theta, d=128):
+    """Raw inputs of a C-row sequence and its absolute bf16 key cache."""
+    xq, xk, v, _ = make_qkv(seed, C, Hq, Hkv, d)
+    kc = to_dev(xk)
+    jl.rope_apply(kc, theta)
+    return xq, xk, v, kc, to_dev(v)
+
+
+@pytest.mark.parametrize("q_off,Tq,w0,w_pre", [
+    (0, 700, 100, 512),      # a whole sequence read from the cache (G = 2)
+    (1000, 300, 100, 512),   # a chunk in the middle, L = 1300 (G = 3)
+    (1024, 1, 100, 512),     # one row: a decode step at pos 1024
+    (900, 124, 64, 512),     # L = 1024 exactly (G = 2)
+    (1000, 50, 100, 512),    # L = 1050: the chunk moves G from 2 to 3
+    (1537, 263, 0, 600),     # w0 = 0, ragged chunk, G = 3
+])
+def test_prefill_cached_matches_oracle(q_off, Tq, w0, w_pre):
+    theta, Hq, Hkv = 1e6, 8, 2
+    L = q_off + Tq
+    C = L + 37  # rows past L hold other keys: they must not be read
+    xq, xk, v, kc, vc = _cache(7300 + L, C, Hq, Hkv, theta)
+    k_before = kc.clone()
+    for mode in ("fused", "plain"):
+        note(f"prefill_cached q_off={q_off} Tq={Tq} w0={w0} G={group_size(L, w_pre)} {mode}")
+        o, lse = jl.bifocal_prefill_cached(to_dev(xq[q_off:L]), kc, vc, q_off, w0, w_pre, theta,
+                                           mode=mode)
+        torch.cuda.synchronize()
+        O, LSE = bifocal_attention(xq[:L], xk[:L], v[:L], BIG if mode == "plain" else w0, w_pre,
+                                   theta, rows=np.arange(q_off, L))
+        assert_bf16_close(to_host(o), O, f"cached q_off={q_off} Tq={Tq} {mode}")
+        assert errs(to_host(lse), LSE)[0] <= BF16_LSE_ABS
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k_before), "prefill_cached wrote the cache"
+
+
+def test_prefill_cached_agrees_with_prefill_and_decode():
+    """GPU against GPU: a cached chunk covering the whole sequence equals the
+    ordinary prefill, and a one-row chunk equals the decode step, within the
+    rounding of the bf16 cache."""
+    theta, w0, w_pre, L = 1e6, 100, 512, 1500
+    xq, xk, v, kc, vc = _cache(7400, L, 8, 2, theta)
+    note("prefill_cached vs prefill, whole sequence")
+    o_c, l_c = jl.bifocal_prefill_cached(to_dev(xq), kc, vc, 0, w0, w_pre, theta)
+    o_p, l_p = jl.bifocal_prefill(to_dev(xq), to_dev(xk), to_dev(v), w0, w_pre, theta)
+    torch.cuda.synchronize()
+    assert np.abs(to_host(o_c) - to_host(o_p)).max() <= 1.6e-2
+    assert np.abs(to_host(l_c) - to_host(l_p)).max() <= 1.6e-2
+    for pos in (1023, 1024, 1499):
+        note(f"prefill_cached one row vs decode pos={pos}")
+        o_1, l_1 = jl.bifocal_prefill_cached(to_dev(xq[pos:pos + 1]), kc, vc, pos, w0, w_pre, theta)
+        o_d, l_d = jl.bifocal_decode(to_dev(xq[pos]), kc, vc, pos, w0, w_pre, theta)
+        torch.cuda.synchronize()
+        assert np.abs(to_host(o_1)[0] - to_host(o_d)).max() <= 1.6e-2
+        assert np.abs(to_host(l_1)[:, 0] - to_host(l_d)).max() <= 1.6e-2

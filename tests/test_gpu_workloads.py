@@ -18,8 +18,8 @@ import pytest
 import torch
 
 import rope_context_extension_jl_amd as jl
-from oracle import bifocal_attention, decode_row, group_size
-from synth_inputs import WORKLOADS, edge_rows, make_qkv, sample_rows
+from oracle import bifocal_attention, decode_row, group_size, rope
+from synth_inputs import WORKLOADS, edge_rows, make_qkv, quantize_bf16, sample_rows
 from tests._gpu_common import BF16_LSE_ABS, assert_bf16_close, errs, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -196,3 +196,38 @@ def test_decode_128k_plain_and_splits(dec):
         ref = oh if ref is None else ref
         assert np.abs(oh - ref).max() <= 8e-3
     assert float(dec["kc"].float().sum()) == dec["ksum"], "decode wrote the cache"
+
+
+# ------------------------------------------------- prefill continued on a cache
+def test_prefill_cached_128k_last_chunk(p128k):
+    """The last 8192 rows of the 128K workload as one chunk on an absolute
+    cache of all 131072 keys (G = 4), in the launch configuration bench.py
+    times, against the oracle on sampled rows of the chunk.
+
+    For this path the cache is the input: it holds the keys rotated at their
+    absolute positions and rounded to bf16, a rounding the raw-key oracle
+    does not see (on this workload's x8 key rows it alone moves outputs by
+    several 1e-2). The cache is therefore built here on the CPU, with the
+    oracle's rotation, and the oracle is evaluated on the keys it holds:
+    R_{-k} applied in float64 to each cached row (exact up to float64)."""
+    c = p128k.cfg
+    L, Tq = p128k.L, 8192
+    q_off = L - Tq
+    pos = np.arange(L)
+    cache = quantize_bf16(rope(p128k.xk, pos, c["theta"]).astype(np.float32))
+    xk_eff = rope(cache, -pos, c["theta"])
+    kc, vc = to_dev(cache), to_dev(p128k.v)
+    note("prefill_cached 128K last 8192 rows")
+    o, lse = jl.bifocal_prefill_cached(to_dev(p128k.xq[q_off:]), kc, vc, q_off, c["w0"],
+                                       c["w_pre"], c["theta"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    rows = np.unique(np.concatenate([[q_off, q_off + 1, L - 1],
+                                     q_off + rng.choice(Tq, 61, replace=False)]))
+    oh, lh = to_host(o[rows - q_off]), to_host(lse)[:, rows - q_off]
+    del o, lse, kc, vc
+    torch.cuda.empty_cache()
+    O, LSE = bifocal_attention(p128k.xq, xk_eff, p128k.v, c["w0"], c["w_pre"], c["theta"],
+                               rows=rows)
+    assert_bf16_close(oh, O, "128K cached chunk")
+    assert errs(lh, LSE)[0] <= BF16_LSE_ABS

@@ -201,3 +201,32 @@ def test_calibration_argument_errors():
     assert g(None, 4, 10, None) == -1
     assert g(P, 0, 10, None) == -1
     assert g(P, 4, 0, None) == -1
+
+
+def _cached(**kw):
+    args = dict(xq=P, kc=P, vc=P, o=P, lse=None, q_off=100, Tq=50, cap=1000, Hq=8, Hkv=2, d=128,
+                w0=16, w_pre=64, theta=1e4, scale=0.0, dt=0, mode=0, ws=P, ws_bytes=1 << 40,
+                stream=None)
+    args.update(kw)
+    return jl.lib().jl_bifocal_prefill_cached(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_off=-1), -1), (dict(Tq=-1), -1), (dict(q_off=960), -1), (dict(cap=0), -1),
+    (dict(Hq=6, Hkv=4), -1), (dict(w0=-1), -1), (dict(w_pre=0), -1), (dict(theta=1.0), -1),
+    (dict(mode=1), -2), (dict(mode=9), -1), (dict(dt=1), -2), (dict(d=64), -2), (dict(dt=4), -1),
+    (dict(xq=None), -1), (dict(kc=None), -1), (dict(ws=None), -4), (dict(ws_bytes=64), -4),
+    (dict(ws=ctypes.c_void_p(16 + 8)), -1),
+])
+def test_prefill_cached_argument_errors(kw, code):
+    assert _cached(**kw) == code
+
+
+def test_prefill_cached_empty_is_noop_and_sizes():
+    assert _cached(Tq=0, xq=None, kc=None, vc=None, o=None, ws=None, ws_bytes=0) == 0
+    a = jl.prefill_cached_workspace_size(0, 1000, 8, 2, 128)
+    b = jl.prefill_cached_workspace_size(1000, 1000, 8, 2, 128)
+    assert 0 < a < b
+    assert b == jl.prefill_workspace_size(2000, 1, 8, 2, 128)
+    assert jl.prefill_cached_workspace_size(0, 10, 8, 2, 64) == 0
+    assert jl.prefill_cached_workspace_size(0, 10, 8, 2, 128, mode="ie") == 0

@@ -12,7 +12,8 @@ time (effective TFLOP/s).
 Also reported (not part of the timed step): the attention kernel alone (live
 HIP events around it, for the roofline), the library's plain causal RoPE
 attention at the same shape (overhead ratio), the Eq. 7 inclusion-exclusion
-alternative, the 64K and packed-varlen workloads, a window-size sweep, decode latency
+alternative, the 64K and packed-varlen workloads, prefill continued on the cache for the
+last 8192 rows, a window-size sweep, decode latency
 at positions 32767 .. 131071 of a 131072-key cache with L2 / MALL evicted
 before every step, calibrated HBM-read and MFMA ceilings, and the float64 CPU
 oracle on a bounded sample of rows.
@@ -226,6 +227,37 @@ def main():
                              "worst_cancellation_ratio": float(ratio.max()),
                              "rows_ratio_over_1e3": float((ratio > 1e3).float().mean())}
         del ws_ie, ratio
+        torch.cuda.empty_cache()
+
+        # ---------------------------------------------------- chunked prefill
+        log("prefill continued on the cache: last 8192 rows of the 128K sequence")
+        Tq = 8192
+        q_off = L - Tq
+        qc = q[q_off:].contiguous()
+        ws_c = torch.empty(jl.prefill_cached_workspace_size(q_off, Tq, Hq, Hkv, d),
+                           dtype=torch.uint8, device=dev)
+        oc = torch.empty_like(qc)
+        lc = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+        fl_c = sum(4.0 * (p + 1) * d * Hq for p in range(q_off, L))
+        call = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        jl.bifocal_prefill_cached(qc, kcache, vv, q_off, w0, w_pre, theta, out=oc, lse=lc,
+                                  workspace=ws_c)
+        torch.cuda.synchronize()
+        ck, cc_ = [], []
+        for _ in range(5):
+            call[0].record(stream)
+            jl.bifocal_prefill_cached(qc, kcache, vv, q_off, w0, w_pre, theta, out=oc, lse=lc,
+                                      workspace=ws_c, events=pe)
+            call[1].record(stream)
+            torch.cuda.synchronize()
+            ck.append(pe[0].elapsed_time(pe[1]))
+            cc_.append(call[0].elapsed_time(call[1]))
+        extras["prefill_cached_128k_last8k"] = {
+            "q_off": q_off, "rows": Tq, "kernel_ms": round(float(np.median(ck)), 4),
+            "tflops": round(fl_c / float(np.median(ck)) / 1e9, 2),
+            "call_ms": round(float(np.median(cc_)), 4),
+            "note": "call_ms adds the plan and the pre-pass that rotates all 131072 cached keys"}
+        del ws_c, oc, lc, qc
         torch.cuda.empty_cache()
 
         # ---------------------------------------------------- w0 sweep

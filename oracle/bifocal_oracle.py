@@ -19,6 +19,11 @@ Citations (page title, then the part of the page):
   [Pith/Ledger]    pith.science review of arXiv 2607.07740, Axiom &
                    Free-Parameter Ledger: Sec. 3.1 Eq. 2 (G), Sec. 3.2
                    Eqs. 5-6 (correction rotation), Sec. 3.3 Eq. 7 (merge).
+  [Pith/Review]    the same page's Referee Report, major comment 2 (Sec. 3.1
+                   Eqs. 2-3 and Table 6) and the ledger's axiom on the
+                   discrete angle grid (Sec. 4.5 / Table 6): the comparison
+                   arm with continuous frequency interpolation in place of
+                   floor-division aliasing.
   [RoFormer]       the rotary embedding the pages build on (their reference
                    list: Su et al., RoFormer). The pages print no frequency
                    formula; the reading used here is stated in rope().
@@ -27,7 +32,10 @@ Readings of points the pages leave open (each also listed in the design
 notes): positions are 0-based per sequence; q - k == w0 is local; the
 softmax scale is 1/sqrt(d) in both branches; RoPE pairs element i with
 i + d/2 and uses omega_i = theta^(-2i/d); query head h reads KV head
-h // (Hq/Hkv); decode at position p uses L = p + 1.
+h // (Hq/Hkv); decode at position p uses L = p + 1. The continuous remote
+map (the Table 6 comparison arm, whose formula the pages do not print) is
+read as f(x) = x / G, a real number, with the same G and the same local
+window: positional interpolation of the remote branch by the factor G.
 
 Status of the pins (tests/test_oracle_pins.py): every public function here is
 pinned against closed forms, library routines, brute force or invariants.
@@ -61,11 +69,16 @@ def group_size(L: int, w_pre: int) -> int:
     return max(1, -(-L // w_pre))
 
 
-def remap(p, G: int):
-    """f(x) = floor(x / G) for non-negative integer positions.
-
+def remap(p, G: int, continuous: bool = False):
+    """f(x) = floor(x / G) for non-negative integer positions
     [Digest/Method, "Dynamic group size"].
+
+    continuous=True: f(x) = x / G as a float64 real number, the continuous
+    frequency-interpolation arm [Pith/Review, Table 6]: a rotation by
+    (x / G) * omega_i is a rotation by x at the frequency omega_i / G.
     """
+    if continuous:
+        return np.asarray(p, dtype=np.int64).astype(np.float64) / float(G)
     return np.asarray(p, dtype=np.int64) // int(G)
 
 
@@ -110,21 +123,23 @@ def rope(x, pos, theta: float) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Eq. 1: the bifocal score
 # ---------------------------------------------------------------------------
-def bifocal_scores(xq_rows, q_pos, xk, k_pos, w0: int, G: int, theta: float) -> np.ndarray:
+def bifocal_scores(xq_rows, q_pos, xk, k_pos, w0: int, G: int, theta: float,
+                   continuous: bool = False) -> np.ndarray:
     """S(q, k) for one head: [len(q_pos), len(k_pos)] before scaling/masking.
 
     S = RoPE(x_q, q) . RoPE(x_k, k)          if q - k <= w0
       = RoPE(x_q, f(q)) . RoPE(x_k, f(k))    otherwise,   f(x) = floor(x/G).
     [Digest/Method, Eq. 1]. Both branches are computed in full from the raw
     vectors and the result is selected element by element on the distance.
-    xq_rows: [nq, d], xk: [nk, d] raw (pre-RoPE) vectors.
+    xq_rows: [nq, d], xk: [nk, d] raw (pre-RoPE) vectors. continuous: remote
+    branch at f(x) = x / G (see remap).
     """
     q_pos = np.asarray(q_pos, dtype=np.int64)
     k_pos = np.asarray(k_pos, dtype=np.int64)
     qa = rope(xq_rows, q_pos, theta)
-    qr = rope(xq_rows, remap(q_pos, G), theta)
+    qr = rope(xq_rows, remap(q_pos, G, continuous), theta)
     ka = rope(xk, k_pos, theta)
-    kr = rope(xk, remap(k_pos, G), theta)
+    kr = rope(xk, remap(k_pos, G, continuous), theta)
     s_local = qa @ ka.T
     s_remote = qr @ kr.T
     dist = q_pos[:, None] - k_pos[None, :]
@@ -144,7 +159,8 @@ def _softmax_rows(S: np.ndarray, vals: np.ndarray):
 
 
 def bifocal_attention(xq, xk, v, w0: int, w_pre: int, theta: float, scale=None,
-                      rows=None, heads=None, G=None, row_chunk: int = 128):
+                      rows=None, heads=None, G=None, row_chunk: int = 128,
+                      continuous: bool = False):
     """Causal bifocal attention for ONE sequence (positions 0 .. L-1).
 
     xq: [L, Hq, d], xk / v: [L, Hkv, d] raw float arrays (upcast to fp64).
@@ -157,6 +173,7 @@ def bifocal_attention(xq, xk, v, w0: int, w_pre: int, theta: float, scale=None,
     reads KV head h // (Hq / Hkv). [Digest/Method, Eq. 1 and "Dynamic group
     size".] Rotations are applied directly to the raw vectors at the absolute
     and the remapped positions, never through correction offsets.
+    continuous: remote branch at f(x) = x / G (see remap).
     """
     xq = np.asarray(xq)
     xk = np.asarray(xk)
@@ -178,10 +195,10 @@ def bifocal_attention(xq, xk, v, w0: int, w_pre: int, theta: float, scale=None,
     kpos = np.arange(L, dtype=np.int64)
     # Keys rotated once per KV head at absolute and remapped positions.
     ka_all = rope(xk, kpos, theta)
-    kr_all = rope(xk, remap(kpos, G), theta)
+    kr_all = rope(xk, remap(kpos, G, continuous), theta)
     v64 = v.astype(np.float64)
     qa_all = rope(xq[rows], rows, theta)
-    qr_all = rope(xq[rows], remap(rows, G), theta)
+    qr_all = rope(xq[rows], remap(rows, G, continuous), theta)
     for h in heads:
         g = h // r
         for c0 in range(0, len(rows), row_chunk):
@@ -200,7 +217,7 @@ def bifocal_attention(xq, xk, v, w0: int, w_pre: int, theta: float, scale=None,
 
 
 def bifocal_varlen(xq, xk, v, cu_seqlens, w0, w_pre, theta, scale=None, rows_per_seq=None,
-                   heads=None):
+                   heads=None, continuous: bool = False):
     """Packed batch: sequence b owns tokens cu_seqlens[b] .. cu_seqlens[b+1]-1.
 
     Each sequence is independent: positions restart at 0 and G comes from
@@ -218,7 +235,7 @@ def bifocal_varlen(xq, xk, v, cu_seqlens, w0, w_pre, theta, scale=None, rows_per
             out.append((np.zeros(0, dtype=np.int64), np.zeros((0, Hq, d)), np.zeros((Hq, 0))))
             continue
         O, LSE = bifocal_attention(xq[s:e], xk[s:e], v[s:e], w0, w_pre, theta, scale=scale,
-                                   rows=rows, heads=heads)
+                                   rows=rows, heads=heads, continuous=continuous)
         out.append((np.arange(e - s) if rows is None else np.asarray(rows), O, LSE))
     return out
 
@@ -227,7 +244,7 @@ def bifocal_varlen(xq, xk, v, cu_seqlens, w0, w_pre, theta, scale=None, rows_per
 # Decode: one query at position p against the absolute cache
 # ---------------------------------------------------------------------------
 def decode_row(xq_row, xk_cache, v_cache, pos: int, w0: int, w_pre: int, theta: float,
-               scale=None):
+               scale=None, continuous: bool = False):
     """Single-token step at position `pos`, keys 0 .. pos, L = pos + 1.
 
     xq_row: [Hq, d] raw query; xk_cache / v_cache: [>= pos+1, Hkv, d] raw keys
@@ -237,7 +254,7 @@ def decode_row(xq_row, xk_cache, v_cache, pos: int, w0: int, w_pre: int, theta: 
     lse [Hq]) in float64. [Digest/Method, Eq. 1 and "KV cache invariant":
     the cache holds absolute keys and is never rewritten when G changes.]
     Written independently of bifocal_attention so that the two can be
-    compared.
+    compared. continuous: remote route at pos / G and k / G (real numbers).
     """
     xq_row = np.asarray(xq_row, dtype=np.float64)
     Hq, d = xq_row.shape
@@ -251,9 +268,13 @@ def decode_row(xq_row, xk_cache, v_cache, pos: int, w0: int, w_pre: int, theta: 
     xk = np.asarray(xk_cache[:L], dtype=np.float64)
     vv = np.asarray(v_cache[:L], dtype=np.float64)
     local = (pos - keys) <= w0
-    k_at = rope(xk, np.where(local, keys, keys // G), theta)  # [L, Hkv, d]
+    if continuous:
+        k_rem_pos, q_rem_pos = keys / float(G), pos / float(G)
+    else:
+        k_rem_pos, q_rem_pos = keys // G, pos // G
+    k_at = rope(xk, np.where(local, keys, k_rem_pos), theta)  # [L, Hkv, d]
     q_abs = rope(xq_row[None], [pos], theta)[0]
-    q_rem = rope(xq_row[None], [pos // G], theta)[0]
+    q_rem = rope(xq_row[None], [q_rem_pos], theta)[0]
     o = np.zeros((Hq, d))
     lse = np.zeros(Hq)
     for h in range(Hq):
@@ -269,7 +290,8 @@ def decode_row(xq_row, xk_cache, v_cache, pos: int, w0: int, w_pre: int, theta: 
 # ---------------------------------------------------------------------------
 # Eq. 7: inclusion-exclusion over three attention passes
 # ---------------------------------------------------------------------------
-def ie_pass(xq, xk, v, which: str, w0: int, G: int, theta: float, scale=None):
+def ie_pass(xq, xk, v, which: str, w0: int, G: int, theta: float, scale=None,
+            continuous: bool = False):
     """One of the three plain attention passes, one sequence, all rows/heads.
 
     'A': keys with 0 <= q-k <= w0, RoPE at absolute positions;
@@ -279,6 +301,7 @@ def ie_pass(xq, xk, v, which: str, w0: int, G: int, theta: float, scale=None):
     once with the right rotation. [Digest/Method, "Inclusion-exclusion
     prefill"; ResearchPod dialogue: local view, remapped distant view and
     corrected local view.] Returns (O [L,Hq,d], LSE [Hq,L]) float64.
+    continuous: passes B and C rotate at x / G (real numbers).
     """
     xq = np.asarray(xq, dtype=np.float64)
     xk = np.asarray(xk, dtype=np.float64)
@@ -289,7 +312,10 @@ def ie_pass(xq, xk, v, which: str, w0: int, G: int, theta: float, scale=None):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     pos = np.arange(L, dtype=np.int64)
-    p_rot = pos if which == "A" else pos // G
+    if which == "A":
+        p_rot = pos
+    else:
+        p_rot = pos / float(G) if continuous else pos // G
     q = rope(xq, p_rot, theta)
     k = rope(xk, p_rot, theta)
     dist = pos[:, None] - pos[None, :]

@@ -21,9 +21,10 @@ def _rotate(vec, p, theta):
     return out
 
 
-def brute_attention(xq, xk, v, w0, w_pre, theta, scale=None, positions=None):
+def brute_attention(xq, xk, v, w0, w_pre, theta, scale=None, positions=None, continuous=False):
     """xq: list[L][Hq][d], xk / v: list[L][Hkv][d] (nested Python lists).
-    Returns (O list[L][Hq][d], LSE list[Hq][L])."""
+    Returns (O list[L][Hq][d], LSE list[Hq][L]). continuous: remote pairs
+    rotate at the real positions q / G and k / G instead of floor(. / G)."""
     L = len(xq)
     Hq = len(xq[0])
     Hkv = len(xk[0])
@@ -44,6 +45,8 @@ def brute_attention(xq, xk, v, w0, w_pre, theta, scale=None, positions=None):
             for k in range(q + 1):
                 if q - k <= w0:
                     pq, pk = q, k
+                elif continuous:
+                    pq, pk = q / G, k / G
                 else:
                     pq, pk = q // G, k // G
                 a = _rotate(xq[q][h], pq, theta)

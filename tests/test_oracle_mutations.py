@@ -33,6 +33,15 @@ MUTATIONS = {
                  "    L = pos + 1\n    G = group_size(pos, w_pre) if pos else 1"),
     "tile_diag_flag": ("    if (~causal).any():\n        cls += 4", "    if (~causal).all():\n        cls += 4"),
     "lse_log2": ("lse = (m + np.log(l))[:, 0]", "lse = (m + np.log2(l))[:, 0]"),
+    "continuous_floored": ("return np.asarray(p, dtype=np.int64).astype(np.float64) / float(G)",
+                           "return (np.asarray(p, dtype=np.int64) // int(G)).astype(np.float64)"),
+    "continuous_times_g": ("return np.asarray(p, dtype=np.int64).astype(np.float64) / float(G)",
+                           "return np.asarray(p, dtype=np.int64).astype(np.float64) * float(G)"),
+    "continuous_decode_query_floor": (
+        "k_rem_pos, q_rem_pos = keys / float(G), pos / float(G)",
+        "k_rem_pos, q_rem_pos = keys / float(G), pos // G"),
+    "continuous_ie_floor": ("p_rot = pos / float(G) if continuous else pos // G",
+                            "p_rot = pos // G"),
 }
 
 

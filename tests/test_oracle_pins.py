@@ -361,3 +361,127 @@ def test_tile_class_map_ragged():
     assert m[0, 0] == 3 + 4 and m[0, 2] == 0 and m[2, 0] == 2  # q-k up to 3 > 2 on tile (0,0)
     # last tiles clipped at L-1 = 9: query tile [8, 9], key tile [9, 9] is diagonal+local
     assert m[2, 3] == 1 + 4
+
+
+# ---------------------------------------------------------------- continuous remote map
+# The comparison arm of Table 6 [Pith/Review, major comment 2; ledger axiom
+# on the discrete grid]: continuous frequency interpolation in place of
+# floor-division aliasing, read as f(x) = x / G with the same G and window.
+def test_continuous_remap_values():
+    """f(x) = x / G exactly, as a real number, against hand values."""
+    np.testing.assert_array_equal(remap([0, 1, 2, 3, 5, 8, 9], 4, continuous=True),
+                                  [0.0, 0.25, 0.5, 0.75, 1.25, 2.0, 2.25])
+    np.testing.assert_array_equal(remap([0, 7, 131071], 1, continuous=True), [0.0, 7.0, 131071.0])
+    assert remap([7], 3, continuous=True).dtype == np.float64
+
+
+def _freq_scaled_rope(x, pos, theta, factor):
+    """Rotation of pair (i, i + d/2) by pos * omega_i / factor, written with
+    complex numbers: the frequency-interpolation form (every frequency
+    divided by the factor) rather than a remapped position."""
+    d = x.shape[-1]
+    h = d // 2
+    w = theta ** (-(2.0 * np.arange(h)) / d) / factor
+    z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * np.asarray(pos, float)[:, None, None] * w)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+@pytest.mark.parametrize("w0", [0, -1])
+def test_continuous_no_window_is_frequency_interpolation(w0):
+    """With no key outside the diagonal in the window (w0 = 0; the diagonal
+    has relative angle 0 on both routes) or none at all (w0 = -1), the
+    continuous arm is plain causal RoPE attention with every frequency
+    divided by G (positional interpolation), checked with torch SDPA."""
+    L, Hq, Hkv, d, theta, w_pre = 50, 2, 1, 16, 1e4, 16
+    G = group_size(L, w_pre)
+    assert G == 4
+    xq, xk, v = _rand(40, L, Hq, d), _rand(41, L, Hkv, d), _rand(42, L, Hkv, d)
+    O, _ = bifocal_attention(xq, xk, v, w0, w_pre, theta, continuous=True)
+    p = np.arange(L)
+    ref = _sdpa_causal(_freq_scaled_rope(xq, p, theta, G),
+                       np.repeat(_freq_scaled_rope(xk, p, theta, G), 2, 1),
+                       np.repeat(v, 2, 1), 1 / math.sqrt(d))
+    np.testing.assert_allclose(O, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,w_pre,w0", [(48, 64, 5), (40, 3, 100)])
+def test_continuous_reduces_like_discrete(L, w_pre, w0):
+    """G = 1 or an all-local window: both maps give the same result (the
+    base model inside the pretrained window)."""
+    Hq, Hkv, d, theta = 2, 1, 16, 1e4
+    xq, xk, v = _rand(43, L, Hq, d), _rand(44, L, Hkv, d), _rand(45, L, Hkv, d)
+    Oc, Lc = bifocal_attention(xq, xk, v, w0, w_pre, theta, continuous=True)
+    Od, Ld = bifocal_attention(xq, xk, v, w0, w_pre, theta)
+    np.testing.assert_allclose(Oc, Od, atol=1e-13)
+    np.testing.assert_allclose(Lc, Ld, atol=1e-13)
+
+
+@pytest.mark.parametrize("w0,w_pre", [(0, 4), (3, 8), (7, 5), (2, 1)])
+def test_continuous_brute_force_agrees(w0, w_pre):
+    """Scalar loops with remote pairs at q / G, k / G vs the vectorized oracle;
+    and the two maps differ once G > 1 and some pair is remote."""
+    L, Hq, Hkv, d, theta = 37, 2, 1, 8, 1e4
+    xq, xk, v = _rand(46, L, Hq, d), _rand(47, L, Hkv, d), _rand(48, L, Hkv, d)
+    O, LSE = bifocal_attention(xq, xk, v, w0, w_pre, theta, continuous=True)
+    Ob, Lb = brute_attention(xq.tolist(), xk.tolist(), v.tolist(), w0, w_pre, theta,
+                             continuous=True)
+    np.testing.assert_allclose(O, np.array(Ob), atol=1e-12)
+    np.testing.assert_allclose(LSE, np.array(Lb), atol=1e-12)
+    Od, _ = bifocal_attention(xq, xk, v, w0, w_pre, theta)
+    assert np.abs(O - Od).max() > 1e-3
+
+
+def test_continuous_remote_scores_shift_invariant_by_any_step():
+    """Remote scores of the continuous map depend on (q - k) / G only, so any
+    integer shift of both positions leaves them unchanged (the floor map
+    needs multiples of G)."""
+    d, theta, G = 16, 1e4, 4
+    xq, xk = _rand(49, 6, d), _rand(50, 6, d)
+    qp = np.array([100, 101, 102, 103, 104, 105])
+    kp = np.array([10, 11, 12, 13, 14, 15])
+    r0 = bifocal_scores(xq, qp, xk, kp, -1, G, theta, continuous=True)
+    for c in (1, 3, 17):
+        r1 = bifocal_scores(xq, qp + c, xk, kp + c, -1, G, theta, continuous=True)
+        np.testing.assert_allclose(r0, r1, atol=1e-10)
+    rf0 = bifocal_scores(xq, qp, xk, kp, -1, G, theta)
+    rf1 = bifocal_scores(xq, qp + 1, xk, kp + 1, -1, G, theta)
+    assert np.abs(rf1 - rf0).max() > 1e-3
+
+
+@pytest.mark.parametrize("pos", [6, 8, 9, 17, 30])
+def test_continuous_decode_row_equals_prefill_last_row(pos):
+    """The decode form (keys rotated at their own route, real positions)
+    equals row p of the continuous prefill of length p + 1."""
+    Hq, Hkv, d, theta, w0, w_pre = 4, 2, 8, 1e4, 3, 8
+    C = 40
+    xq, xk, v = _rand(51, C, Hq, d), _rand(52, C, Hkv, d), _rand(53, C, Hkv, d)
+    o, lse = decode_row(xq[pos], xk, v, pos, w0, w_pre, theta, continuous=True)
+    O, LSE = bifocal_attention(xq[: pos + 1], xk[: pos + 1], v[: pos + 1], w0, w_pre, theta,
+                               rows=[pos], continuous=True)
+    np.testing.assert_allclose(o, O[0], atol=1e-13)
+    np.testing.assert_allclose(lse, LSE[:, 0], atol=1e-13)
+
+
+def test_continuous_correction_rotation_of_cached_keys():
+    """R_{k/G - k} applied to a key rotated at k gives the key rotated at
+    k / G: the cache stays valid for the continuous map too (rotations by
+    real angles compose additively) [Digest/Method, "KV cache invariant"]."""
+    d, theta, G = 32, 1e6, 3
+    k = np.arange(0, 5000, 7)
+    x = _rand(54, len(k), 1, d)
+    corr = rope(rope(x, k, theta), k / G - k, theta)
+    np.testing.assert_allclose(corr, rope(x, k / G, theta), atol=1e-9)
+
+
+@pytest.mark.parametrize("L,w0,w_pre", [(40, 6, 10), (57, 9, 7)])
+def test_continuous_inclusion_exclusion_equals_masked(L, w0, w_pre):
+    """Eq. 7 over the three passes with B and C at x / G equals the direct
+    continuous result."""
+    Hq, Hkv, d, theta = 2, 1, 8, 1e4
+    G = group_size(L, w_pre)
+    xq, xk, v = _rand(55, L, Hq, d), _rand(56, L, Hkv, d), _rand(57, L, Hkv, d)
+    parts = [ie_pass(xq, xk, v, w, w0, G, theta, continuous=True) for w in "ABC"]
+    O, LSE = ie_merge(*parts[0], *parts[1], *parts[2])
+    Od, Ld = bifocal_attention(xq, xk, v, w0, w_pre, theta, continuous=True)
+    np.testing.assert_allclose(O, Od, atol=1e-10)
+    np.testing.assert_allclose(LSE, Ld, atol=1e-10)

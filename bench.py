@@ -13,9 +13,9 @@ Also reported (not part of the timed step): the attention kernel alone (live
 HIP events around it, for the roofline), the library's plain causal RoPE
 attention at the same shape (overhead ratio), the Eq. 7 inclusion-exclusion
 alternative, the 64K and packed-varlen workloads, prefill continued on the cache for the
-last 8192 rows, a window-size sweep, decode latency
-at positions 32767 .. 131071 of a 131072-key cache with L2 / MALL evicted
-before every step, calibrated HBM-read and MFMA ceilings, and the float64 CPU
+last 8192 rows, a window-size sweep, the continuous remote map x/G (prefill
+kernel and decode), decode latency at positions 32767 .. 131071 of a
+131072-key cache with L2 / MALL evicted before every step, calibrated HBM-read and MFMA ceilings, and the float64 CPU
 oracle on a bounded sample of rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -277,6 +277,23 @@ def main():
                              "vs_plain": round(wm / plain_ms, 4)}
         extras["w0_sweep_128k"] = sweep
 
+        # ---------------------------------------------------- continuous remote map
+        log("continuous remote map x/G at 128K (fused attention kernel)")
+        jl.bifocal_prefill(q, k, vv, w0, w_pre, theta, out=o, lse=lse, workspace=ws,
+                           remap="continuous")
+        torch.cuda.synchronize()
+        ct = []
+        for _ in range(3):
+            jl.bifocal_prefill(q, k, vv, w0, w_pre, theta, out=o, lse=lse, workspace=ws,
+                               events=pe, remap="continuous")
+            torch.cuda.synchronize()
+            ct.append(pe[0].elapsed_time(pe[1]))
+        cm = float(np.median(ct))
+        extras["continuous_map_128k"] = {"kernel_ms": round(cm, 4),
+                                         "tflops": round(flops / cm / 1e9, 2),
+                                         "vs_floor_map": round(cm / kern_avg, 4),
+                                         "vs_plain": round(cm / plain_ms, 4)}
+
         # ---------------------------------------------------- decode
         log("decode on the 131072-key absolute cache (L2/MALL evicted by a clean read per step)")
         cdec = WORKLOADS["decode_128k"]
@@ -293,15 +310,17 @@ def main():
         for pos in cdec["decode_positions"]:
             qd = q[pos].contiguous()
             row = {}
-            for mode in ("fused", "plain"):
-                for evict in ("read", "write"):
+            for mode in ("fused", "plain", "continuous"):
+                for evict in (("read",) if mode == "continuous" else ("read", "write")):
                     ts = []
                     for it in range(args.decode_iters + 3):
                         if evict == "read":
                             flush.sum()
                         else:
                             flush.zero_()
-                        jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta, mode=mode,
+                        jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta,
+                                          mode="fused" if mode == "continuous" else mode,
+                                          remap="continuous" if mode == "continuous" else "floor",
                                           out=od, lse=ld, workspace=wsd, events=de)
                         torch.cuda.synchronize()
                         if it >= 3:

@@ -60,6 +60,17 @@ typedef enum { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
  *        the bifocal overhead is measured against. */
 typedef enum { JL_MODE_FUSED = 0, JL_MODE_IE = 1, JL_MODE_PLAIN = 2 } jl_mode;
 
+/* Remote-map flag, OR-ed into the mode argument of every call that takes one
+ * (e.g. (jl_mode)(JL_MODE_FUSED | JL_REMAP_CONTINUOUS)). Without it the
+ * remote branch of Eq. 1 rotates at f(x) = floor(x / G), the aliasing map.
+ * With it f(x) = x / G as a real number: continuous frequency interpolation by
+ * the same G, the arm the aliasing map is compared against in the pith.science
+ * review's Table 6 discussion (Referee Report major comment 2; ledger axiom on
+ * the discrete angle grid). The window, G, routing and tiling are unchanged,
+ * and the cached keys are corrected by the real-angle rotation R_{k/G - k}.
+ * JL_MODE_PLAIN has no remote pair and ignores the flag. */
+#define JL_REMAP_CONTINUOUS 16
+
 /* Eq. 2: G = max(1, ceil(L / w_pre)) in exact integer arithmetic.
  * Returns G >= 1, or JL_EINVAL when L < 1 or w_pre < 1. Host only. */
 int64_t jl_group_size(int64_t L, int64_t w_pre);

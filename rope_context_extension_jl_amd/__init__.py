@@ -18,12 +18,19 @@ __all__ = [
     "status_string", "rope_apply", "prefill_workspace_size", "bifocal_prefill",
     "decode_workspace_size", "bifocal_decode", "debug_tile_classes", "ie_ratio_view",
     "prefill_cached_workspace_size", "bifocal_prefill_cached",
-    "calib_stream_read", "calib_mfma_bf16", "MODES",
+    "calib_stream_read", "calib_mfma_bf16", "MODES", "REMAPS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbifocal.so")
 JL_BF16, JL_FP32 = 0, 1
 MODES = {"fused": 0, "ie": 1, "plain": 2}
+# Remote map, OR-ed into the mode code: floor(x / G) (aliasing) or the real
+# x / G (continuous frequency interpolation, JL_REMAP_CONTINUOUS).
+REMAPS = {"floor": 0, "continuous": 16}
+
+
+def _mode_code(mode: str, remap: str) -> int:
+    return MODES[mode] | REMAPS[remap]
 
 _c_i64, _c_int, _c_dbl, _c_flt, _c_p, _c_sz = (ctypes.c_int64, ctypes.c_int, ctypes.c_double,
                                               ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t)
@@ -195,10 +202,11 @@ def bifocal_prefill(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, w0: int
                     cu_seqlens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, kcache_out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
-                    events=None):
+                    events=None, remap: str = "floor"):
     """Causal bifocal attention; xq/xk/v are RAW [T, H, d]. Returns (o, lse).
     events: optional (begin, end) torch.cuda.Event pair, recorded around the
-    attention kernels only (jl_bifocal_prefill_timed)."""
+    attention kernels only (jl_bifocal_prefill_timed). remap: "floor" or
+    "continuous" (remote positions x / G as real numbers)."""
     T, Hq, d = xq.shape
     Hkv = xk.shape[1]
     B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -212,7 +220,7 @@ def bifocal_prefill(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, w0: int
     st = lib().jl_bifocal_prefill_timed(
         _dev(xq, "xq"), _dev(xk, "xk"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
         _dev(kcache_out, "kcache_out"), _dev(cu_seqlens, "cu_seqlens"), B, T, Hq, Hkv, d,
-        int(w0), int(w_pre), float(theta), float(scale), _dtype_code(xq), MODES[mode],
+        int(w0), int(w_pre), float(theta), float(scale), _dtype_code(xq), _mode_code(mode, remap),
         _dev(workspace, "workspace"), workspace.numel(), _stream(xq.device), *_events(events))
     _check("jl_bifocal_prefill", st)
     return out, lse
@@ -231,7 +239,7 @@ def bifocal_prefill_cached(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch
                            mode: str = "fused", out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None,
                            workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
-                           events=None):
+                           events=None, remap: str = "floor"):
     """Chunked prefill: RAW queries xq [Tq, Hq, d] at positions q_off .. q_off+Tq-1
     against the absolute cache [capacity, Hkv, d] (rows up to q_off+Tq-1 filled).
     Returns (o [Tq, Hq, d], lse [Hq, Tq])."""
@@ -247,7 +255,7 @@ def bifocal_prefill_cached(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch
     st = lib().jl_bifocal_prefill_cached_timed(
         _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
         _dev(lse, "lse"), int(q_off), Tq, C, Hq, Hkv, d, int(w0), int(w_pre), float(theta),
-        float(scale), _dtype_code(xq), MODES[mode], _dev(workspace, "workspace"),
+        float(scale), _dtype_code(xq), _mode_code(mode, remap), _dev(workspace, "workspace"),
         workspace.numel(), _stream(xq.device), *_events(events))
     _check("jl_bifocal_prefill_cached", st)
     return out, lse
@@ -257,7 +265,7 @@ def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                    w0: int, w_pre: int, theta: float, scale: float = 0.0, mode: str = "fused",
                    num_splits: int = 0, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   want_lse: bool = True, events=None):
+                   want_lse: bool = True, events=None, remap: str = "floor"):
     """One decode step at `pos` with a RAW query xq [Hq, d] against the absolute
     cache [capacity, Hkv, d]. Returns (o [Hq, d], lse [Hq])."""
     Hq, d = xq.shape
@@ -272,7 +280,8 @@ def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
     st = lib().jl_bifocal_decode_timed(
         _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
         _dev(lse, "lse"), int(pos), C, Hq, Hkv, d, int(w0), int(w_pre), float(theta),
-        float(scale), _dtype_code(xq), MODES[mode], int(num_splits), _dev(workspace, "workspace"),
+        float(scale), _dtype_code(xq), _mode_code(mode, remap), int(num_splits),
+        _dev(workspace, "workspace"),
         workspace.numel(), _stream(xq.device), *_events(events))
     _check("jl_bifocal_decode", st)
     return out, lse

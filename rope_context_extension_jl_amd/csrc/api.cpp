@@ -102,6 +102,13 @@ int jl_rope_apply(void* x, int64_t T, int H, int d, const int32_t* cu_seqlens, i
                                       dt == JL_FP32, (hipStream_t)stream));
 }
 
+// The remote-map flag rides in the mode argument; the rest is the mode proper.
+static jl_mode strip_remap(jl_mode mode, int* cont) {
+  const int m = (int)mode;
+  if (cont) *cont = (m & JL_REMAP_CONTINUOUS) ? 1 : 0;
+  return (jl_mode)(m & ~JL_REMAP_CONTINUOUS);
+}
+
 static bool prefill_shape_ok(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt, jl_mode mode) {
   if (T < 0 || B < 1 || B > 4096 || Hq < 1 || Hkv < 1 || Hq % Hkv) return false;
   if (T > (int64_t)INT32_MAX / 2) return false;
@@ -113,6 +120,7 @@ static bool prefill_shape_ok(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype 
 
 size_t jl_prefill_workspace_size(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt,
                                  jl_mode mode) {
+  mode = strip_remap(mode, nullptr);
   if (!prefill_shape_ok(T, B, Hq, Hkv, d, dt, mode)) return 0;
   return prefill_layout(T, B, Hq, Hkv, d, dt, mode).total;
 }
@@ -127,6 +135,8 @@ int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void
                              int Hq, int Hkv, int d, int64_t w0, int64_t w_pre, double theta,
                              float scale, jl_dtype dt, jl_mode mode, void* workspace,
                              size_t ws_bytes, void* stream, void* ev_begin, void* ev_end) {
+  int cont;
+  mode = strip_remap(mode, &cont);
   if (!cu_seqlens && B != 1) return JL_EINVAL;
   if (!prefill_shape_ok(T, B, Hq, Hkv, d, dt, mode)) return JL_EINVAL;
   if (w0 < 0 || w_pre < 1 || !(theta > 1.0) || !(scale == scale)) return JL_EINVAL;
@@ -148,7 +158,7 @@ int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void
   const int need_rem = mode != JL_MODE_PLAIN;
   if (dt == JL_BF16) {
     e = launch_prefill_prep_bf16(xk, v, kcache_out, T, B, Hkv, need_rem, 0,
-                                 sc * 1.4426950408889634f, fr, workspace, lay, st);
+                                 sc * 1.4426950408889634f, cont, fr, workspace, lay, st);
     if (e != hipSuccess) return hip_status(e);
     if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
       return hip_status(e);
@@ -159,16 +169,17 @@ int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void
       const int passes[3] = {PASS_IE_A, PASS_IE_B, PASS_IE_C};
       for (int i = 0; i < 3; ++i) {
         e = launch_prefill_bf16(passes[i], xq, base_o + i * on, base_l + i * ln, T, B, Hq, Hkv,
-                                w0, 0, sc, fr, workspace, lay, st);
+                                w0, 0, sc, cont, fr, workspace, lay, st);
         if (e != hipSuccess) return hip_status(e);
       }
       e = launch_ie_merge(o, lse, 0, T, Hq, d, workspace, lay, st);
     } else {
       e = launch_prefill_bf16(mode == JL_MODE_PLAIN ? PASS_PLAIN : PASS_FUSED, xq, o, lse, T, B,
-                              Hq, Hkv, w0, 0, sc, fr, workspace, lay, st);
+                              Hq, Hkv, w0, 0, sc, cont, fr, workspace, lay, st);
     }
   } else {
-    e = launch_prefill_prep_f32(xk, kcache_out, T, B, Hkv, d, need_rem, fr, workspace, lay, st);
+    e = launch_prefill_prep_f32(xk, kcache_out, T, B, Hkv, d, need_rem, cont, fr, workspace, lay,
+                                st);
     if (e != hipSuccess) return hip_status(e);
     if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
       return hip_status(e);
@@ -179,13 +190,13 @@ int jl_bifocal_prefill_timed(const void* xq, const void* xk, const void* v, void
       const int passes[3] = {PASS_IE_A, PASS_IE_B, PASS_IE_C};
       for (int i = 0; i < 3; ++i) {
         e = launch_prefill_f32(passes[i], xq, v, base_o + i * on, base_l + i * ln, T, B, Hq, Hkv,
-                               d, w0, sc, fr, workspace, lay, st);
+                               d, w0, sc, cont, fr, workspace, lay, st);
         if (e != hipSuccess) return hip_status(e);
       }
       e = launch_ie_merge(o, lse, 1, T, Hq, d, workspace, lay, st);
     } else {
       e = launch_prefill_f32(mode == JL_MODE_PLAIN ? PASS_PLAIN : PASS_FUSED, xq, v, o, lse, T, B,
-                             Hq, Hkv, d, w0, sc, fr, workspace, lay, st);
+                             Hq, Hkv, d, w0, sc, cont, fr, workspace, lay, st);
     }
   }
   if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
@@ -210,6 +221,7 @@ static bool cached_shape_ok(int64_t q_off, int64_t Tq, int Hq, int Hkv) {
 
 size_t jl_prefill_cached_workspace_size(int64_t q_off, int64_t Tq, int Hq, int Hkv, int d,
                                         jl_mode mode) {
+  mode = strip_remap(mode, nullptr);
   if (!cached_shape_ok(q_off, Tq, Hq, Hkv) || d != PF_D) return 0;
   if (mode != JL_MODE_FUSED && mode != JL_MODE_PLAIN) return 0;
   return prefill_layout(q_off + Tq, 1, Hq, Hkv, d, JL_BF16, mode).total;
@@ -221,6 +233,8 @@ int jl_bifocal_prefill_cached_timed(const void* xq, const void* kcache, const vo
                                     int64_t w_pre, double theta, float scale, jl_dtype dt,
                                     jl_mode mode, void* workspace, size_t ws_bytes, void* stream,
                                     void* ev_begin, void* ev_end) {
+  int cont;
+  mode = strip_remap(mode, &cont);
   if (!cached_shape_ok(q_off, Tq, Hq, Hkv)) return JL_EINVAL;
   if (capacity < 1 || q_off + Tq > capacity) return JL_EINVAL;
   if (w0 < 0 || w_pre < 1 || !(theta > 1.0) || !(scale == scale)) return JL_EINVAL;
@@ -242,12 +256,12 @@ int jl_bifocal_prefill_cached_timed(const void* xq, const void* kcache, const vo
   hipError_t e = launch_prefill_plan(nullptr, 1, L, q_off, w_pre, PF_BM, workspace, lay, st);
   if (e != hipSuccess) return hip_status(e);
   e = launch_prefill_prep_bf16(kcache, vcache, nullptr, L, 1, Hkv, mode != JL_MODE_PLAIN, 1,
-                               sc * 1.4426950408889634f, fr, workspace, lay, st);
+                               sc * 1.4426950408889634f, cont, fr, workspace, lay, st);
   if (e != hipSuccess) return hip_status(e);
   if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
     return hip_status(e);
   e = launch_prefill_bf16(mode == JL_MODE_PLAIN ? PASS_PLAIN : PASS_FUSED, xq, o, lse, Tq, 1, Hq,
-                          Hkv, w0, q_off, sc, fr, workspace, lay, st);
+                          Hkv, w0, q_off, sc, cont, fr, workspace, lay, st);
   if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
   return hip_status(e);
 }
@@ -277,6 +291,8 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
                             int64_t w0, int64_t w_pre, double theta, float scale, jl_dtype dt,
                             jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
                             void* stream, void* ev_begin, void* ev_end) {
+  int cont;
+  mode = strip_remap(mode, &cont);
   if (pos < 0 || capacity < 1 || pos >= capacity || capacity > (int64_t)INT32_MAX) return JL_EINVAL;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 0 || w_pre < 1 || !(theta > 1.0)) return JL_EINVAL;
   if (num_splits < 0 || !(scale == scale)) return JL_EINVAL;
@@ -329,7 +345,7 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
     return hip_status(e);
   e = launch_decode(xq, kcache, vcache, o, lse, pos, Hq, Hkv, d,
                     w0 > (int64_t)INT32_MAX ? INT32_MAX : w0, G, sc, fr, mode == JL_MODE_PLAIN,
-                    dt == JL_FP32, S, workspace, st);
+                    cont, dt == JL_FP32, S, workspace, st);
   if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
   return hip_status(e);
 }

@@ -31,6 +31,8 @@ struct DecArgs {
   void* o;
   float* lse;
   int pos, Hq, Hkv, w0, G, plain, S, kps;
+  int cont;        // remote map x / G (real) instead of floor(x / G)
+  double fk_rel;   // with cont: f(k) - k = k * fk_rel, fk_rel = 1 / G - 1
   float scale_log2;
   RopeFreqs fr;
 };
@@ -67,7 +69,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int dl = lane % NL, kl = lane / NL;
   const int h0 = g * R;
-  const int fpos = a.pos / a.G;
+  const double fpos = remap_pos(a.pos, a.G, a.cont);
   // rotated queries for the R heads of this KV group
   for (int idx = tid; idx < R * HALF; idx += 256) {
     const int hl = idx / HALF, i = idx % HALF;
@@ -77,7 +79,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
     rope_cs((double)a.pos, a.fr.w(i), c, sn);
     qa_s[hl][i] = x0 * c - x1 * sn;
     qa_s[hl][HALF + i] = x0 * sn + x1 * c;
-    rope_cs((double)fpos, a.fr.w(i), c, sn);
+    rope_cs(fpos, a.fr.w(i), c, sn);
     qr_s[hl][i] = x0 * c - x1 * sn;
     qr_s[hl][HALF + i] = x0 * sn + x1 * c;
   }
@@ -118,12 +120,13 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
     }
     const bool remote = !a.plain && (a.pos - kk > a.w0);
     if (remote && a.G > 1) {
-      const int delta = kk / a.G - kk;  // f(k) - k
+      // f(k) - k
+      const double delta = a.cont ? (double)kk * a.fk_rel : (double)(kk / a.G - kk);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float c, sn;
-        if constexpr (F32) rope_cs((double)delta, wl[e], c, sn);
-        else rope_cs_turns((double)delta, wl[e], c, sn);
+        if constexpr (F32) rope_cs(delta, wl[e], c, sn);
+        else rope_cs_turns(delta, wl[e], c, sn);
         const float x0 = k0[e], x1 = k1[e];
         k0[e] = x0 * c - x1 * sn;
         k1[e] = x0 * sn + x1 * c;
@@ -260,6 +263,8 @@ struct DecCtx {
   const uint16_t* vbase;  // the head's V row 0
   int64_t rstride;        // elements between consecutive keys
   int pos, w0, G, plain, correct, k_hi;
+  int cont;       // remote map x / G (real) instead of floor(x / G)
+  double fk_rel;  // with cont: f(k) - k = k * fk_rel
   int lane, g16, r16;
 };
 
@@ -362,7 +367,7 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
     dh8v kf[NDS];
     if (c.correct && c.pos - key > c.w0) {
       // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2)
-      const double delta = (double)(key / c.G - key);
+      const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
@@ -495,7 +500,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   {
     const bool qv = r16 < R;
     const uint16_t* qp = xq + (int64_t)(h0 + (qv ? r16 : 0)) * D;
-    const int fpos = a.pos / a.G;
+    const double fpos = remap_pos(a.pos, a.G, a.cont);
 #pragma unroll
     for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
@@ -507,7 +512,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
         rope_cs_turns((double)a.pos, w2pi_s[i], c, sn);
         qa[ds][j] = (_Float16)((x0 * c - x1 * sn) * a.scale_log2);
         qa[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * c) * a.scale_log2);
-        rope_cs_turns((double)fpos, w2pi_s[i], c, sn);
+        rope_cs_turns(fpos, w2pi_s[i], c, sn);
         qr[ds][j] = (_Float16)((x0 * c - x1 * sn) * a.scale_log2);
         qr[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * c) * a.scale_log2);
       }
@@ -521,6 +526,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   c.pos = a.pos;
   c.w0 = a.w0;
   c.G = a.G;
+  c.cont = a.cont;
+  c.fk_rel = a.fk_rel;
   c.plain = a.plain;
   c.correct = !a.plain && a.G > 1;
   c.lane = lane;
@@ -648,8 +655,8 @@ static void launch_decode_t(int R, dim3 grid, hipStream_t st, const DecArgs& a) 
 
 hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
                          int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
-                         const RopeFreqs& fr, int plain, int is_f32, int num_splits, void* ws,
-                         hipStream_t st) {
+                         const RopeFreqs& fr, int plain, int cont, int is_f32, int num_splits,
+                         void* ws, hipStream_t st) {
   DecArgs a;
   a.xq = xq;
   a.kc = kc;
@@ -663,6 +670,8 @@ hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o
   a.w0 = (int)w0;
   a.G = (int)G;
   a.plain = plain;
+  a.cont = cont;
+  a.fk_rel = 1.0 / (double)G - 1.0;
   const int keys = (int)pos + 1;
   int kps = (keys + num_splits - 1) / num_splits;
   a.S = (keys + kps - 1) / kps;  // no empty split

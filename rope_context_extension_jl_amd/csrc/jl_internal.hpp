@@ -79,23 +79,25 @@ hipError_t launch_prefill_plan(const int32_t* cu, int B, int64_t T, int64_t qoff
 
 // from_abs: the keys are already rotated at their absolute positions.
 // kscale multiplies the fp16 key operands (not the bf16 cache written).
+// cont (here and below): remote positions are the real numbers x / G
+// instead of floor(x / G) (the continuous-interpolation remote map).
 hipError_t launch_prefill_prep_bf16(const void* xk, const void* v, void* kcache_out, int64_t T,
                                     int B, int Hkv, int need_rem, int from_abs, float kscale,
-                                    const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
-                                    hipStream_t st);
+                                    int cont, const RopeFreqs& fr, void* ws,
+                                    const PrefillLayout& lay, hipStream_t st);
 
 hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, int64_t T, int B,
-                               int Hq, int Hkv, int64_t w0, int64_t qoff, float scale,
+                               int Hq, int Hkv, int64_t w0, int64_t qoff, float scale, int cont,
                                const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
                                hipStream_t st);
 
 hipError_t launch_prefill_prep_f32(const void* xk, void* kcache_out, int64_t T, int B, int Hkv,
-                                   int d, int need_rem, const RopeFreqs& fr, void* ws,
+                                   int d, int need_rem, int cont, const RopeFreqs& fr, void* ws,
                                    const PrefillLayout& lay, hipStream_t st);
 
 hipError_t launch_prefill_f32(int pass, const void* xq, const void* v, void* o, float* lse,
                               int64_t T, int B, int Hq, int Hkv, int d, int64_t w0, float scale,
-                              const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
+                              int cont, const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
                               hipStream_t st);
 
 hipError_t launch_ie_merge(void* o, float* lse, int out_f32, int64_t T, int Hq, int d, void* ws,
@@ -103,8 +105,8 @@ hipError_t launch_ie_merge(void* o, float* lse, int out_f32, int64_t T, int Hq, 
 
 hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
                          int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
-                         const RopeFreqs& fr, int plain, int is_f32, int num_splits, void* ws,
-                         hipStream_t st);
+                         const RopeFreqs& fr, int plain, int cont, int is_f32, int num_splits,
+                         void* ws, hipStream_t st);
 
 hipError_t launch_tile_dump(int64_t L, int64_t w0, int8_t* out, hipStream_t st);
 
@@ -139,6 +141,13 @@ __device__ inline void rope_cs_turns(double p, double w2pi, float& c, float& s) 
   const float f = (float)(t - __builtin_rint(t));
   s = __builtin_amdgcn_sinf(f);
   c = __builtin_amdgcn_cosf(f);
+}
+
+// Remote position f(x) of Eq. 1: floor(x / G), the aliasing map, or with
+// cont set the real number x / G (continuous frequency interpolation by the
+// same factor: a rotation by (x / G) w is a rotation by x at frequency w / G).
+__device__ inline double remap_pos(int x, int G, int cont) {
+  return cont ? (double)x / (double)G : (double)(x / G);
 }
 
 __device__ inline float bf16_bits_to_f32(uint16_t b) {

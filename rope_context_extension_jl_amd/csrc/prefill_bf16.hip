@@ -188,7 +188,7 @@ __device__ inline int seq_of_padded_row(const SeqInfo* seqs, int B, int r) {
 __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
     const uint16_t* __restrict__ xk, const uint16_t* __restrict__ v, uint16_t* __restrict__ kcache,
     const SeqInfo* __restrict__ seqs, const int* __restrict__ hdr, int B, int Hkv, int R,
-    int need_rem, int from_abs, float kscale, uint16_t* __restrict__ kabs,
+    int need_rem, int from_abs, float kscale, int cont, uint16_t* __restrict__ kabs,
     uint16_t* __restrict__ krem, uint16_t* __restrict__ vt, RopeFreqs fr) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * (PF_D + 8)];
   const int r0 = blockIdx.x * 64;
@@ -205,7 +205,8 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
     const bool valid = trel < sq.len;
     float ca[8], sa[8], cr[8], sr[8];
     const double pa = from_abs ? 0.0 : (double)trel;
-    const double pr = from_abs ? (double)(trel / sq.G - trel) : (double)(trel / sq.G);
+    const double fk = remap_pos(trel, sq.G, cont);
+    const double pr = from_abs ? fk - (double)trel : fk;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       rope_cs(pa, fr.w(8 * c + j), ca[j], sa[j]);
@@ -274,14 +275,14 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
 
 hipError_t launch_prefill_prep_bf16(const void* xk, const void* v, void* kcache_out, int64_t T,
                                     int B, int Hkv, int need_rem, int from_abs, float kscale,
-                                    const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
-                                    hipStream_t st) {
+                                    int cont, const RopeFreqs& fr, void* ws,
+                                    const PrefillLayout& lay, hipStream_t st) {
   char* w = (char*)ws;
   const int blocks = (int)(lay.R / 64);
   hipLaunchKernelGGL(prefill_prep_bf16_kernel, dim3(blocks), dim3(256), 0, st,
                      (const uint16_t*)xk, (const uint16_t*)v, (uint16_t*)kcache_out,
                      (const SeqInfo*)(w + lay.seqs), (const int*)(w + lay.hdr), B, Hkv,
-                     (int)lay.R, need_rem, from_abs, kscale, (uint16_t*)(w + lay.kabs),
+                     (int)lay.R, need_rem, from_abs, kscale, cont, (uint16_t*)(w + lay.kabs),
                      (uint16_t*)(w + lay.krem), (uint16_t*)(w + lay.vt), fr);
   (void)T;
   return hipGetLastError();
@@ -305,6 +306,7 @@ struct PfArgs {
   int T, R, Hq, Hkv, w0;
   int qoff;       // position of the first query row (0 unless continuing on a cache)
   int ie_remote;  // pass B of Eq. 7 (1) or pass C (0)
+  int cont;       // remote map x / G (real) instead of floor(x / G)
   RopeFreqs fr;
 };
 
@@ -582,7 +584,7 @@ __device__ __forceinline__ void walk_boundary(const Tctx& c, int j0, int j1, int
 // RoPE(x_q, p) of the lane's raw query row as the fp16 QK^T operand. The lane
 // holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs (d, d+64)
 // are chunks (c, c+4) of the same lane. w2pi: omega_i / (2 pi) in LDS.
-__device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], int p, int hh,
+__device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], double p, int hh,
                                              const double* w2pi, h8v (&out)[8]) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -590,7 +592,7 @@ __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], int p, int h
     for (int j = 0; j < 8; ++j) {
       const float x0 = bf16_lane(raw[c], j), x1 = bf16_lane(raw[c + 4], j);
       float cs, sn;
-      rope_cs_turns((double)p, w2pi[16 * c + 8 * hh + j], cs, sn);
+      rope_cs_turns(p, w2pi[16 * c + 8 * hh + j], cs, sn);
       out[c][j] = (_Float16)(x0 * cs - x1 * sn);
       out[c + 4][j] = (_Float16)(x0 * sn + x1 * cs);
     }
@@ -654,7 +656,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   // before each rotation rather than kept live across the key loops
   const uint16_t* qp =
       a.xq + ((int64_t)(sq.start + (qvalid ? c.myq - a.qoff : 0)) * Hq + head) * PF_D + 8 * c.hh;
-  auto rotq = [&](int p, h8v (&out)[8]) __attribute__((always_inline)) {
+  auto rotq = [&](double p, h8v (&out)[8]) __attribute__((always_inline)) {
     u32x4 raw[8];
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
@@ -692,7 +694,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     const int jl0 = max(j_nr, j_loc);
     {
       h8v qr[8];
-      rotq(c.myq / sq.G, qr);
+      rotq(remap_pos(c.myq, sq.G, a.cont), qr);
       // remote phase: remapped query against remapped key tiles
       walk(c, 0, j_nr, true, j_nr < c.nkt ? j_nr : -1, false, MASK_NONE, qr, Ks, Vs, stg, st);
       if (j_nr < j_loc) {  // boundary phase: both routes, element-wise select
@@ -720,7 +722,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     // keys of the boundary tiles and the all-remote tiles. The shared window
     // part then cancels in W_B O_B - W_C O_C up to fp32 rounding.
     h8v qr[8];
-    rotq(c.myq / sq.G, qr);
+    rotq(remap_pos(c.myq, sq.G, a.cont), qr);
     const int seg2 = j_nr < j_loc ? j_nr : (j_nr > 0 ? 0 : -1);
     walk(c, j_nr, c.nkt, true, a.ie_remote ? seg2 : -1, true, MASK_WINDOW, qr, Ks, Vs, stg, st);
     if (a.ie_remote) {
@@ -763,7 +765,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
 }
 
 hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, int64_t T, int B,
-                               int Hq, int Hkv, int64_t w0, int64_t qoff, float scale,
+                               int Hq, int Hkv, int64_t w0, int64_t qoff, float scale, int cont,
                                const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
                                hipStream_t st) {
   char* w = (char*)ws;
@@ -786,6 +788,7 @@ hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, in
   a.w0 = (int)w0;
   a.qoff = (int)qoff;
   a.ie_remote = pass == PASS_IE_B;
+  a.cont = cont;
   (void)scale;  // the score scale is carried by the key operands (pre-pass)
   a.fr = fr;
   const int64_t blocks = lay.max_tiles * Hq;

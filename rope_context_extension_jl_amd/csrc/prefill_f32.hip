@@ -24,7 +24,8 @@ __device__ inline int seq_of_padded_row32(const SeqInfo* seqs, int B, int r) {
 template <int D>
 __global__ void __launch_bounds__(256) prefill_prep_f32_kernel(
     const float* __restrict__ xk, float* __restrict__ kcache, const SeqInfo* __restrict__ seqs,
-    const int* __restrict__ hdr, int B, int Hkv, int R, int need_rem, float* __restrict__ kabs,
+    const int* __restrict__ hdr, int B, int Hkv, int R, int need_rem, int cont,
+    float* __restrict__ kabs,
     float* __restrict__ krem, RopeFreqs fr) {
   constexpr int GROUPS = D / 16;            // 8 pairs per thread
   constexpr int ROWS_PER_PASS = 256 / GROUPS;
@@ -41,7 +42,7 @@ __global__ void __launch_bounds__(256) prefill_prep_f32_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       rope_cs((double)trel, fr.w(8 * c + j), ca[j], sa[j]);
-      if (need_rem) rope_cs((double)(trel / sq.G), fr.w(8 * c + j), cr[j], sr[j]);
+      if (need_rem) rope_cs(remap_pos(trel, sq.G, cont), fr.w(8 * c + j), cr[j], sr[j]);
     }
     for (int g = 0; g < Hkv; ++g) {
       float x0[8], x1[8];
@@ -73,7 +74,7 @@ __global__ void __launch_bounds__(256) prefill_prep_f32_kernel(
 }
 
 hipError_t launch_prefill_prep_f32(const void* xk, void* kcache_out, int64_t T, int B, int Hkv,
-                                   int d, int need_rem, const RopeFreqs& fr, void* ws,
+                                   int d, int need_rem, int cont, const RopeFreqs& fr, void* ws,
                                    const PrefillLayout& lay, hipStream_t st) {
   char* w = (char*)ws;
   const int blocks = (int)(lay.R / 64);
@@ -82,11 +83,11 @@ hipError_t launch_prefill_prep_f32(const void* xk, void* kcache_out, int64_t T, 
   if (d == 64)
     hipLaunchKernelGGL(prefill_prep_f32_kernel<64>, dim3(blocks), dim3(256), 0, st,
                        (const float*)xk, (float*)kcache_out, seqs, hdr, B, Hkv, (int)lay.R,
-                       need_rem, (float*)(w + lay.kabs), (float*)(w + lay.krem), fr);
+                       need_rem, cont, (float*)(w + lay.kabs), (float*)(w + lay.krem), fr);
   else
     hipLaunchKernelGGL(prefill_prep_f32_kernel<128>, dim3(blocks), dim3(256), 0, st,
                        (const float*)xk, (float*)kcache_out, seqs, hdr, B, Hkv, (int)lay.R,
-                       need_rem, (float*)(w + lay.kabs), (float*)(w + lay.krem), fr);
+                       need_rem, cont, (float*)(w + lay.kabs), (float*)(w + lay.krem), fr);
   (void)T;
   return hipGetLastError();
 }
@@ -103,6 +104,7 @@ struct Pf32Args {
   const int* order;
   const int* tbase;
   int T, R, Hq, Hkv, w0;
+  int cont;  // remote map x / G (real) instead of floor(x / G)
   float scale;
   RopeFreqs fr;
 };
@@ -136,7 +138,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(Pf32Args a) {
   float qa[D], qr[D], acc[D];
   {
     const float* qp = a.xq + ((int64_t)(sq.start + (qvalid ? myq : 0)) * a.Hq + head) * D;
-    const int fq = myq / sq.G;
+    const double fq = remap_pos(myq, sq.G, a.cont);
 #pragma unroll
     for (int i = 0; i < D / 2; ++i) {
       const float x0 = qvalid ? qp[i] : 0.f, x1 = qvalid ? qp[i + D / 2] : 0.f;
@@ -147,7 +149,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(Pf32Args a) {
         qa[i + D / 2] = x0 * s + x1 * c;
       }
       if (kRem) {
-        rope_cs((double)fq, a.fr.w(i), c, s);
+        rope_cs(fq, a.fr.w(i), c, s);
         qr[i] = x0 * c - x1 * s;
         qr[i + D / 2] = x0 * s + x1 * c;
       }
@@ -230,7 +232,7 @@ static void launch_f32_pass(int pass, dim3 grid, hipStream_t st, const Pf32Args&
 
 hipError_t launch_prefill_f32(int pass, const void* xq, const void* v, void* o, float* lse,
                               int64_t T, int B, int Hq, int Hkv, int d, int64_t w0, float scale,
-                              const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
+                              int cont, const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
                               hipStream_t st) {
   char* w = (char*)ws;
   Pf32Args a;
@@ -250,6 +252,7 @@ hipError_t launch_prefill_f32(int pass, const void* xq, const void* v, void* o, 
   a.Hkv = Hkv;
   a.w0 = (int)w0;
   a.scale = scale;
+  a.cont = cont;
   a.fr = fr;
   const dim3 grid((unsigned)(lay.max_tiles * Hq));
   if (d == 64) launch_f32_pass<64>(pass, grid, st, a);

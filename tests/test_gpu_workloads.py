@@ -44,30 +44,32 @@ class _Prefill:
         self.rows = _rows(rng, L, cfg["w0"], cfg["w_pre"])
         q, k, v = to_dev(self.xq), to_dev(self.xk), to_dev(self.v)
         self.out = {}
-        for mode in modes:
-            note(f"{name}: GPU prefill mode={mode}")
+        for key in modes:
+            # "<mode>" or "<mode>-continuous" (remote positions x / G, real)
+            mode, _, remap = key.partition("-")
+            note(f"{name}: GPU prefill mode={mode} remap={remap or 'floor'}")
             ws = torch.empty(jl.prefill_workspace_size(L, 1, cfg["Hq"], cfg["Hkv"], cfg["d"],
                                                        mode=mode), dtype=torch.uint8,
                              device="cuda")
             o, lse = jl.bifocal_prefill(q, k, v, cfg["w0"], cfg["w_pre"], cfg["theta"], mode=mode,
-                                        workspace=ws)
+                                        workspace=ws, remap=remap or "floor")
             torch.cuda.synchronize()
             ratio = None
             if mode == "ie":
                 ratio = to_host(jl.ie_ratio_view(ws, L, 1, cfg["Hq"], cfg["Hkv"], cfg["d"]))
                 ratio = ratio[:, self.rows]
-            self.out[mode] = (to_host(o[self.rows]), to_host(lse)[:, self.rows], ratio)
+            self.out[key] = (to_host(o[self.rows]), to_host(lse)[:, self.rows], ratio)
             del o, lse, ws
         del q, k, v
         torch.cuda.empty_cache()
 
-    def oracle(self, g):
+    def oracle(self, g, continuous=False):
         """fp64 oracle for the query heads of KV group g on the sampled rows."""
         c = self.cfg
         r = c["Hq"] // c["Hkv"]
         hs = slice(g * r, (g + 1) * r)
         return bifocal_attention(self.xq[:, hs], self.xk[:, g:g + 1], self.v[:, g:g + 1], c["w0"],
-                                 c["w_pre"], c["theta"], rows=self.rows)
+                                 c["w_pre"], c["theta"], rows=self.rows, continuous=continuous)
 
 
 @pytest.fixture(scope="module")
@@ -80,7 +82,7 @@ def p64k():
 
 @pytest.fixture(scope="module")
 def p128k():
-    d = _Prefill("prefill_128k", modes=("fused", "ie"))
+    d = _Prefill("prefill_128k", modes=("fused", "ie", "fused-continuous"))
     yield d
     del d
     gc.collect()
@@ -113,6 +115,16 @@ def test_prefill_128k(p128k, g):
          f"max-abs (ratio<=1e3) {err[ok].max():.3e}, overall {err.max():.3e}")
     assert err[ok].max() <= 2e-2
     assert np.all(err <= 2e-2 + 64 * rt * 2.0 ** -23 * np.abs(p128k.v).max())
+
+
+@pytest.mark.parametrize("g", [0, 3, 7])
+def test_prefill_128k_continuous(p128k, g):
+    """The continuous remote map (x / G, real) at 128K, G = 4, three KV groups."""
+    r = p128k.cfg["Hq"] // p128k.cfg["Hkv"]
+    O, LSE = p128k.oracle(g, continuous=True)
+    o, lse, _ = p128k.out["fused-continuous"]
+    assert_bf16_close(o[:, g * r:(g + 1) * r], O, f"128K kv{g} fused continuous")
+    assert errs(lse[g * r:(g + 1) * r], LSE)[0] <= BF16_LSE_ABS
 
 
 # ------------------------------------------------------------------ varlen
@@ -174,6 +186,19 @@ def test_decode_128k(dec, pos):
     torch.cuda.synchronize()
     ro, rl = decode_row(dec["xq"][pos], dec["xk"], dec["v"], pos, c["w0"], c["w_pre"], c["theta"])
     assert_bf16_close(to_host(o), ro, f"decode pos={pos}")
+    assert errs(to_host(lse), rl)[0] <= BF16_LSE_ABS
+
+
+@pytest.mark.parametrize("pos", [32768, 65537, 131071])
+def test_decode_128k_continuous(dec, pos):
+    c = dec["c"]
+    note(f"decode continuous pos={pos} G={group_size(pos + 1, c['w_pre'])}")
+    o, lse = jl.bifocal_decode(to_dev(dec["xq"][pos]), dec["kc"], dec["vc"], pos, c["w0"],
+                               c["w_pre"], c["theta"], remap="continuous")
+    torch.cuda.synchronize()
+    ro, rl = decode_row(dec["xq"][pos], dec["xk"], dec["v"], pos, c["w0"], c["w_pre"], c["theta"],
+                        continuous=True)
+    assert_bf16_close(to_host(o), ro, f"decode continuous pos={pos}")
     assert errs(to_host(lse), rl)[0] <= BF16_LSE_ABS
 
 

@@ -230,3 +230,33 @@ def test_prefill_cached_empty_is_noop_and_sizes():
     assert b == jl.prefill_workspace_size(2000, 1, 8, 2, 128)
     assert jl.prefill_cached_workspace_size(0, 10, 8, 2, 64) == 0
     assert jl.prefill_cached_workspace_size(0, 10, 8, 2, 128, mode="ie") == 0
+
+
+CONT = 16  # JL_REMAP_CONTINUOUS
+
+
+def test_continuous_flag_is_declared_and_sizes_unchanged():
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+JL_REMAP_CONTINUOUS\s+16\b", text)
+    assert jl.REMAPS == {"floor": 0, "continuous": CONT}
+    f = jl.lib()
+    for m in (0, 1, 2):
+        assert f.jl_prefill_workspace_size(3000, 2, 8, 2, 128, 0, m | CONT) == \
+            f.jl_prefill_workspace_size(3000, 2, 8, 2, 128, 0, m)
+    for m in (0, 2):
+        assert f.jl_prefill_cached_workspace_size(100, 50, 8, 2, 128, m | CONT) == \
+            f.jl_prefill_cached_workspace_size(100, 50, 8, 2, 128, m)
+
+
+@pytest.mark.parametrize("mode,code", [(1 | CONT, -2), (7 | CONT, -1), (32, -1)])
+def test_continuous_flag_argument_errors(mode, code):
+    assert _decode(mode=mode) == code
+    assert _cached(mode=mode) == code
+    if mode != (1 | CONT):
+        assert _prefill(mode=mode) == code
+
+
+def test_continuous_flag_empty_calls_are_noops():
+    assert _prefill(T=0, xq=None, xk=None, v=None, o=None, ws=None, ws_bytes=0, mode=CONT) == 0
+    assert _cached(Tq=0, xq=None, kc=None, vc=None, o=None, ws=None, ws_bytes=0,
+                   mode=CONT) == 0

@@ -14,9 +14,9 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "bifoca
 MUTATIONS = {
     "window_strict": ("S = np.where(dist <= w0, s_local, s_remote) * scale",
                       "S = np.where(dist < w0, s_local, s_remote) * scale"),
-    "keys_not_remapped": ("kr_all = rope(xk, remap(kpos, G), theta)",
+    "keys_not_remapped": ("kr_all = rope(xk, remap(kpos, G, continuous), theta)",
                           "kr_all = rope(xk, kpos, theta)"),
-    "query_not_remapped": ("qr_all = rope(xq[rows], remap(rows, G), theta)",
+    "query_not_remapped": ("qr_all = rope(xq[rows], remap(rows, G, continuous), theta)",
                            "qr_all = rope(xq[rows], rows, theta)"),
     "gqa_modulo": ("        g = h // r\n        for c0", "        g = h % Hkv\n        for c0"),
     "rotation_sign": ("[a * c - b * s, a * s + b * c]", "[a * c + b * s, -a * s + b * c]"),

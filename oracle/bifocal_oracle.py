@@ -48,7 +48,7 @@ import numpy as np
 
 __all__ = [
     "group_size", "remap", "rope_frequencies", "rope", "bifocal_scores",
-    "bifocal_attention", "bifocal_varlen", "decode_row", "ie_pass",
+    "bifocal_attention", "bifocal_varlen", "decode_row", "decode_batch", "ie_pass",
     "ie_merge", "tile_class", "tile_class_map",
 ]
 
@@ -284,6 +284,32 @@ def decode_row(xq_row, xk_cache, v_cache, pos: int, w0: int, w_pre: int, theta: 
         p = np.exp(s - m)
         o[h] = (p @ vv[:, g]) / p.sum()
         lse[h] = m + math.log(p.sum())
+    return o, lse
+
+
+def decode_batch(xq, k_rows, v_rows, positions, starts, w0: int, w_pre: int, theta: float,
+                 max_keys=None, scale=None, continuous: bool = False):
+    """One decode step for each of B independent sequences sharing a cache
+    buffer: sequence b's key k is row starts[b] + k of k_rows / v_rows (raw
+    keys and values, [rows, Hkv, d]); its query xq[b] sits at positions[b]
+    and takes G from its own L = positions[b] + 1 [Digest/Method, "Dynamic
+    group size": G follows the current length of each sequence].
+
+    An entry whose keys would fall outside the buffer (position < 0, start <
+    0, start + position >= rows) or at or past max_keys (when given) has no
+    defined result: its outputs are NaN. Returns (o [B, Hq, d], lse [B, Hq]).
+    """
+    xq = np.asarray(xq, dtype=np.float64)
+    B, Hq, d = xq.shape
+    rows = np.asarray(k_rows).shape[0]
+    o = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for b in range(B):
+        p, s0 = int(positions[b]), int(starts[b])
+        if p < 0 or s0 < 0 or s0 + p >= rows or (max_keys is not None and p >= max_keys):
+            continue
+        o[b], lse[b] = decode_row(xq[b], k_rows[s0:s0 + p + 1], v_rows[s0:s0 + p + 1], p, w0,
+                                  w_pre, theta, scale=scale, continuous=continuous)
     return o, lse
 
 

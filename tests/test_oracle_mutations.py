@@ -42,6 +42,9 @@ MUTATIONS = {
         "k_rem_pos, q_rem_pos = keys / float(G), pos // G"),
     "continuous_ie_floor": ("p_rot = pos / float(G) if continuous else pos // G",
                             "p_rot = pos // G"),
+    "batch_start_ignored": ("k_rows[s0:s0 + p + 1], v_rows[s0:s0 + p + 1]",
+                            "k_rows[:p + 1], v_rows[:p + 1]"),
+    "batch_bound_inclusive": ("s0 + p >= rows or", "s0 + p > rows or"),
 }
 
 
@@ -84,7 +87,8 @@ def _pin_calls():
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_mutation(name, monkeypatch):
     mod = _load_mutant(name, *MUTATIONS[name])
-    for attr in ("bifocal_attention", "bifocal_scores", "bifocal_varlen", "decode_row",
+    for attr in ("bifocal_attention", "bifocal_scores", "bifocal_varlen", "decode_batch",
+                 "decode_row",
                  "group_size", "ie_merge", "ie_pass", "remap", "rope", "rope_frequencies",
                  "tile_class", "tile_class_map"):
         monkeypatch.setattr(pins, attr, getattr(mod, attr))

@@ -13,8 +13,9 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (bifocal_attention, bifocal_scores, bifocal_varlen, decode_row, group_size,
-                    ie_merge, ie_pass, remap, rope, rope_frequencies, tile_class, tile_class_map)
+from oracle import (bifocal_attention, bifocal_scores, bifocal_varlen, decode_batch, decode_row,
+                    group_size, ie_merge, ie_pass, remap, rope, rope_frequencies, tile_class,
+                    tile_class_map)
 from tests._brute import brute_attention
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -485,3 +486,47 @@ def test_continuous_inclusion_exclusion_equals_masked(L, w0, w_pre):
     Od, Ld = bifocal_attention(xq, xk, v, w0, w_pre, theta, continuous=True)
     np.testing.assert_allclose(O, Od, atol=1e-10)
     np.testing.assert_allclose(LSE, Ld, atol=1e-10)
+
+
+# ---------------------------------------------------------------- batched decode
+def test_decode_batch_equals_varlen_prefill_last_rows():
+    """A batch of packed sequences (gaps between them, G = 1..5 with
+    w_pre = 8) decoded at their last positions equals the last row of each
+    sequence in a packed varlen prefill (an independent code path); two
+    entries share one cache region at different positions (a shared prefix)."""
+    Hq, Hkv, d, theta, w0, w_pre = 4, 2, 8, 1e4, 3, 8
+    lens = [1, 9, 17, 33, 40]
+    gaps = [2, 0, 5, 1, 3]
+    starts, rows = [], 0
+    for n, g in zip(lens, gaps):
+        rows += g
+        starts.append(rows)
+        rows += n
+    xk, v = _rand(60, rows, Hkv, d), _rand(61, rows, Hkv, d)
+    xq_rows = _rand(62, rows, Hq, d)
+    positions = [n - 1 for n in lens] + [20]
+    starts = starts + [starts[-1]]
+    xq = np.stack([xq_rows[s0 + p] for s0, p in zip(starts, positions)])
+    o, lse = decode_batch(xq, xk, v, positions, starts, w0, w_pre, theta)
+    for b, (s0, p) in enumerate(zip(starts, positions)):
+        n = p + 1
+        O, LSE = bifocal_attention(xq_rows[s0:s0 + n], xk[s0:s0 + n], v[s0:s0 + n], w0, w_pre,
+                                   theta, rows=[p])
+        np.testing.assert_allclose(o[b], O[0], atol=1e-13)
+        np.testing.assert_allclose(lse[b], LSE[:, 0], atol=1e-13)
+    assert [group_size(p + 1, w_pre) for p in positions] == [1, 2, 3, 5, 5, 3]
+
+
+def test_decode_batch_invalid_entries_are_nan():
+    """Entries whose keys leave the buffer or pass max_keys get NaN; the
+    others are unaffected."""
+    Hq, Hkv, d, theta = 2, 1, 8, 1e4
+    xk, v = _rand(63, 30, Hkv, d), _rand(64, 30, Hkv, d)
+    xq = _rand(65, 5, Hq, d)
+    positions, starts = [5, -1, 10, 25, 3], [0, 0, 20, 4, -2]
+    o, lse = decode_batch(xq, xk, v, positions, starts, 2, 4, theta, max_keys=20)
+    assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
+    assert np.isnan(o[4]).all() and np.isnan(lse[[1, 2, 3, 4]]).all()
+    ref, rl = decode_row(xq[0], xk, v, 5, 2, 4, theta)
+    np.testing.assert_allclose(o[0], ref, atol=1e-14)
+    np.testing.assert_allclose(lse[0], rl, atol=1e-14)

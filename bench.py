@@ -15,7 +15,8 @@ attention at the same shape (overhead ratio), the Eq. 7 inclusion-exclusion
 alternative, the 64K and packed-varlen workloads, prefill continued on the cache for the
 last 8192 rows, a window-size sweep, the continuous remote map x/G (prefill
 kernel and decode), decode latency at positions 32767 .. 131071 of a
-131072-key cache with L2 / MALL evicted before every step, calibrated HBM-read and MFMA ceilings, and the float64 CPU
+131072-key cache with L2 / MALL evicted before every step, a batch of 16
+sequences decoding in one launch, calibrated HBM-read and MFMA ceilings, and the float64 CPU
 oracle on a bounded sample of rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -78,7 +79,7 @@ def main():
     import torch
 
     import rope_context_extension_jl_amd as jl
-    from synth_inputs import WORKLOADS, make_qkv
+    from synth_inputs import WORKLOADS, make_decode_seq, make_qkv, packed_starts
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -343,7 +344,56 @@ def main():
                 f"({row['fused']['pct_hbm_peak']}% HBM, {row['fused']['pct_calibrated_read']}% "
                 f"of the calibrated read rate), plain {row['plain']['us_median']} us")
         result["decode"] = dec
-        del flush, wsd
+        del wsd
+
+        # ---------------------------------------------------- batched decode
+        cb = WORKLOADS["decode_batch_16"]
+        bpos = cb["positions"]
+        log(f"batched decode: {len(bpos)} sequences in one launch (L2/MALL evicted per step)")
+        bst, brows = packed_starts(bpos)
+        kb = torch.empty((brows, Hkv, d), dtype=torch.bfloat16, device=dev)
+        vb = torch.empty_like(kb)
+        xb = torch.empty((len(bpos), Hq, d), dtype=torch.bfloat16, device=dev)
+        for b, (p, s0) in enumerate(zip(bpos, bst)):
+            qn, kn, vn = make_decode_seq(cb["seed"], b, p + 1, Hq, Hkv, d, cb["std"], cb["dtype"])
+            xb[b] = up(qn)
+            kb[s0:s0 + p + 1] = up(kn)
+            vb[s0:s0 + p + 1] = up(vn)
+            jl.rope_apply(kb[s0:s0 + p + 1], cb["theta"])
+            del qn, kn, vn
+        pos_t = torch.tensor(bpos, dtype=torch.int32, device=dev)
+        st_t = torch.tensor(bst, dtype=torch.int32, device=dev)
+        mk = max(bpos) + 1
+        wsb = torch.empty(jl.decode_batch_workspace_size(len(bpos), mk, Hq, d), dtype=torch.uint8,
+                          device=dev)
+        ob = torch.empty_like(xb)
+        lb = torch.empty((len(bpos), Hq), dtype=torch.float32, device=dev)
+        bbytes = sum(4.0 * (p + 1) * Hkv * d for p in bpos)
+        brow = {"B": len(bpos), "keys": int(sum(p + 1 for p in bpos)), "max_keys": mk}
+        for mode in ("fused", "plain"):
+            ts = []
+            for it in range(args.decode_iters + 3):
+                flush.sum()
+                jl.bifocal_decode_batch(xb, kb, vb, pos_t, st_t, mk, cb["w0"], cb["w_pre"],
+                                        cb["theta"], mode=mode, out=ob, lse=lb, workspace=wsb,
+                                        events=de)
+                torch.cuda.synchronize()
+                if it >= 3:
+                    ts.append(de[0].elapsed_time(de[1]) * 1e3)
+            med = float(np.median(ts))
+            brow[mode] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
+                          "us_p90": round(pct(ts, 90), 2),
+                          "tokens_per_s": round(len(bpos) / (med * 1e-6), 1),
+                          "GBps": round(bbytes / (med * 1e-6) / 1e9, 1),
+                          "pct_hbm_peak": round(100 * bbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                                2),
+                          "pct_calibrated_read": round(100 * bbytes / (med * 1e-6) / 1e9 /
+                                                       read_gbs, 2)}
+        brow["overhead_ratio"] = round(brow["fused"]["us_median"] / brow["plain"]["us_median"], 4)
+        extras["decode_batch_16"] = brow
+        log(f"batched decode: {brow['fused']['us_median']} us per step "
+            f"({brow['fused']['pct_calibrated_read']}% of the calibrated read rate)")
+        del kb, vb, xb, wsb, ob, lb, flush
         torch.cuda.empty_cache()
 
         # ---------------------------------------------------- other workloads

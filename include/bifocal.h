@@ -228,6 +228,52 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
                             jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
                             void* stream, void* ev_begin, void* ev_end);
 
+/* Bytes of device workspace jl_bifocal_decode_batch needs for B sequences
+ * whose positions are all below max_keys (any num_splits it would choose or
+ * accept); 0 for arguments it would reject. */
+size_t jl_decode_batch_workspace_size(int B, int64_t max_keys, int Hq, int d);
+
+/* One generation step for each of B independent sequences in one launch
+ * (decode as in jl_bifocal_decode, per sequence: L = pos_b + 1 and its own
+ * G = max(1, ceil(L / w_pre)), "Dynamic group size" of the digest's Method;
+ * remote keys corrected by R_{f(k) - k}, "KV cache invariant"). The caches of
+ * the sequences share one buffer of cache_rows rows; sequence b's key k is
+ * row cache_starts[b] + k, so packed (varlen) and padded layouts both fit.
+ *   xq           [B, Hq, d]         RAW query of each sequence's new token
+ *   kcache       [cache_rows, Hkv, d] keys rotated at their absolute positions
+ *   vcache       [cache_rows, Hkv, d] values; neither cache is written
+ *   o            [B, Hq, d]; lse [B, Hq] float32 (natural log) or NULL
+ *   positions    device int32 [B]: pos_b, keys 0 .. pos_b are read
+ *   cache_starts device int32 [B]: first cache row of sequence b
+ *   max_keys     host bound with pos_b + 1 <= max_keys for every b: the split
+ *                plan and the workspace are sized for it
+ * The per-sequence values stay on the device (the step can be replayed with
+ * new positions without a host round trip). An entry with pos_b < 0,
+ * pos_b >= max_keys, cache_starts[b] < 0 or cache_starts[b] + pos_b >=
+ * cache_rows reads nothing and gets NaN in o (and lse); the other entries are
+ * unaffected. num_splits: splits of max_keys / num_splits keys each, 0 lets the
+ * library choose. Supported: bf16 or fp32, d = 128 or 64, Hq / Hkv in
+ * {1, 2, 4, 8}; mode FUSED or PLAIN, optionally with JL_REMAP_CONTINUOUS.
+ * Errors: JL_EINVAL (B < 0 or > 65535, max_keys < 1 or > 2^31 - 1,
+ * cache_rows < 1, bad heads or scalars, NULL pointers), JL_EUNSUPPORTED,
+ * JL_EWORKSPACE, JL_EHIP. B == 0 is a no-op. */
+int jl_bifocal_decode_batch(const void* xq, const void* kcache, const void* vcache, void* o,
+                            float* lse, const int32_t* positions, const int32_t* cache_starts,
+                            int B, int64_t max_keys, int64_t cache_rows, int Hq, int Hkv, int d,
+                            int64_t w0, int64_t w_pre, double theta, float scale, jl_dtype dt,
+                            jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* jl_bifocal_decode_batch plus timing: ev_begin / ev_end (caller-created
+ * hipEvent_t, or NULL) bracket the split and merge kernels on `stream`. */
+int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void* vcache, void* o,
+                                  float* lse, const int32_t* positions,
+                                  const int32_t* cache_starts, int B, int64_t max_keys,
+                                  int64_t cache_rows, int Hq, int Hkv, int d, int64_t w0,
+                                  int64_t w_pre, double theta, float scale, jl_dtype dt,
+                                  jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
+                                  void* stream, void* ev_begin, void* ev_end);
+
 /* Device-side tile classifier dump: out_dev[i * nk + j] (int8, device) gets
  * the class the prefill kernels compute for query tile i and key tile j of a
  * length-L sequence, nq = ceil(L / BM), nk = ceil(L / BN) with BM, BN from

@@ -18,6 +18,7 @@ __all__ = [
     "status_string", "rope_apply", "prefill_workspace_size", "bifocal_prefill",
     "decode_workspace_size", "bifocal_decode", "debug_tile_classes", "ie_ratio_view",
     "prefill_cached_workspace_size", "bifocal_prefill_cached",
+    "decode_batch_workspace_size", "bifocal_decode_batch",
     "calib_stream_read", "calib_mfma_bf16", "MODES", "REMAPS",
 ]
 
@@ -66,6 +67,14 @@ _SIGS = {
     "jl_bifocal_decode_timed": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int,
                                          _c_int, _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int,
                                          _c_int, _c_int, _c_p, _c_sz, _c_p, _c_p, _c_p]),
+    "jl_decode_batch_workspace_size": (_c_sz, [_c_int, _c_i64, _c_int, _c_int]),
+    "jl_bifocal_decode_batch": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_i64,
+                                         _c_i64, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_dbl,
+                                         _c_flt, _c_int, _c_int, _c_int, _c_p, _c_sz, _c_p]),
+    "jl_bifocal_decode_batch_timed": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int,
+                                               _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_i64,
+                                               _c_i64, _c_dbl, _c_flt, _c_int, _c_int, _c_int,
+                                               _c_p, _c_sz, _c_p, _c_p, _c_p]),
     "jl_debug_tile_classes": (_c_int, [_c_i64, _c_i64, _c_p, _c_p]),
     "jl_calib_stream_read": (_c_int, [_c_p, _c_sz, _c_p, _c_int, _c_p]),
     "jl_calib_mfma_bf16": (_c_int, [_c_p, _c_int, _c_int, _c_p]),
@@ -284,6 +293,43 @@ def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
         _dev(workspace, "workspace"),
         workspace.numel(), _stream(xq.device), *_events(events))
     _check("jl_bifocal_decode", st)
+    return out, lse
+
+
+def decode_batch_workspace_size(B, max_keys, Hq, d) -> int:
+    return int(lib().jl_decode_batch_workspace_size(int(B), int(max_keys), int(Hq), int(d)))
+
+
+def bifocal_decode_batch(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                         positions: torch.Tensor, cache_starts: torch.Tensor, max_keys: int,
+                         w0: int, w_pre: int, theta: float, scale: float = 0.0,
+                         mode: str = "fused", num_splits: int = 0,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                         events=None, remap: str = "floor"):
+    """One decode step for B sequences: RAW queries xq [B, Hq, d]; sequence b's
+    keys 0 .. positions[b] are rows cache_starts[b] + k of the shared cache
+    [rows, Hkv, d]. positions / cache_starts: device int32 [B]; max_keys: a
+    host bound on positions[b] + 1. Returns (o [B, Hq, d], lse [B, Hq])."""
+    B, Hq, d = xq.shape
+    C, Hkv, _ = kcache.shape
+    for t, name in ((positions, "positions"), (cache_starts, "cache_starts")):
+        if t.dtype != torch.int32 or t.numel() != B or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor of {B} entries")
+    if out is None:
+        out = torch.empty_like(xq)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=xq.device)
+    if workspace is None:
+        workspace = torch.empty(max(decode_batch_workspace_size(B, max_keys, Hq, d), 1),
+                                dtype=torch.uint8, device=xq.device)
+    st = lib().jl_bifocal_decode_batch_timed(
+        _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
+        _dev(lse, "lse"), _dev(positions, "positions"), _dev(cache_starts, "cache_starts"), B,
+        int(max_keys), C, Hq, Hkv, d, int(w0), int(w_pre), float(theta), float(scale),
+        _dtype_code(xq), _mode_code(mode, remap), int(num_splits), _dev(workspace, "workspace"),
+        workspace.numel(), _stream(xq.device), *_events(events))
+    _check("jl_bifocal_decode_batch", st)
     return out, lse
 
 

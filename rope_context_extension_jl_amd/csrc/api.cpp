@@ -276,6 +276,20 @@ int jl_bifocal_prefill_cached(const void* xq, const void* kcache, const void* vc
                                          stream, nullptr, nullptr);
 }
 
+// bf16 single decode: one wave per split, four KV heads per workgroup, two
+// workgroups fit a CU: pick the split count so the workgroups cover the 256
+// CUs evenly (two per CU when each split gets >= 256 keys, else one), since a
+// few CUs holding an extra workgroup would set the kernel's time
+static int decode_bf16_splits(int64_t keys, int Hkv) {
+  const int64_t hg = (Hkv + 3) / 4;
+  const int64_t s_full = 512 / hg > 0 ? 512 / hg : 1, s_half = 256 / hg > 0 ? 256 / hg : 1;
+  int64_t want;
+  if (keys >= 256 * s_full) want = s_full;
+  else if (keys >= 128 * s_half) want = s_half;
+  else want = (keys + 127) / 128;
+  return (int)want;
+}
+
 static int decode_max_splits(int64_t capacity) {
   int64_t s = (capacity + 63) / 64;
   return (int)(s < 1024 ? s : 1024);
@@ -310,17 +324,7 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
   int S = num_splits;
   if (S == 0) {
     if (dt == JL_BF16) {
-      // one wave per split, four KV heads per workgroup, two workgroups fit a
-      // CU: pick the split count so the workgroups cover the 256 CUs evenly
-      // (two per CU when each split gets >= 256 keys, else one), since a few
-      // CUs holding an extra workgroup would set the kernel's time
-      const int64_t hg = (Hkv + 3) / 4;
-      const int64_t s_full = 512 / hg > 0 ? 512 / hg : 1, s_half = 256 / hg > 0 ? 256 / hg : 1;
-      int64_t want;
-      if (keys >= 256 * s_full) want = s_full;
-      else if (keys >= 128 * s_half) want = s_half;
-      else want = (keys + 127) / 128;
-      S = (int)want;
+      S = decode_bf16_splits(keys, Hkv);
     } else {
       // float32: one workgroup per split, ~4 per CU, at least 64 keys
       int64_t want = (1024 + Hkv - 1) / Hkv;
@@ -348,6 +352,99 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
                     cont, dt == JL_FP32, S, workspace, st);
   if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
   return hip_status(e);
+}
+
+// ---- batched decode
+// fp32: one workgroup per (split, KV head, sequence), ~4 per CU in all
+static int decode_batch_f32_splits(int B, int64_t max_keys, int Hkv) {
+  const int64_t units = (int64_t)B * Hkv;
+  const int64_t by_wg = 1024 / units > 0 ? 1024 / units : 1;
+  const int64_t by_keys = (max_keys + 63) / 64;
+  const int64_t want = by_wg < by_keys ? by_wg : by_keys;
+  return want < 1 ? 1 : (int)want;
+}
+
+// Partials [B, Hq, S, d + 2] fp32, then the bf16 work list int32 [B + 1].
+static size_t decode_batch_list_offset(int B, int Hq, int S, int d) {
+  return align256((size_t)B * Hq * S * (d + 2) * sizeof(float));
+}
+
+size_t jl_decode_batch_workspace_size(int B, int64_t max_keys, int Hq, int d) {
+  if (B < 1 || max_keys < 1 || max_keys > (int64_t)INT32_MAX || Hq < 1 || d < 2) return 0;
+  return decode_batch_list_offset(B, Hq, decode_max_splits(max_keys), d) +
+         align256((size_t)(B + 1) * sizeof(int));
+}
+
+int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void* vcache, void* o,
+                                  float* lse, const int32_t* positions,
+                                  const int32_t* cache_starts, int B, int64_t max_keys,
+                                  int64_t cache_rows, int Hq, int Hkv, int d, int64_t w0,
+                                  int64_t w_pre, double theta, float scale, jl_dtype dt,
+                                  jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
+                                  void* stream, void* ev_begin, void* ev_end) {
+  int cont;
+  mode = strip_remap(mode, &cont);
+  if (B < 0 || B > 65535 || max_keys < 1 || max_keys > (int64_t)INT32_MAX || cache_rows < 1)
+    return JL_EINVAL;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 0 || w_pre < 1 || !(theta > 1.0)) return JL_EINVAL;
+  if (num_splits < 0 || !(scale == scale)) return JL_EINVAL;
+  if (dt != JL_BF16 && dt != JL_FP32) return JL_EINVAL;
+  if (mode == JL_MODE_IE) return JL_EUNSUPPORTED;
+  if (mode != JL_MODE_FUSED && mode != JL_MODE_PLAIN) return JL_EINVAL;
+  if (d != 128 && d != 64) return JL_EUNSUPPORTED;
+  {
+    const int r = Hq / Hkv;
+    if (r != 1 && r != 2 && r != 4 && r != 8) return JL_EUNSUPPORTED;
+  }
+  if (B == 0) return JL_OK;
+  if (!xq || !kcache || !vcache || !o || !positions || !cache_starts) return JL_EINVAL;
+  const int maxs = decode_max_splits(max_keys);
+  // bf16: the splits of the longest sequence are sized as a single decode of
+  // it would size them; every sequence is cut into splits of that many keys
+  // and a fixed grid walks the resulting work list. fp32: one grid over all
+  // (split, head, sequence) triples.
+  int S = num_splits;
+  if (S == 0) {
+    S = dt == JL_BF16 ? decode_bf16_splits(max_keys, Hkv) : decode_batch_f32_splits(B, max_keys, Hkv);
+    if (S > maxs) S = maxs;
+  }
+  if (S > maxs) return JL_EINVAL;
+  if ((int64_t)S > max_keys) S = (int)max_keys;
+  const int kps = (int)((max_keys + S - 1) / S);
+  S = (int)((max_keys + kps - 1) / kps);  // no split past max_keys
+  const size_t list_off = decode_batch_list_offset(B, Hq, S, d);
+  const size_t need = list_off + (size_t)(B + 1) * sizeof(int);
+  if (!workspace || ws_bytes < need) return JL_EWORKSPACE;
+  const int64_t hg = (Hkv + 3) / 4;
+  const int64_t units = (int64_t)B * S * hg;  // upper bound of the work list
+  const int grid_wg = (int)(units < 512 ? units : 512);  // two workgroups per CU
+  if (((uintptr_t)workspace) & 15) return JL_EINVAL;
+  const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d));
+  RopeFreqs fr;
+  make_freqs(fr, d, theta);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (ev_begin && (e = hipEventRecord((hipEvent_t)ev_begin, st)) != hipSuccess)
+    return hip_status(e);
+  e = launch_decode_batch(xq, kcache, vcache, o, lse, positions, cache_starts, B, max_keys,
+                          cache_rows, Hq, Hkv, d, w0 > (int64_t)INT32_MAX ? INT32_MAX : w0,
+                          w_pre > (int64_t)INT32_MAX ? (int64_t)INT32_MAX : w_pre, sc, fr,
+                          mode == JL_MODE_PLAIN, cont, dt == JL_FP32, S, kps, workspace,
+                          (int*)((char*)workspace + list_off), grid_wg, st);
+  if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
+  return hip_status(e);
+}
+
+int jl_bifocal_decode_batch(const void* xq, const void* kcache, const void* vcache, void* o,
+                            float* lse, const int32_t* positions, const int32_t* cache_starts,
+                            int B, int64_t max_keys, int64_t cache_rows, int Hq, int Hkv, int d,
+                            int64_t w0, int64_t w_pre, double theta, float scale, jl_dtype dt,
+                            jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  return jl_bifocal_decode_batch_timed(xq, kcache, vcache, o, lse, positions, cache_starts, B,
+                                       max_keys, cache_rows, Hq, Hkv, d, w0, w_pre, theta, scale,
+                                       dt, mode, num_splits, workspace, ws_bytes, stream, nullptr,
+                                       nullptr);
 }
 
 int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, void* o, float* lse,

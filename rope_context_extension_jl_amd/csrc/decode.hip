@@ -35,7 +35,54 @@ struct DecArgs {
   double fk_rel;   // with cont: f(k) - k = k * fk_rel, fk_rel = 1 / G - 1
   float scale_log2;
   RopeFreqs fr;
+  // batched decode: per-sequence position and first cache row (device), the
+  // bound on pos + 1 the split plan was made for, the cache's row count and
+  // w_pre (each sequence takes G from its own L = pos + 1)
+  const int* bpos;
+  const int* bstart;
+  int max_keys;
+  int64_t cap_rows;
+  int64_t w_pre;
 };
+
+// One sequence's view of the arguments: a single decode takes it from the
+// scalars; a batched one from the per-sequence arrays, b being the grid's
+// batch index. ok is false for a batch entry whose position or cache rows
+// fall outside the bounds the caller gave: the kernels skip it and the merge
+// writes NaN for it, so no read goes out of bounds.
+struct DecSeq {
+  int pos, G;
+  double fk_rel;
+  bool ok;
+  const char* xq;  // this sequence's query rows [Hq, D]
+  const char* kc;  // its cache row 0 [.., Hkv, D]
+  const char* vc;
+  float* part;     // its partials [Hq, S, D + 2]
+};
+
+template <bool BATCH>
+__device__ __forceinline__ DecSeq dec_seq(const DecArgs& a, int b, int D, int esz) {
+  DecSeq q;
+  int64_t row0 = 0;
+  if constexpr (BATCH) {
+    const int p = a.bpos[b], st = a.bstart[b];
+    q.ok = p >= 0 && p < a.max_keys && st >= 0 && (int64_t)st + p < a.cap_rows;
+    q.pos = q.ok ? p : 0;
+    q.G = (int)(((int64_t)q.pos + a.w_pre) / a.w_pre);  // Eq. 2 with L = pos + 1
+    q.fk_rel = 1.0 / (double)q.G - 1.0;
+    row0 = q.ok ? st : 0;
+  } else {
+    q.pos = a.pos;
+    q.G = a.G;
+    q.fk_rel = a.fk_rel;
+    q.ok = true;
+  }
+  q.xq = (const char*)a.xq + (int64_t)b * a.Hq * D * esz;
+  q.kc = (const char*)a.kc + row0 * a.Hkv * D * esz;
+  q.vc = (const char*)a.vc + row0 * a.Hkv * D * esz;
+  q.part = a.part + (int64_t)b * a.Hq * a.S * (D + 2);
+  return q;
+}
 
 template <bool F32>
 __device__ inline void load4(const void* base, int64_t idx, float* out) {
@@ -57,7 +104,7 @@ __device__ inline float load1(const void* base, int64_t idx) {
   else return bf16_bits_to_f32(((const uint16_t*)base)[idx]);
 }
 
-template <bool F32, int D, int R>
+template <bool F32, int D, int R, bool BATCH>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
   constexpr int NL = D / 8;     // lanes per key
   constexpr int KPW = 64 / NL;  // keys per wave step
@@ -66,17 +113,20 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
   __shared__ float red_m[4][R], red_l[4][R];
   __shared__ float red_acc[4][R][D];
   const int s = blockIdx.x, g = blockIdx.y;
+  const DecSeq sq = dec_seq<BATCH>(a, blockIdx.z, D, F32 ? 4 : 2);
+  // workgroup-uniform exits, before any barrier
+  if (!sq.ok || s * a.kps > sq.pos) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int dl = lane % NL, kl = lane / NL;
   const int h0 = g * R;
-  const double fpos = remap_pos(a.pos, a.G, a.cont);
+  const double fpos = remap_pos(sq.pos, sq.G, a.cont);
   // rotated queries for the R heads of this KV group
   for (int idx = tid; idx < R * HALF; idx += 256) {
     const int hl = idx / HALF, i = idx % HALF;
-    const float x0 = load1<F32>(a.xq, (int64_t)(h0 + hl) * D + i);
-    const float x1 = load1<F32>(a.xq, (int64_t)(h0 + hl) * D + HALF + i);
+    const float x0 = load1<F32>(sq.xq, (int64_t)(h0 + hl) * D + i);
+    const float x1 = load1<F32>(sq.xq, (int64_t)(h0 + hl) * D + HALF + i);
     float c, sn;
-    rope_cs((double)a.pos, a.fr.w(i), c, sn);
+    rope_cs((double)sq.pos, a.fr.w(i), c, sn);
     qa_s[hl][i] = x0 * c - x1 * sn;
     qa_s[hl][HALF + i] = x0 * sn + x1 * c;
     rope_cs(fpos, a.fr.w(i), c, sn);
@@ -106,22 +156,22 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) wl[e] = F32 ? a.fr.w(4 * dl + e) : a.fr.w(4 * dl + e) * kInvTwoPi;
   const int k_lo = s * a.kps;
-  const int k_hi = min(k_lo + a.kps, a.pos + 1);
+  const int k_hi = min(k_lo + a.kps, sq.pos + 1);
   for (int kb = k_lo + wave * KPW; kb < k_hi; kb += 4 * KPW) {
     const int kk = kb + kl;
     const bool valid = kk < k_hi;
     float k0[4] = {0, 0, 0, 0}, k1[4] = {0, 0, 0, 0}, v0[4] = {0, 0, 0, 0}, v1[4] = {0, 0, 0, 0};
     if (valid) {
       const int64_t row = ((int64_t)kk * a.Hkv + g) * D;
-      load4<F32>(a.kc, row + 4 * dl, k0);
-      load4<F32>(a.kc, row + HALF + 4 * dl, k1);
-      load4<F32>(a.vc, row + 4 * dl, v0);
-      load4<F32>(a.vc, row + HALF + 4 * dl, v1);
+      load4<F32>(sq.kc, row + 4 * dl, k0);
+      load4<F32>(sq.kc, row + HALF + 4 * dl, k1);
+      load4<F32>(sq.vc, row + 4 * dl, v0);
+      load4<F32>(sq.vc, row + HALF + 4 * dl, v1);
     }
-    const bool remote = !a.plain && (a.pos - kk > a.w0);
-    if (remote && a.G > 1) {
+    const bool remote = !a.plain && (sq.pos - kk > a.w0);
+    if (remote && sq.G > 1) {
       // f(k) - k
-      const double delta = a.cont ? (double)kk * a.fk_rel : (double)(kk / a.G - kk);
+      const double delta = a.cont ? (double)kk * sq.fk_rel : (double)(kk / sq.G - kk);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float c, sn;
@@ -198,7 +248,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
       lt += red_l[w][h] * sc;
       at += red_acc[w][h][dd] * sc;
     }
-    float* pp = a.part + ((int64_t)(h0 + h) * a.S + s) * (D + 2);
+    float* pp = sq.part + ((int64_t)(h0 + h) * a.S + s) * (D + 2);
     pp[2 + dd] = at;
     if (dd == 0) {
       pp[0] = mm;
@@ -467,32 +517,20 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
   }
 }
 
+// One work unit of the bf16 decode for one wave: keys [s kps, (s + 1) kps)
+// of KV head kvh of sequence sq, leaving the partial of each query head of
+// the group. vA / vB: this wave's two V stages.
 template <int D>
-__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
+__device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int s, int kvh,
+                                         const double* w2pi_s, uint8_t* sA, uint8_t* sB) {
   using G = DecGeom<D>;
-  constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
-  // two V stages per wave, as separate arrays so that reads of one are known
-  // not to alias the transfers in flight into the other
-  __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
-  __shared__ double w2pi_s[D / 2];
-  // the wave index is uniform per wave: say so, so that every split-derived
-  // value (key range, route of a key block) lives in scalar registers and the
-  // route branches are scalar jumps; matrix instructions then never run under
-  // a partial or empty EXEC mask
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  constexpr int NDS = G::NDS, NDB = G::NDB;
+  const int lane = threadIdx.x & 63;
   const int g16 = lane >> 4, r16 = lane & 15;
-  if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
-  __syncthreads();
-  // workgroup = one split of four KV heads (wave w: head 4 hg + w), so the
-  // waves running together read neighbouring head slices of the same key rows
-  const int hgroups = (a.Hkv + 3) >> 2;
-  const int s = blockIdx.x / hgroups, kvh = (blockIdx.x % hgroups) * 4 + wave;
-  if (kvh >= a.Hkv) return;
   const int R = a.Hq / a.Hkv, h0 = kvh * R;
-  const uint16_t* xq = (const uint16_t*)a.xq;
-  const uint16_t* kc = (const uint16_t*)a.kc;
-  const uint16_t* vc = (const uint16_t*)a.vc;
+  const uint16_t* xq = (const uint16_t*)sq.xq;
+  const uint16_t* kc = (const uint16_t*)sq.kc;
+  const uint16_t* vc = (const uint16_t*)sq.vc;
 
   // query operands (B of S^T = K Q^T): lane holds dims 32 ds + 8 g16 + j of
   // query head r16, rotated at pos (qa) and at f(pos) (qr), times scale*log2 e
@@ -500,7 +538,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   {
     const bool qv = r16 < R;
     const uint16_t* qp = xq + (int64_t)(h0 + (qv ? r16 : 0)) * D;
-    const double fpos = remap_pos(a.pos, a.G, a.cont);
+    const double fpos = remap_pos(sq.pos, sq.G, a.cont);
 #pragma unroll
     for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
@@ -509,7 +547,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
         const float x0 = qv ? bf16_bits_to_f32(qp[i]) : 0.f;
         const float x1 = qv ? bf16_bits_to_f32(qp[i + D / 2]) : 0.f;
         float c, sn;
-        rope_cs_turns((double)a.pos, w2pi_s[i], c, sn);
+        rope_cs_turns((double)sq.pos, w2pi_s[i], c, sn);
         qa[ds][j] = (_Float16)((x0 * c - x1 * sn) * a.scale_log2);
         qa[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * c) * a.scale_log2);
         rope_cs_turns(fpos, w2pi_s[i], c, sn);
@@ -519,17 +557,17 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   }
   const int k_lo = s * a.kps;
   DecCtx c;
-  c.k_hi = min(k_lo + a.kps, a.pos + 1);
+  c.k_hi = min(k_lo + a.kps, sq.pos + 1);
   c.rstride = (int64_t)a.Hkv * D;
   c.kbase = kc + (int64_t)kvh * D + 8 * g16;
   c.vbase = vc + (int64_t)kvh * D;
-  c.pos = a.pos;
+  c.pos = sq.pos;
   c.w0 = a.w0;
-  c.G = a.G;
+  c.G = sq.G;
   c.cont = a.cont;
-  c.fk_rel = a.fk_rel;
+  c.fk_rel = sq.fk_rel;
   c.plain = a.plain;
-  c.correct = !a.plain && a.G > 1;
+  c.correct = !a.plain && sq.G > 1;
   c.lane = lane;
   c.g16 = g16;
   c.r16 = r16;
@@ -546,8 +584,6 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   // clamped to the split, so past the end it re-reads the last key (from L2)
   // and the loads need no branch.
   DecBuf<D> bA, bB;
-  uint8_t* sA = vstA[wave];
-  uint8_t* sB = vstB[wave];
   int k0 = k_lo;
   dec_issue_k<D>(c, k0, bA);
   dec_issue_v<D>(c, k0, sA);
@@ -564,14 +600,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
     if (k0 + 2 * DEC_CHUNK >= c.k_hi) break;
     k0 += 2 * DEC_CHUNK;
   }
-  // no transfer into this workgroup's LDS may outlive it
+  // no transfer into these LDS stages may outlive the unit
   __builtin_amdgcn_s_waitcnt(0);
   const float m = st.m, lsum = st.lsum;
   df32x4 (&acc)[NDB] = st.acc;
   // ---- split partial: m (log2 domain), l, unnormalised O for each query head
   float lt = lsum + __shfl_xor(lsum, 16);
   lt += __shfl_xor(lt, 32);
-  float* part = a.part;
+  float* part = sq.part;
   if (g16 == 0 && r16 < R) {
     float* pp = part + ((int64_t)(h0 + r16) * a.S + s) * (D + 2);
     pp[0] = m;
@@ -588,20 +624,120 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   }
 }
 
+// Single sequence: workgroup = one split of four KV heads (wave w: head
+// 4 hg + w), so the waves running together read neighbouring head slices of
+// the same key rows.
+template <int D>
+__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
+  using G = DecGeom<D>;
+  // two V stages per wave, as separate arrays so that reads of one are known
+  // not to alias the transfers in flight into the other
+  __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
+  __shared__ double w2pi_s[D / 2];
+  // the wave index is uniform per wave: say so, so that every split-derived
+  // value (key range, route of a key block) lives in scalar registers and the
+  // route branches are scalar jumps; matrix instructions then never run under
+  // a partial or empty EXEC mask
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
+  __syncthreads();
+  const int hgroups = (a.Hkv + 3) >> 2;
+  const int s = blockIdx.x / hgroups, kvh = (blockIdx.x % hgroups) * 4 + wave;
+  if (kvh >= a.Hkv) return;
+  const DecSeq sq = dec_seq<false>(a, 0, D, 2);
+  dec_unit<D>(a, sq, s, kvh, w2pi_s, vstA[wave], vstB[wave]);
+}
+
+// Batch: a fixed grid of workgroups walks the work list the plan kernel
+// built (unit u = (entry of the list, KV-head group); the list holds the
+// splits s * kps <= pos_b of every valid sequence b, base[b] .. base[b+1] -
+// 1), round robin, so the work spreads evenly over the CUs whatever the mix
+// of sequence lengths.
+template <int D>
+__global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, const int* base,
+                                                                   int B) {
+  using G = DecGeom<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
+  __shared__ double w2pi_s[D / 2];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
+  __syncthreads();
+  const int hgroups = (a.Hkv + 3) >> 2;
+  const int units = base[B] * hgroups;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int item = u / hgroups, kvh = (u % hgroups) * 4 + wave;
+    if (kvh >= a.Hkv) continue;
+    int lo = 0, hi = B - 1;  // the sequence b with base[b] <= item < base[b + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (base[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const DecSeq sq = dec_seq<true>(a, lo, D, 2);
+    dec_unit<D>(a, sq, item - base[lo], kvh, w2pi_s, vstA[wave], vstB[wave]);
+  }
+}
+
+// Splits of batch entry b that hold keys (s * kps <= pos), 0 for an entry
+// the kernels skip.
+__device__ __forceinline__ int dec_batch_nsplit(const DecArgs& a, int b) {
+  const DecSeq sq = dec_seq<true>(a, b, 0, 0);
+  return sq.ok ? (sq.pos + a.kps) / a.kps : 0;
+}
+
+// Work list of a batched decode: base[b] = number of splits of the entries
+// before b; base[B] = their total. One workgroup.
+__global__ void __launch_bounds__(1024) decode_batch_plan_kernel(DecArgs a, int* base, int B) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (B + 1023) / 1024;
+  const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += dec_batch_nsplit(a, b);
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid ? part[tid - 1] : 0;
+  for (int b = b0; b < b1; ++b) {
+    base[b] = run;
+    run += dec_batch_nsplit(a, b);
+  }
+  if (tid == 1023) base[B] = part[1023];
+}
+
 // Merge of the split partials of one query head with LSE weights, one pass:
 // workgroup (head h, 16 output dims), thread (split group g of 16, dim):
 // each thread folds its splits s = g, g + 16, ... with a running maximum
 // (all loads independent of the arithmetic, so they are in flight together),
 // then the 16 groups are combined through LDS.
-template <bool F32, int D>
+template <bool F32, int D, bool BATCH>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
   __shared__ float rm[256], rl[256], ra[256];
   const int h = blockIdx.x, d0 = 16 * blockIdx.y, tid = threadIdx.x;
   const int dd = tid & 15, grp = tid >> 4;
-  const float* pp = a.part + (int64_t)h * a.S * (D + 2);
+  const int b = blockIdx.z;
+  const DecSeq sq = dec_seq<BATCH>(a, b, D, F32 ? 4 : 2);
+  const int64_t orow = (int64_t)b * a.Hq + h;  // output row of (sequence, head)
+  if (!sq.ok) {  // a skipped batch entry: NaN marks it (uniform exit)
+    if (grp == 0) {
+      if constexpr (F32) ((float*)a.o)[orow * D + d0 + dd] = __builtin_nanf("");
+      else ((uint16_t*)a.o)[orow * D + d0 + dd] = 0x7fc0;
+      if (a.lse && d0 + dd == 0) a.lse[orow] = __builtin_nanf("");
+    }
+    return;
+  }
+  // splits that hold keys of this sequence: s * kps <= pos
+  const int S = BATCH ? (sq.pos + a.kps) / a.kps : a.S;
+  const float* pp = sq.part + (int64_t)h * a.S * (D + 2);
   float M = -INFINITY, L = 0.f, A = 0.f;
 #pragma unroll 4
-  for (int s = grp; s < a.S; s += 16) {
+  for (int s = grp; s < S; s += 16) {
     const float* q = pp + (int64_t)s * (D + 2);
     const float ms = q[0], ls = q[1], as = q[2 + d0 + dd];
     if (ms > M) {  // -inf partials (no keys) never pass
@@ -631,32 +767,50 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
       At += w * ra[16 * g + dd];
     }
     const float out = At / Lt;
-    if constexpr (F32) ((float*)a.o)[(int64_t)h * D + d0 + dd] = out;
-    else ((uint16_t*)a.o)[(int64_t)h * D + d0 + dd] = f32_to_bf16_bits(out);
-    if (a.lse && d0 + dd == 0) a.lse[h] = (Mt + __log2f(Lt)) * 0.69314718055994530942f;
+    if constexpr (F32) ((float*)a.o)[orow * D + d0 + dd] = out;
+    else ((uint16_t*)a.o)[orow * D + d0 + dd] = f32_to_bf16_bits(out);
+    if (a.lse && d0 + dd == 0) a.lse[orow] = (Mt + __log2f(Lt)) * 0.69314718055994530942f;
   }
 }
 
-template <bool F32, int D>
-static void launch_decode_t(int R, dim3 grid, hipStream_t st, const DecArgs& a) {
+template <bool F32, int D, bool BATCH>
+static void launch_decode_t(int R, int B, int* base, int grid_wg, hipStream_t st,
+                            const DecArgs& a) {
   if constexpr (F32) {
+    const dim3 grid(a.S, a.Hkv, B);
     switch (R) {
-      case 1: hipLaunchKernelGGL((decode_split_kernel<F32, D, 1>), grid, dim3(256), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((decode_split_kernel<F32, D, 2>), grid, dim3(256), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((decode_split_kernel<F32, D, 4>), grid, dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL((decode_split_kernel<F32, D, 8>), grid, dim3(256), 0, st, a); break;
+      case 1: hipLaunchKernelGGL((decode_split_kernel<F32, D, 1, BATCH>), grid, dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((decode_split_kernel<F32, D, 2, BATCH>), grid, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((decode_split_kernel<F32, D, 4, BATCH>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((decode_split_kernel<F32, D, 8, BATCH>), grid, dim3(256), 0, st, a); break;
     }
+  } else if constexpr (BATCH) {
+    hipLaunchKernelGGL(decode_batch_plan_kernel, dim3(1), dim3(1024), 0, st, a, base, B);
+    hipLaunchKernelGGL((decode_mfma_batch_kernel<D>), dim3(grid_wg), dim3(256), 0, st, a,
+                       (const int*)base, B);
   } else {
-    const dim3 g2(a.S * ((a.Hkv + 3) / 4));
-    hipLaunchKernelGGL((decode_mfma_kernel<D>), g2, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D>), dim3(a.S * ((a.Hkv + 3) / 4)), dim3(256), 0, st,
+                       a);
   }
-  hipLaunchKernelGGL((decode_merge_kernel<F32, D>), dim3(a.Hq, D / 16), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<F32, D, BATCH>), dim3(a.Hq, D / 16, B), dim3(256), 0, st,
+                     a);
 }
 
-hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
-                         int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
-                         const RopeFreqs& fr, int plain, int cont, int is_f32, int num_splits,
-                         void* ws, hipStream_t st) {
+template <bool BATCH>
+static void launch_decode_any(int is_f32, int d, int R, int B, int* base, int grid_wg,
+                              hipStream_t st, const DecArgs& a) {
+  if (is_f32) {
+    if (d == 64) launch_decode_t<true, 64, BATCH>(R, B, base, grid_wg, st, a);
+    else launch_decode_t<true, 128, BATCH>(R, B, base, grid_wg, st, a);
+  } else {
+    if (d == 64) launch_decode_t<false, 64, BATCH>(R, B, base, grid_wg, st, a);
+    else launch_decode_t<false, 128, BATCH>(R, B, base, grid_wg, st, a);
+  }
+}
+
+static DecArgs decode_args(const void* xq, const void* kc, const void* vc, void* o, float* lse,
+                           int Hq, int Hkv, int64_t w0, float scale, const RopeFreqs& fr,
+                           int plain, int cont, void* ws) {
   DecArgs a;
   a.xq = xq;
   a.kc = kc;
@@ -664,29 +818,55 @@ hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o
   a.part = (float*)ws;
   a.o = o;
   a.lse = lse;
-  a.pos = (int)pos;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.w0 = (int)w0;
-  a.G = (int)G;
   a.plain = plain;
   a.cont = cont;
-  a.fk_rel = 1.0 / (double)G - 1.0;
-  const int keys = (int)pos + 1;
-  int kps = (keys + num_splits - 1) / num_splits;
-  a.S = (keys + kps - 1) / kps;  // no empty split
-  a.kps = kps;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.fr = fr;
-  const int R = Hq / Hkv;
-  const dim3 grid(a.S, Hkv);
-  if (is_f32) {
-    if (d == 64) launch_decode_t<true, 64>(R, grid, st, a);
-    else launch_decode_t<true, 128>(R, grid, st, a);
-  } else {
-    if (d == 64) launch_decode_t<false, 64>(R, grid, st, a);
-    else launch_decode_t<false, 128>(R, grid, st, a);
-  }
+  a.pos = 0;
+  a.G = 1;
+  a.fk_rel = 0.0;
+  a.bpos = nullptr;
+  a.bstart = nullptr;
+  a.max_keys = 0;
+  a.cap_rows = 0;
+  a.w_pre = 1;
+  return a;
+}
+
+hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
+                         int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
+                         const RopeFreqs& fr, int plain, int cont, int is_f32, int num_splits,
+                         void* ws, hipStream_t st) {
+  DecArgs a = decode_args(xq, kc, vc, o, lse, Hq, Hkv, w0, scale, fr, plain, cont, ws);
+  a.pos = (int)pos;
+  a.G = (int)G;
+  a.fk_rel = 1.0 / (double)G - 1.0;
+  const int keys = (int)pos + 1;
+  const int kps = (keys + num_splits - 1) / num_splits;
+  a.S = (keys + kps - 1) / kps;  // no empty split
+  a.kps = kps;
+  launch_decode_any<false>(is_f32, d, Hq / Hkv, 1, nullptr, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_batch(const void* xq, const void* kc, const void* vc, void* o, float* lse,
+                               const int32_t* positions, const int32_t* starts, int B,
+                               int64_t max_keys, int64_t cap_rows, int Hq, int Hkv, int d,
+                               int64_t w0, int64_t w_pre, float scale, const RopeFreqs& fr,
+                               int plain, int cont, int is_f32, int splits, int kps, void* ws,
+                               int* base, int grid_wg, hipStream_t st) {
+  DecArgs a = decode_args(xq, kc, vc, o, lse, Hq, Hkv, w0, scale, fr, plain, cont, ws);
+  a.bpos = positions;
+  a.bstart = starts;
+  a.max_keys = (int)max_keys;
+  a.cap_rows = cap_rows;
+  a.w_pre = w_pre;
+  a.S = splits;
+  a.kps = kps;
+  launch_decode_any<true>(is_f32, d, Hq / Hkv, B, base, grid_wg, st, a);
   return hipGetLastError();
 }
 

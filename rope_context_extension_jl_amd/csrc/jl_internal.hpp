@@ -108,6 +108,18 @@ hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o
                          const RopeFreqs& fr, int plain, int cont, int is_f32, int num_splits,
                          void* ws, hipStream_t st);
 
+// Batched decode: sequence b's query is row b of xq [B, Hq, d], its keys
+// 0 .. positions[b] sit at cache rows starts[b] + k; `splits` splits of `kps`
+// keys each cover max_keys keys (the partials, at ws, are
+// [B, Hq, splits, d + 2]). bf16: base (int32 [B + 1], device) receives the
+// work list and grid_wg workgroups walk it.
+hipError_t launch_decode_batch(const void* xq, const void* kc, const void* vc, void* o, float* lse,
+                               const int32_t* positions, const int32_t* starts, int B,
+                               int64_t max_keys, int64_t cap_rows, int Hq, int Hkv, int d,
+                               int64_t w0, int64_t w_pre, float scale, const RopeFreqs& fr,
+                               int plain, int cont, int is_f32, int splits, int kps, void* ws,
+                               int* base, int grid_wg, hipStream_t st);
+
 hipError_t launch_tile_dump(int64_t L, int64_t w0, int8_t* out, hipStream_t st);
 
 hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, int blocks,

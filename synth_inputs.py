@@ -8,7 +8,10 @@ path receive what these functions return.
 Recipe: numpy.random.default_rng(seed) draws float32 standard normals in the
 order x_q, x_k, v, then (for the peaked workload) the permutation choosing
 the amplified key rows, then the permutation choosing sampled rows. Workload
-c in 1..5 uses seed 1000 + c.
+c in 1..5 uses seed 1000 + c. The batched-decode workload (seed 1006) draws
+each sequence b from its own generator default_rng([seed, b]): its query
+row, then its pos_b + 1 key rows and value rows; sequences are packed back to
+back in one cache buffer.
 """
 from __future__ import annotations
 
@@ -27,6 +30,13 @@ WORKLOADS = {
                         decode_positions=[32767, 32768, 32769, 65537, 131071]),
     "varlen_4seq": dict(seed=1005, lengths=[8192, 40960, 73728, 106496], Hq=32, Hkv=8, d=128,
                         w_pre=32768, w0=2048, theta=1e6, std=1.0, dtype="bf16"),
+    # 16 sequences decoding at once, positions spread over G = 1..4 (with the
+    # G edges 32767 / 32768 and the longest 131071): 906,870 cached keys
+    "decode_batch_16": dict(seed=1006, positions=[131071, 4095, 32767, 32768, 98303, 65537, 16383,
+                                                  120000, 8191, 49151, 81920, 24575, 110000,
+                                                  57343, 73727, 1023],
+                            Hq=32, Hkv=8, d=128, w_pre=32768, w0=4096, theta=1e6, std=1.0,
+                            dtype="bf16"),
 }
 
 
@@ -77,6 +87,30 @@ def make_qkv(seed, T, Hq, Hkv, d, std=1.0, dtype="bf16", peaked_frac=0.0, peaked
             idx = rng.permutation(T)[:n]
             xk[idx, g, :] *= np.float32(peaked_gain)
     return xq, xk, v, rng
+
+
+def make_decode_seq(seed, b, n_keys, Hq, Hkv, d, std=1.0, dtype="bf16"):
+    """Sequence b of a batched-decode workload: (xq [Hq, d], xk [n_keys, Hkv, d],
+    v [n_keys, Hkv, d]) raw, from default_rng([seed, b]) in that order."""
+    rng = np.random.default_rng([seed, b])
+    xq = gaussian(rng, (Hq, d), std)
+    xk = gaussian(rng, (n_keys, Hkv, d), std)
+    v = gaussian(rng, (n_keys, Hkv, d), std)
+    if dtype == "bf16":
+        xq, xk, v = quantize_bf16(xq), quantize_bf16(xk), quantize_bf16(v)
+    return xq, xk, v
+
+
+def packed_starts(positions, gaps=None):
+    """First cache row of each sequence when sequence b's pos_b + 1 rows follow
+    the previous sequence's rows (after gaps[b] unused rows, if given);
+    returns (starts, total rows)."""
+    starts, row = [], 0
+    for b, p in enumerate(positions):
+        row += 0 if gaps is None else int(gaps[b])
+        starts.append(row)
+        row += int(p) + 1
+    return starts, row
 
 
 def sample_rows(rng, L, n, must_include):

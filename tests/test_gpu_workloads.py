@@ -7,6 +7,8 @@ pages measure on; seeds 1002..1005, see synth_inputs.WORKLOADS):
   prefill_64k  : L=65536, Hq/Hkv=16/8, d=128, w_pre=32768 (G=2), w0=4096
   prefill_128k : L=131072, Hq/Hkv=32/8, G=4, w0=4096, 1% of key rows x8
   decode_128k  : 131072-key absolute cache, steps at 32767..131071
+  decode_batch_16 : 16 sequences decoding together, positions 1023..131071
+                 (G = 1..4), 906,870 keys packed in one cache buffer
   varlen_4seq  : 8192/40960/73728/106496 packed, G = 1..4, w0=2048
 Rows: 512 per head (per sequence for varlen), always including the window,
 pretrained-window, tile and G-group edges; the rest a seeded uniform draw.
@@ -18,8 +20,9 @@ import pytest
 import torch
 
 import rope_context_extension_jl_amd as jl
-from oracle import bifocal_attention, decode_row, group_size, rope
-from synth_inputs import WORKLOADS, edge_rows, make_qkv, quantize_bf16, sample_rows
+from oracle import bifocal_attention, decode_batch, decode_row, group_size, rope
+from synth_inputs import (WORKLOADS, edge_rows, make_decode_seq, make_qkv, packed_starts,
+                          quantize_bf16, sample_rows)
 from tests._gpu_common import BF16_LSE_ABS, assert_bf16_close, errs, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -256,3 +259,35 @@ def test_prefill_cached_128k_last_chunk(p128k):
                                rows=rows)
     assert_bf16_close(oh, O, "128K cached chunk")
     assert errs(lh, LSE)[0] <= BF16_LSE_ABS
+
+
+# ------------------------------------------------------------------ batched decode
+def test_decode_batch_16_workload():
+    """All 16 sequences of the batched-decode workload in one launch (the
+    configuration the benchmark times), every entry against the oracle."""
+    c = WORKLOADS["decode_batch_16"]
+    pos = c["positions"]
+    starts, rows = packed_starts(pos)
+    Hq, Hkv, d = c["Hq"], c["Hkv"], c["d"]
+    k_rows = np.empty((rows, Hkv, d), dtype=np.float32)
+    v_rows = np.empty((rows, Hkv, d), dtype=np.float32)
+    xq = np.empty((len(pos), Hq, d), dtype=np.float32)
+    for b, (p, s0) in enumerate(zip(pos, starts)):
+        xq[b], k_rows[s0:s0 + p + 1], v_rows[s0:s0 + p + 1] = make_decode_seq(
+            c["seed"], b, p + 1, Hq, Hkv, d, c["std"], c["dtype"])
+    kc = to_dev(k_rows)
+    for p, s0 in zip(pos, starts):
+        jl.rope_apply(kc[s0:s0 + p + 1], c["theta"])
+    vc = to_dev(v_rows)
+    note(f"decode_batch_16: B={len(pos)} rows={rows}")
+    o, lse = jl.bifocal_decode_batch(
+        to_dev(xq), kc, vc, torch.tensor(pos, dtype=torch.int32, device="cuda"),
+        torch.tensor(starts, dtype=torch.int32, device="cuda"), max(pos) + 1, c["w0"], c["w_pre"],
+        c["theta"])
+    torch.cuda.synchronize()
+    oh, lh = to_host(o), to_host(lse)
+    del kc, vc, o, lse
+    torch.cuda.empty_cache()
+    ro, rl = decode_batch(xq, k_rows, v_rows, pos, starts, c["w0"], c["w_pre"], c["theta"])
+    assert_bf16_close(oh, ro, "decode_batch_16")
+    assert errs(lh, rl)[0] <= BF16_LSE_ABS

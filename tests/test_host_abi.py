@@ -260,3 +260,33 @@ def test_continuous_flag_empty_calls_are_noops():
     assert _prefill(T=0, xq=None, xk=None, v=None, o=None, ws=None, ws_bytes=0, mode=CONT) == 0
     assert _cached(Tq=0, xq=None, kc=None, vc=None, o=None, ws=None, ws_bytes=0,
                    mode=CONT) == 0
+
+
+def _batch(**kw):
+    args = dict(xq=P, kc=P, vc=P, o=P, lse=None, pos=P, st=P, B=4, max_keys=1000, rows=5000,
+                Hq=8, Hkv=2, d=128, w0=16, w_pre=64, theta=1e4, scale=0.0, dt=0, mode=0, splits=0,
+                ws=P, ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return jl.lib().jl_bifocal_decode_batch(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -1), (dict(B=70000), -1), (dict(max_keys=0), -1), (dict(max_keys=2 ** 31), -1),
+    (dict(rows=0), -1), (dict(Hq=6, Hkv=4), -1), (dict(w0=-1), -1), (dict(w_pre=0), -1),
+    (dict(theta=1.0), -1), (dict(splits=-1), -1), (dict(splits=5000), -1), (dict(mode=1), -2),
+    (dict(mode=9), -1), (dict(d=96), -2), (dict(Hq=32, Hkv=2), -2), (dict(dt=4), -1),
+    (dict(pos=None), -1), (dict(st=None), -1), (dict(kc=None), -1), (dict(ws=None), -4),
+    (dict(ws_bytes=100), -4), (dict(ws=ctypes.c_void_p(16 + 8)), -1),
+])
+def test_decode_batch_argument_errors(kw, code):
+    assert _batch(**kw) == code
+
+
+def test_decode_batch_empty_and_sizes():
+    assert _batch(B=0, xq=None, kc=None, vc=None, o=None, pos=None, st=None, ws=None,
+                  ws_bytes=0) == 0
+    a = jl.decode_batch_workspace_size(1, 131072, 32, 128)
+    assert a == jl.decode_workspace_size(131072, 32, 128) + 256  # + the work list
+    assert jl.decode_batch_workspace_size(16, 131072, 32, 128) >= 16 * 32 * 1024 * 130 * 4
+    assert jl.decode_batch_workspace_size(0, 10, 8, 128) == 0
+    assert jl.decode_batch_workspace_size(2, 0, 8, 128) == 0

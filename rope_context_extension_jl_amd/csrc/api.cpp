@@ -276,18 +276,27 @@ int jl_bifocal_prefill_cached(const void* xq, const void* kcache, const void* vc
                                          stream, nullptr, nullptr);
 }
 
-// bf16 single decode: one wave per split, four KV heads per workgroup, two
-// workgroups fit a CU: pick the split count so the workgroups cover the 256
-// CUs evenly (two per CU when each split gets >= 256 keys, else one), since a
-// few CUs holding an extra workgroup would set the kernel's time
-static int decode_bf16_splits(int64_t keys, int Hkv) {
+// bf16 decode: keys per split. One wave per split, four KV heads per
+// workgroup, two workgroups fit a CU: aim at a split count that covers the 256
+// CUs evenly (two workgroups per CU when each split gets >= 256 keys, else
+// one), since a few CUs holding an extra workgroup would set the kernel's
+// time. The kernel walks 32-key chunks, so a split of 32 c + 1 keys costs a
+// whole extra chunk: sizes are whole chunks, rounded down when that leaves
+// only a small last split (its workgroups finish almost at once), else up.
+static int64_t decode_bf16_kps(int64_t keys, int Hkv) {
   const int64_t hg = (Hkv + 3) / 4;
   const int64_t s_full = 512 / hg > 0 ? 512 / hg : 1, s_half = 256 / hg > 0 ? 256 / hg : 1;
   int64_t want;
   if (keys >= 256 * s_full) want = s_full;
   else if (keys >= 128 * s_half) want = s_half;
   else want = (keys + 127) / 128;
-  return (int)want;
+  const int64_t kc = 32 * ((keys + 32 * want - 1) / (32 * want));
+  const int64_t kf = 32 * (keys / (32 * want));
+  if (kf >= 32) {
+    const int64_t sf = (keys + kf - 1) / kf;
+    if (sf == want + 1 && keys - (sf - 1) * kf <= kf / 4) return kf;
+  }
+  return kc;
 }
 
 static int decode_max_splits(int64_t capacity) {
@@ -324,7 +333,8 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
   int S = num_splits;
   if (S == 0) {
     if (dt == JL_BF16) {
-      S = decode_bf16_splits(keys, Hkv);
+      const int64_t kps = decode_bf16_kps(keys, Hkv);
+      S = (int)((keys + kps - 1) / kps);
     } else {
       // float32: one workgroup per split, ~4 per CU, at least 64 keys
       int64_t want = (1024 + Hkv - 1) / Hkv;
@@ -405,7 +415,12 @@ int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void
   // (split, head, sequence) triples.
   int S = num_splits;
   if (S == 0) {
-    S = dt == JL_BF16 ? decode_bf16_splits(max_keys, Hkv) : decode_batch_f32_splits(B, max_keys, Hkv);
+    if (dt == JL_BF16) {
+      const int64_t kps = decode_bf16_kps(max_keys, Hkv);
+      S = (int)((max_keys + kps - 1) / kps);
+    } else {
+      S = decode_batch_f32_splits(B, max_keys, Hkv);
+    }
     if (S > maxs) S = maxs;
   }
   if (S > maxs) return JL_EINVAL;

@@ -330,22 +330,22 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
   if (!xq || !kcache || !vcache || !o) return JL_EINVAL;
   const int maxs = decode_max_splits(capacity);
   const int64_t keys = pos + 1;
-  int S = num_splits;
-  if (S == 0) {
-    if (dt == JL_BF16) {
-      const int64_t kps = decode_bf16_kps(keys, Hkv);
-      S = (int)((keys + kps - 1) / kps);
-    } else {
+  if (num_splits > maxs) return JL_EINVAL;
+  int64_t kps;
+  if (num_splits == 0 && dt == JL_BF16) {
+    kps = decode_bf16_kps(keys, Hkv);
+  } else {
+    int64_t S0 = num_splits;
+    if (S0 == 0) {
       // float32: one workgroup per split, ~4 per CU, at least 64 keys
-      int64_t want = (1024 + Hkv - 1) / Hkv;
-      int64_t by_keys = (keys + 63) / 64;
-      S = (int)(want < by_keys ? want : by_keys);
+      const int64_t want = (1024 + Hkv - 1) / Hkv, by_keys = (keys + 63) / 64;
+      S0 = want < by_keys ? want : by_keys;
     }
-    if (S > maxs) S = maxs;
+    if (S0 > keys) S0 = keys;
+    kps = (keys + S0 - 1) / S0;
   }
-  if (S < 1) S = 1;
-  if (S > maxs) return JL_EINVAL;
-  if ((int64_t)S > keys) S = (int)keys;
+  if ((keys + kps - 1) / kps > maxs) kps = (keys + maxs - 1) / maxs;
+  const int S = (int)((keys + kps - 1) / kps);  // no empty split
   const size_t need = (size_t)Hq * S * (d + 2) * sizeof(float);
   if (!workspace || ws_bytes < need) return JL_EWORKSPACE;
   if (((uintptr_t)workspace) & 15) return JL_EINVAL;
@@ -359,7 +359,7 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
     return hip_status(e);
   e = launch_decode(xq, kcache, vcache, o, lse, pos, Hq, Hkv, d,
                     w0 > (int64_t)INT32_MAX ? INT32_MAX : w0, G, sc, fr, mode == JL_MODE_PLAIN,
-                    cont, dt == JL_FP32, S, workspace, st);
+                    cont, dt == JL_FP32, (int)kps, workspace, st);
   if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
   return hip_status(e);
 }
@@ -413,20 +413,17 @@ int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void
   // it would size them; every sequence is cut into splits of that many keys
   // and a fixed grid walks the resulting work list. fp32: one grid over all
   // (split, head, sequence) triples.
-  int S = num_splits;
-  if (S == 0) {
-    if (dt == JL_BF16) {
-      const int64_t kps = decode_bf16_kps(max_keys, Hkv);
-      S = (int)((max_keys + kps - 1) / kps);
-    } else {
-      S = decode_batch_f32_splits(B, max_keys, Hkv);
-    }
-    if (S > maxs) S = maxs;
+  if (num_splits > maxs) return JL_EINVAL;
+  int64_t kps;
+  if (num_splits == 0 && dt == JL_BF16) {
+    kps = decode_bf16_kps(max_keys, Hkv);
+  } else {
+    int64_t S0 = num_splits ? num_splits : decode_batch_f32_splits(B, max_keys, Hkv);
+    if (S0 > max_keys) S0 = max_keys;
+    kps = (max_keys + S0 - 1) / S0;
   }
-  if (S > maxs) return JL_EINVAL;
-  if ((int64_t)S > max_keys) S = (int)max_keys;
-  const int kps = (int)((max_keys + S - 1) / S);
-  S = (int)((max_keys + kps - 1) / kps);  // no split past max_keys
+  if ((max_keys + kps - 1) / kps > maxs) kps = (max_keys + maxs - 1) / maxs;
+  const int S = (int)((max_keys + kps - 1) / kps);  // no split past max_keys
   const size_t list_off = decode_batch_list_offset(B, Hq, S, d);
   const size_t need = list_off + (size_t)(B + 1) * sizeof(int);
   if (!workspace || ws_bytes < need) return JL_EWORKSPACE;
@@ -444,7 +441,7 @@ int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void
   e = launch_decode_batch(xq, kcache, vcache, o, lse, positions, cache_starts, B, max_keys,
                           cache_rows, Hq, Hkv, d, w0 > (int64_t)INT32_MAX ? INT32_MAX : w0,
                           w_pre > (int64_t)INT32_MAX ? (int64_t)INT32_MAX : w_pre, sc, fr,
-                          mode == JL_MODE_PLAIN, cont, dt == JL_FP32, S, kps, workspace,
+                          mode == JL_MODE_PLAIN, cont, dt == JL_FP32, S, (int)kps, workspace,
                           (int*)((char*)workspace + list_off), grid_wg, st);
   if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
   return hip_status(e);

@@ -711,11 +711,12 @@ __global__ void __launch_bounds__(1024) decode_batch_plan_kernel(DecArgs a, int*
   if (tid == 1023) base[B] = part[1023];
 }
 
-// Merge of the split partials of one query head with LSE weights, one pass:
+// Merge of the split partials of one query head with LSE weights:
 // workgroup (head h, 16 output dims), thread (split group g of 16, dim):
-// each thread folds its splits s = g, g + 16, ... with a running maximum
-// (all loads independent of the arithmetic, so they are in flight together),
-// then the 16 groups are combined through LDS.
+// each thread takes the splits s = g, g + 16, ... sixteen at a time, all of a
+// batch's loads issued before any is used (one memory round trip for up to
+// 256 splits), folds them with a running maximum, and the 16 groups are
+// combined through LDS.
 template <bool F32, int D, bool BATCH>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
   __shared__ float rm[256], rl[256], ra[256];
@@ -736,19 +737,31 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
   const int S = BATCH ? (sq.pos + a.kps) / a.kps : a.S;
   const float* pp = sq.part + (int64_t)h * a.S * (D + 2);
   float M = -INFINITY, L = 0.f, A = 0.f;
-#pragma unroll 4
-  for (int s = grp; s < S; s += 16) {
-    const float* q = pp + (int64_t)s * (D + 2);
-    const float ms = q[0], ls = q[1], as = q[2 + d0 + dd];
-    if (ms > M) {  // -inf partials (no keys) never pass
-      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - ms);
+  for (int s0 = grp; s0 < S; s0 += 256) {
+    float ms[16], ls[16], as[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int s = s0 + 16 * j;
+      const float* q = pp + (int64_t)(s < S ? s : 0) * (D + 2);
+      ms[j] = s < S ? q[0] : -INFINITY;
+      ls[j] = s < S ? q[1] : 0.f;
+      as[j] = s < S ? q[2 + d0 + dd] : 0.f;
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mb = fmaxf(mb, ms[j]);
+    if (mb > -INFINITY) {  // -inf partials (no keys) carry no weight
+      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mb);
       L *= sc;
       A *= sc;
-      M = ms;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float w = ms[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[j] - mb);
+        L += w * ls[j];
+        A += w * as[j];
+      }
+      M = mb;
     }
-    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    L += w * ls;
-    A += w * as;
   }
   rm[tid] = M;
   rl[tid] = L;
@@ -838,14 +851,13 @@ static DecArgs decode_args(const void* xq, const void* kc, const void* vc, void*
 
 hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
                          int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
-                         const RopeFreqs& fr, int plain, int cont, int is_f32, int num_splits,
+                         const RopeFreqs& fr, int plain, int cont, int is_f32, int kps,
                          void* ws, hipStream_t st) {
   DecArgs a = decode_args(xq, kc, vc, o, lse, Hq, Hkv, w0, scale, fr, plain, cont, ws);
   a.pos = (int)pos;
   a.G = (int)G;
   a.fk_rel = 1.0 / (double)G - 1.0;
   const int keys = (int)pos + 1;
-  const int kps = (keys + num_splits - 1) / num_splits;
   a.S = (keys + kps - 1) / kps;  // no empty split
   a.kps = kps;
   launch_decode_any<false>(is_f32, d, Hq / Hkv, 1, nullptr, 0, st, a);

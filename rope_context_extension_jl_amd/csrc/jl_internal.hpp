@@ -105,7 +105,7 @@ hipError_t launch_ie_merge(void* o, float* lse, int out_f32, int64_t T, int Hq, 
 
 hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
                          int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
-                         const RopeFreqs& fr, int plain, int cont, int is_f32, int num_splits,
+                         const RopeFreqs& fr, int plain, int cont, int is_f32, int kps,
                          void* ws, hipStream_t st);
 
 // Batched decode: sequence b's query is row b of xq [B, Hq, d], its keys

@@ -405,6 +405,29 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
                                           DecState<D>& st) {
   using G = DecGeom<D>;
   constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
+  // ---- cos / sin of the correction R_{f(k) - k} of the lane's key in both
+  // blocks (pairs (ds, ds + NDS/2), frequencies 32 ds + 8 g16 + j), packed as
+  // fp16 pairs. They depend on the key index only, so they are computed
+  // before the chunk's data is first touched, i.e. while its loads (and the
+  // next chunk's) are still in flight.
+  typedef _Float16 dh2v __attribute__((ext_vector_type(2)));
+  dh2v rot[2][NDS / 2][8];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = k0 + 16 * kb + c.r16;
+    if (c.correct && c.pos - (k0 + 16 * kb) > c.w0) {  // the block has remote keys
+      const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
+#pragma unroll
+      for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float cs, sn;
+          rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + j], cs, sn);
+          rot[kb][ds][j] = dh2v{(_Float16)cs, (_Float16)sn};
+        }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // ---- S^T = K Q^T per 16-key block, seeded with -m
   df32x4 s2[2];
 #pragma unroll
@@ -417,13 +440,11 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
     dh8v kf[NDS];
     if (c.correct && c.pos - key > c.w0) {
       // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2)
-      const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float cs, sn;
-          rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + j], cs, sn);
+          const float cs = (float)rot[kb][ds][j][0], sn = (float)rot[kb][ds][j][1];
           const float x0 = bf16_lane(b.k[kb][ds], j), x1 = bf16_lane(b.k[kb][ds + NDS / 2], j);
           kf[ds][j] = (_Float16)(x0 * cs - x1 * sn);
           kf[ds + NDS / 2][j] = (_Float16)(x0 * sn + x1 * cs);
@@ -536,16 +557,24 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   // query head r16, rotated at pos (qa) and at f(pos) (qr), times scale*log2 e
   dh8v qa[NDS], qr[NDS];
   {
+    // the lane's dims 32 ds + 8 g16 .. + 8 and their partners + D/2, as
+    // 16-byte loads of a valid row (head r16 clamped), zeroed past R heads
     const bool qv = r16 < R;
     const uint16_t* qp = xq + (int64_t)(h0 + (qv ? r16 : 0)) * D;
+    du32x4 raw0[NDS / 2], raw1[NDS / 2];
+#pragma unroll
+    for (int ds = 0; ds < NDS / 2; ++ds) {
+      raw0[ds] = *(const du32x4*)(qp + 32 * ds + 8 * g16);
+      raw1[ds] = *(const du32x4*)(qp + 32 * ds + 8 * g16 + D / 2);
+    }
     const double fpos = remap_pos(sq.pos, sq.G, a.cont);
 #pragma unroll
     for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 32 * ds + 8 * g16 + j;
-        const float x0 = qv ? bf16_bits_to_f32(qp[i]) : 0.f;
-        const float x1 = qv ? bf16_bits_to_f32(qp[i + D / 2]) : 0.f;
+        const float x0 = qv ? bf16_lane(raw0[ds], j) : 0.f;
+        const float x1 = qv ? bf16_lane(raw1[ds], j) : 0.f;
         float c, sn;
         rope_cs_turns((double)sq.pos, w2pi_s[i], c, sn);
         qa[ds][j] = (_Float16)((x0 * c - x1 * sn) * a.scale_log2);

@@ -13,7 +13,8 @@ Also reported (not part of the timed step): the attention kernel alone (live
 HIP events around it, for the roofline), the library's plain causal RoPE
 attention at the same shape (overhead ratio), the Eq. 7 inclusion-exclusion
 alternative, the 64K and packed-varlen workloads, prefill continued on the cache for the
-last 8192 rows, a window-size sweep, the continuous remote map x/G (prefill
+last 8192 rows, absolute RoPE (jl_rope_apply) of the query and key tensors, a
+window-size sweep, the continuous remote map x/G (prefill
 kernel and decode), decode latency at positions 32767 .. 131071 of a
 131072-key cache with L2 / MALL evicted before every step, a batch of 16
 sequences decoding in one launch, calibrated HBM-read and MFMA ceilings, and the float64 CPU
@@ -65,7 +66,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-iters", type=int, default=100)
-    ap.add_argument("--cpu-rows", type=int, default=128, help="oracle rows for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle rows for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the timed prefill steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -264,6 +265,29 @@ def main():
         del ws_c, oc, lc, qc
         torch.cuda.empty_cache()
 
+        # ---------------------------------------------------- absolute RoPE
+        log("absolute RoPE (jl_rope_apply) of the 128K query and key tensors, in place")
+        rope_x = {"queries": q.clone(), "keys": k.clone()}
+        rope_res = {}
+        for nm, xt in rope_x.items():
+            jl.rope_apply(xt, theta)
+            torch.cuda.synchronize()
+            rt = []
+            for _ in range(5):
+                call[0].record(stream)
+                jl.rope_apply(xt, theta)
+                call[1].record(stream)
+                torch.cuda.synchronize()
+                rt.append(call[0].elapsed_time(call[1]))
+            rm = float(np.median(rt))
+            nb = 2.0 * xt.numel() * xt.element_size()  # read and written once
+            rope_res[nm] = {"shape": list(xt.shape), "ms": round(rm, 4),
+                            "GBps": round(nb / (rm * 1e-3) / 1e9, 1),
+                            "pct_hbm_peak": round(100 * nb / (rm * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+        extras["rope_apply_128k"] = rope_res
+        del rope_x
+        torch.cuda.empty_cache()
+
         # ---------------------------------------------------- w0 sweep
         log("window sweep at 128K (fused attention kernel)")
         sweep = {}
@@ -460,8 +484,10 @@ def main():
             "value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": len(os.sched_getaffinity(0)), "blas_threads": blas_threads,
             "kind": "oracle", "seconds": round(dt, 3),
+            "rows_per_s": round(len(rows) * Hq / dt, 2),
             "sample": f"{len(rows)} seeded query rows x {Hq} heads of prefill_128k (all keys "
-                      "of each row, float64 NumPy), FLOPs 4 (q+1) d per row and head"}
+                      "of each row, float64 NumPy), FLOPs 4 (q+1) d per row and head; "
+                      "rows_per_s counts (row, head) pairs"}
         log(f"CPU oracle: {dt:.2f} s")
     print(json.dumps(result), flush=True)
 

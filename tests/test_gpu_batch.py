@@ -156,3 +156,35 @@ def test_decode_batch_split_invariance_and_single_agreement():
                                        w0, w_pre, theta)
         torch.cuda.synchronize()
         assert torch.equal(one[0], single) and torch.equal(l1[0], ls)
+
+
+def test_decode_batch_many_sequences():
+    """B = 2500 short sequences (more entries than the plan kernel's 1024
+    threads, so each thread scans several), positions 0 .. 300 drawn at
+    random, every 97th entry invalid; checked on a sample of entries plus
+    all invalid ones."""
+    w0, w_pre, theta, Hq, Hkv, d = 20, 64, 1e6, 4, 2, 64
+    rng = np.random.default_rng(8600)
+    B = 2500
+    pos = [int(p) for p in rng.integers(0, 301, B)]
+    xq, k_rows, v_rows, starts, kc, vc, pos_t, st_t, _ = _batch(8600, pos, Hq, Hkv, d, theta)
+    rows = k_rows.shape[0]
+    bad = list(range(0, B, 97))
+    pos_b, st_b = list(pos), list(starts)
+    for i in bad:
+        st_b[i] = rows - 1 if i % 2 else -1  # past the buffer, or a negative start
+    note(f"decode_batch B={B} rows={rows}")
+    o, lse = jl.bifocal_decode_batch(to_dev(xq), kc, vc,
+                                     torch.tensor(pos_b, dtype=torch.int32, device="cuda"),
+                                     torch.tensor(st_b, dtype=torch.int32, device="cuda"), 301,
+                                     w0, w_pre, theta)
+    torch.cuda.synchronize()
+    oh, lh = to_host(o), to_host(lse)
+    for i in bad:
+        if pos_b[i] + st_b[i] >= rows or st_b[i] < 0:
+            assert np.isnan(oh[i]).all() and np.isnan(lh[i]).all(), i
+    sample = sorted(set(rng.choice([i for i in range(B) if i not in bad], 120, replace=False)))
+    ro, rl = decode_batch(xq[sample], k_rows, v_rows, [pos[i] for i in sample],
+                          [starts[i] for i in sample], w0, w_pre, theta)
+    assert_bf16_close(oh[sample], ro, f"decode_batch B={B} sample")
+    assert errs(lh[sample], rl)[0] <= BF16_LSE_ABS

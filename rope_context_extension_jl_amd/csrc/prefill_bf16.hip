@@ -11,8 +11,9 @@
 //     remapped position (fp32 arithmetic, float64-reduced angles) and stores
 //     both as fp16 tiles in the workspace, head-major and padded so every
 //     sequence starts on a 64-row boundary. It also writes V transposed
-//     (d-major) so the PV product can read 16-byte MFMA operands, and
-//     optionally the bf16 absolute key cache.
+//     (d-major, each 16-key group in the PV operand's key order) so the PV
+//     product reads 16-byte MFMA operands, and optionally the bf16 absolute
+//     key cache.
 //   * The attention kernel gives each workgroup (4 waves, 256 threads) 128
 //     query rows of one query head. Each lane of a wave owns ONE query row:
 //     scores are computed transposed, S^T = K Q^T, so the 32x32 MFMA output
@@ -42,8 +43,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // arrays of it out of registers)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int KS = PF_D + 8;   // LDS row stride (elements) of a key tile: 272 B, conflict-free b128 reads
-constexpr int VS = PF_BN + 8;  // LDS row stride of a transposed value tile: 144 B
+// LDS stages are filled by direct global -> LDS transfers (16 bytes per lane,
+// placed contiguously), so rows are not padded; instead the 16-byte chunks of
+// a row are XOR-swizzled by the row: a key row (128 fp16 = 256 B, 16 chunks)
+// by row & 15, a value^T row (64 bf16 = 128 B, 8 chunks) by (row >> 1) & 7.
+// The 16 lanes reading one operand chunk then hit 16 distinct bank groups.
+__device__ __forceinline__ int kswz(int row) { return row & 15; }
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+
+// Position q (0..15) of a 16-key group in the value^T layout (workspace and
+// LDS) holds key vperm(q) of the group: keys {0-3, 8-11, 4-7, 12-15}, so the
+// 8 keys of a lane's PV operand (see softmax_pv_any) are one 16-byte chunk.
+__device__ __forceinline__ int vperm(int q) {
+  return (((q >> 2) ^ (q >> 3)) & 1) ? q ^ 12 : q;
+}
 
 // ---------------------------------------------------------------------------
 // Plan: per-sequence records and the heaviest-first tile order.
@@ -266,7 +279,10 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
       const int dd = (tid >> 3) + 32 * k, kc = tid & 7;
       uint16_t out[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = tile[(8 * kc + e) * (PF_D + 8) + dd];
+      for (int e = 0; e < 8; ++e) {
+        const int pos = 8 * kc + e;  // column of the 64-key row, in the vperm order
+        out[e] = tile[(16 * (pos >> 4) + vperm(pos & 15)) * (PF_D + 8) + dd];
+      }
       *(uint4*)(vt + ((int64_t)g * PF_D + dd) * R + r0 + 8 * kc) = *(const uint4*)out;
     }
     __syncthreads();
@@ -345,56 +361,68 @@ __device__ __forceinline__ int tile_cls_of(const Tctx& c, int j) {
   return tile_class(c.q0, c.q1, k0, min(k0 + PF_BN, c.len) - 1, c.w0);
 }
 
-// Global -> registers: key tile j (64 x 128 fp16) and value tile j
-// (transposed: 128 rows x 64 keys, bf16), 4 x 16 bytes per thread each.
-__device__ __forceinline__ void tile_gload(const Tctx& c, int j, bool rem, u32x4 (&kreg)[4],
-                                           u32x4 (&vreg)[4]) {
-  const uint16_t* ks = (rem ? c.krem : c.kabs) + (int64_t)j * PF_BN * PF_D;
+// Global -> LDS stage of key tile j (64 x 128 fp16, remapped or absolute) and
+// value^T tile j (128 x 64 bf16) by direct transfers, no registers: 16
+// transfers of 1 KiB each per tile, transfer o = w + 4 i issued by wave w.
+// Lane L of a transfer fills the 16 bytes at 16 L of its window, i.e. row
+// (window start) + L / 16 (keys) or + L / 8 (values) at physical chunk L % 16
+// (L % 8), and fetches the logical chunk the swizzle puts there. With this
+// interleaving a lane's swizzle is the same in all four of its transfers,
+// so its source address advances by a constant per transfer.
+__device__ __forceinline__ void tile_dma(const Tctx& c, int j, bool rem, uint16_t* ks,
+                                         uint16_t* vs) {
+  const int w = __builtin_amdgcn_readfirstlane(c.tid >> 6), lane = c.tid & 63;
+  const uint16_t* kg = (rem ? c.krem : c.kabs) + (int64_t)j * PF_BN * PF_D;
+  {
+    const int r0 = 4 * w + (lane >> 4), lc = (lane & 15) ^ kswz(r0);
+    const uint16_t* src = kg + r0 * PF_D + 8 * lc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (c.tid >> 4) + 16 * i, ch = c.tid & 15;
-    kreg[i] = *(const u32x4*)(ks + row * PF_D + 8 * ch);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src + 16 * PF_D * i),
+          (__attribute__((address_space(3))) void*)(ks + 512 * (w + 4 * i)), 16, 0, 0);
   }
-  const uint16_t* vs = c.vt + j * PF_BN;
+  const uint16_t* vg = c.vt + j * PF_BN;
+  {
+    const int r0 = 8 * w + (lane >> 3), lc = (lane & 7) ^ vswz(r0);
+    const uint16_t* src = vg + (int64_t)r0 * c.R + 8 * lc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int dd = (c.tid >> 3) + 32 * i, ch = c.tid & 7;
-    vreg[i] = *(const u32x4*)(vs + (int64_t)dd * c.R + 8 * ch);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src + (int64_t)32 * c.R * i),
+          (__attribute__((address_space(3))) void*)(vs + 512 * (w + 4 * i)), 16, 0, 0);
   }
+}
+// End of a tile: this wave's transfers into the other stage have landed,
+// then every wave is past its reads of this stage.
+__device__ __forceinline__ void tile_sync() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
-// Registers -> LDS stage. Inside each 16-key group the value columns are
-// stored in the order {0-3, 8-11, 4-7, 12-15}, so a lane half reads the 8
-// keys of its PV operand (see tile_compute) as one 16-byte vector.
-__device__ __forceinline__ void tile_lstore(const Tctx& c, uint16_t* ks, uint16_t* vs,
-                                            const u32x4 (&kreg)[4], const u32x4 (&vreg)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (c.tid >> 4) + 16 * i, ch = c.tid & 15;
-    *(u32x4*)(ks + row * KS + 8 * ch) = kreg[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int dd = (c.tid >> 3) + 32 * i, ch = c.tid & 7;
-    const int base = dd * VS + 16 * (ch >> 1) + 4 * (ch & 1);
-    *(uint2*)(vs + base) = make_uint2(vreg[i].x, vreg[i].y);
-    *(uint2*)(vs + base + 8) = make_uint2(vreg[i].z, vreg[i].w);
-  }
-}
+// The two LDS stages (key, value^T) x 2; the stage a tile uses is picked at
+// run time. Reads of a stage and the transfers in flight into the other
+// touch disjoint LDS; the wait + barrier at the end of each tile orders a
+// transfer before the reads of its data.
+struct Stages {
+  uint16_t *k0, *v0, *k1, *v1;
+};
 
 // S^T (two 32-key blocks) = K Q^T for the key tile in LDS. The A operand is a
 // key row slice d = 16c + 8hh .. +8, the B operand the same slice of the
 // lane's query row; the MFMA's k-index mapping is the same for both.
 __device__ __forceinline__ void qk_lds(const Tctx& c, const uint16_t* ks, const h8v (&q)[8],
                                        const f32x16& negm, f32x16 (&s)[2]) {
+  const int x = kswz(c.l32);
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
-    const uint16_t* krow = ks + (32 * bk + c.l32) * KS + 8 * c.hh;
-    s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)krow, q[0], negm, 0, 0, 0);
+    const uint16_t* krow = ks + (32 * bk + c.l32) * PF_D;
+    s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 8 * (c.hh ^ x)), q[0],
+                                                   negm, 0, 0, 0);
 #pragma unroll
     for (int cc = 1; cc < 8; ++cc)
-      s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 16 * cc), q[cc], s[bk],
-                                                     0, 0, 0);
+      s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          *(const h8v*)(krow + 8 * ((2 * cc + c.hh) ^ x)), q[cc], s[bk], 0, 0, 0);
   }
 }
 
@@ -527,60 +555,65 @@ __device__ __forceinline__ void softmax_pv_any(const Tctx& c, int j, int mask_mo
   st.l += psum;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const uint16_t* vrow = vs + (32 * db + c.l32) * VS + 8 * c.hh;
+    const uint16_t* vrow = vs + (32 * db + c.l32) * PF_BN;
+    const int y = vswz(c.l32);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const b8v*)(vrow + 16 * ks), pb[ks],
-                                                           st.acc[db], 0, 0, 0);
+      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *(const b8v*)(vrow + 8 * ((2 * ks + c.hh) ^ y)), pb[ks], st.acc[db], 0, 0, 0);
   }
 }
 
+// One key tile from stage (kc, vc) while the next one (if any) streams into
+// (kn, vn).
+__device__ __forceinline__ void tile_step(const Tctx& c, int j, int nxt, bool nrem, int mask_mode,
+                                          const h8v (&q)[8], const uint16_t* kc,
+                                          const uint16_t* vc, uint16_t* kn, uint16_t* vn,
+                                          RowState& st) {
+  if (nxt >= 0) tile_dma(c, nxt, nrem, kn, vn);
+  f32x16 s[2];
+  qk_lds(c, kc, q, st.negm, s);
+  softmax_pv_any(c, j, mask_mode, vc, s, st);
+  tile_sync();
+}
 // Double-buffered walk over key tiles [j0, j1) whose LDS key tiles hold the
 // rotation `rem_src` (remote tiles: remapped keys). `next_after` is the tile
 // to prefetch after the last one (-1: none) and `next_rem` its rotation, so
 // segments chain in any order. `stg` is the LDS stage holding tile j0.
 __device__ __forceinline__ void walk(const Tctx& c, int j0, int j1, bool rem_src, int next_after,
                                      bool next_rem, int mask_mode, const h8v (&q)[8],
-                                     uint16_t (&Ks)[2][PF_BN * KS], uint16_t (&Vs)[2][PF_D * VS],
-                                     int& stg, RowState& st) {
-  u32x4 kreg[4], vreg[4];
+                                     const Stages& S, int& stg, RowState& st) {
   for (int j = j0; j < j1; ++j) {
     const int nxt = j + 1 < j1 ? j + 1 : next_after;
-    if (nxt >= 0) tile_gload(c, nxt, j + 1 < j1 ? rem_src : next_rem, kreg, vreg);
-    f32x16 s[2];
-    qk_lds(c, Ks[stg], q, st.negm, s);
-    softmax_pv_any(c, j, mask_mode, Vs[stg], s, st);
-    if (nxt >= 0) tile_lstore(c, Ks[stg ^ 1], Vs[stg ^ 1], kreg, vreg);
-    __syncthreads();
+    const bool nrem = j + 1 < j1 ? rem_src : next_rem;
+    tile_step(c, j, nxt, nrem, mask_mode, q, stg ? S.k1 : S.k0, stg ? S.v1 : S.v0,
+              stg ? S.k0 : S.k1, stg ? S.v0 : S.v1, st);
     stg ^= 1;
   }
 }
-
-// Boundary tiles of the fused pass: both query operands are live, so the
-// next tile is loaded only after this one is consumed (no prefetch
-// registers). The LDS key tile holds the absolute keys.
+// Boundary tiles of the fused pass: the LDS key tile holds the absolute
+// keys; the remapped scores come from the global key tile.
+__device__ __forceinline__ void boundary_step(const Tctx& c, int j, int nxt, const h8v (&qa)[8],
+                                              const h8v (&qr)[8], const uint16_t* kc,
+                                              const uint16_t* vc, uint16_t* kn, uint16_t* vn,
+                                              RowState& st) {
+  if (nxt >= 0) tile_dma(c, nxt, false, kn, vn);
+  f32x16 s[2];
+  qk_lds(c, kc, qa, st.negm, s);
+  boundary_select(c, j, qr, st.negm, s);
+  softmax_pv_any(c, j, MASK_NONE, vc, s, st);
+  tile_sync();
+}
 __device__ __forceinline__ void walk_boundary(const Tctx& c, int j0, int j1, int next_after,
                                               const h8v (&qa)[8], const h8v (&qr)[8],
-                                              uint16_t (&Ks)[2][PF_BN * KS],
-                                              uint16_t (&Vs)[2][PF_D * VS], int& stg,
-                                              RowState& st) {
-  u32x4 kreg[4], vreg[4];
+                                              const Stages& S, int& stg, RowState& st) {
   for (int j = j0; j < j1; ++j) {
     const int nxt = j + 1 < j1 ? j + 1 : next_after;
-    f32x16 s[2];
-    qk_lds(c, Ks[stg], qa, st.negm, s);
-    boundary_select(c, j, qr, st.negm, s);
-    softmax_pv_any(c, j, MASK_NONE, Vs[stg], s, st);
-    __syncthreads();
-    if (nxt >= 0) {
-      tile_gload(c, nxt, false, kreg, vreg);
-      tile_lstore(c, Ks[stg ^ 1], Vs[stg ^ 1], kreg, vreg);
-    }
-    __syncthreads();
+    boundary_step(c, j, nxt, qa, qr, stg ? S.k1 : S.k0, stg ? S.v1 : S.v0, stg ? S.k0 : S.k1,
+                  stg ? S.v0 : S.v1, st);
     stg ^= 1;
   }
 }
-
 // RoPE(x_q, p) of the lane's raw query row as the fp16 QK^T operand. The lane
 // holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs (d, d+64)
 // are chunks (c, c+4) of the same lane. w2pi: omega_i / (2 pi) in LDS.
@@ -601,8 +634,10 @@ __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], double p, in
 
 template <int PASS>
 __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][PF_BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][PF_D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[PF_BN * PF_D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[PF_BN * PF_D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[PF_D * PF_BN];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[PF_D * PF_BN];
   __shared__ double w2pi_s[PF_D / 2];  // omega_i / (2 pi)
 
   const int Hq = a.Hq, Hkv = a.Hkv;
@@ -680,15 +715,14 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   st.m = -INFINITY;
   st.l = 0.f;
   int stg = 0;
+  const Stages S{Ks0, Vs0, Ks1, Vs1};
   {
     // the first key tile: remapped keys for the remote phase of the fused
     // pass and for passes B/C, absolute otherwise
     const bool rem0 = (PASS == PASS_FUSED && jstart < j_nr) || PASS == PASS_IE_B;
-    u32x4 kreg[4], vreg[4];
-    tile_gload(c, jstart, rem0, kreg, vreg);
-    tile_lstore(c, Ks[0], Vs[0], kreg, vreg);
+    tile_dma(c, jstart, rem0, Ks0, Vs0);
   }
-  __syncthreads();  // also publishes w2pi_s
+  tile_sync();  // also publishes w2pi_s
 
   if (PASS == PASS_FUSED) {
     const int jl0 = max(j_nr, j_loc);
@@ -696,25 +730,25 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
       h8v qr[8];
       rotq(remap_pos(c.myq, sq.G, a.cont), qr);
       // remote phase: remapped query against remapped key tiles
-      walk(c, 0, j_nr, true, j_nr < c.nkt ? j_nr : -1, false, MASK_NONE, qr, Ks, Vs, stg, st);
+      walk(c, 0, j_nr, true, j_nr < c.nkt ? j_nr : -1, false, MASK_NONE, qr, S, stg, st);
       if (j_nr < j_loc) {  // boundary phase: both routes, element-wise select
         h8v qa[8];
         rotq(c.myq, qa);
-        walk_boundary(c, j_nr, j_loc, jl0 < c.nkt ? jl0 : -1, qa, qr, Ks, Vs, stg, st);
+        walk_boundary(c, j_nr, j_loc, jl0 < c.nkt ? jl0 : -1, qa, qr, S, stg, st);
       }
     }
     h8v qa[8];
     rotq(c.myq, qa);
     // local phase: absolute query against absolute key tiles
-    walk(c, jl0, c.nkt, false, -1, false, MASK_NONE, qa, Ks, Vs, stg, st);
+    walk(c, jl0, c.nkt, false, -1, false, MASK_NONE, qa, S, stg, st);
   } else if (PASS == PASS_PLAIN) {
     h8v qa[8];
     rotq(c.myq, qa);
-    walk(c, 0, c.nkt, false, -1, false, MASK_NONE, qa, Ks, Vs, stg, st);
+    walk(c, 0, c.nkt, false, -1, false, MASK_NONE, qa, S, stg, st);
   } else if (PASS == PASS_IE_A) {
     h8v qa[8];
     rotq(c.myq, qa);
-    walk(c, j_nr, c.nkt, false, -1, false, MASK_WINDOW, qa, Ks, Vs, stg, st);
+    walk(c, j_nr, c.nkt, false, -1, false, MASK_WINDOW, qa, S, stg, st);
   } else {
     // Passes C and B of Eq. 7 run this same code: the window keys first, in
     // the same order and with the same masks, so pass C's softmax state is a
@@ -724,10 +758,10 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     h8v qr[8];
     rotq(remap_pos(c.myq, sq.G, a.cont), qr);
     const int seg2 = j_nr < j_loc ? j_nr : (j_nr > 0 ? 0 : -1);
-    walk(c, j_nr, c.nkt, true, a.ie_remote ? seg2 : -1, true, MASK_WINDOW, qr, Ks, Vs, stg, st);
+    walk(c, j_nr, c.nkt, true, a.ie_remote ? seg2 : -1, true, MASK_WINDOW, qr, S, stg, st);
     if (a.ie_remote) {
-      walk(c, j_nr, j_loc, true, j_nr > 0 ? 0 : -1, true, MASK_REMOTE, qr, Ks, Vs, stg, st);
-      walk(c, 0, j_nr, true, -1, true, MASK_NONE, qr, Ks, Vs, stg, st);
+      walk(c, j_nr, j_loc, true, j_nr > 0 ? 0 : -1, true, MASK_REMOTE, qr, S, stg, st);
+      walk(c, 0, j_nr, true, -1, true, MASK_NONE, qr, S, stg, st);
     }
   }
 

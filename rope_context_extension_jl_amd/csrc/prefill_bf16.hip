@@ -28,6 +28,9 @@
 //     fp16 range holds them, and fp16 carries 3 more mantissa bits than bf16
 //     at the same MFMA rate); PV uses bf16 P and the raw bf16 V. Accumulation
 //     is fp32 throughout; O is rounded to bf16 once.
+//   * When Hq / Hkv is even, the fused and plain passes run two query heads
+//     of one KV head per workgroup (8 waves, one workgroup per CU) over a
+//     3-stage LDS pipeline; the 4-wave kernel serves odd ratios and Eq. 7.
 //   * The schedule hands the heaviest query tiles out first (longest causal
 //     key range), and consecutive workgroups of one XCD share a KV head so
 //     the key tiles they stream stay in that XCD's L2.
@@ -798,6 +801,206 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Head-pair attention pass (fused and plain). Query heads 2p and 2p + 1 read
+// the same KV head when Hq / Hkv is even, so one workgroup of 8 waves runs
+// both on the same 128 query rows (waves 0-3: head 2p, waves 4-7: head
+// 2p + 1) and every key / value tile staged in LDS feeds twice the MFMA work
+// of the 4-wave pass. One workgroup per CU leaves LDS for three stages: the
+// tile two ahead is in flight while a tile is computed. Both heads see the
+// same tile classes (they depend on positions only), so all waves take the
+// same path and the same barriers.
+// ---------------------------------------------------------------------------
+constexpr int PAIR_STAGES = 3;
+
+// Tile j into a stage by 8 waves: transfer o = w + 8 i (i < 2) of each array.
+__device__ __forceinline__ void tile_dma8(const Tctx& c, int j, bool rem, uint16_t* ks,
+                                          uint16_t* vs) {
+  const int w = __builtin_amdgcn_readfirstlane(c.tid >> 6), lane = c.tid & 63;
+  const uint16_t* kg = (rem ? c.krem : c.kabs) + (int64_t)j * PF_BN * PF_D;
+  {
+    const int r0 = 4 * w + (lane >> 4), lc = (lane & 15) ^ kswz(r0);  // kswz(r0 + 32 i) = kswz(r0)
+    const uint16_t* src = kg + r0 * PF_D + 8 * lc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src + 32 * PF_D * i),
+          (__attribute__((address_space(3))) void*)(ks + 512 * (w + 8 * i)), 16, 0, 0);
+  }
+  const uint16_t* vg = c.vt + j * PF_BN;
+  {
+    const int r0 = 8 * w + (lane >> 3), lc = (lane & 7) ^ vswz(r0);  // vswz(r0 + 64 i) = vswz(r0)
+    const uint16_t* src = vg + (int64_t)r0 * c.R + 8 * lc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src + (int64_t)64 * c.R * i),
+          (__attribute__((address_space(3))) void*)(vs + 512 * (w + 8 * i)), 16, 0, 0);
+  }
+}
+
+// End of a tile of the 3-stage walk: the tile after this one has landed
+// (only the 4 transfers of the tile two ahead may still be in flight when
+// `ahead`), this wave's LDS reads are done, then every wave is past this
+// stage. No fence: it would also wait for the transfers two ahead.
+__device__ __forceinline__ void pair_sync(bool ahead) {
+  if (ahead) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int PASS>
+__global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[PF_BN * PF_D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[PF_BN * PF_D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[PF_BN * PF_D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[PF_D * PF_BN];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[PF_D * PF_BN];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs2[PF_D * PF_BN];
+  __shared__ double w2pi_s[PF_D / 2];  // omega_i / (2 pi)
+
+  const int Hq = a.Hq, Hkv = a.Hkv, npairs = Hq >> 1;
+  // ---- work item: (schedule slot, head pair); XCD-aware pair grouping
+  int slot, pair;
+  {
+    const int w = blockIdx.x;
+    if ((npairs & 7) == 0) {
+      const int hpx = npairs >> 3, k = w >> 3;
+      slot = k / hpx;
+      pair = (w & 7) * hpx + k % hpx;
+    } else {
+      slot = w / npairs;
+      pair = w % npairs;
+    }
+  }
+  const int* __restrict__ hdr = a.hdr;
+  if (slot >= hdr[0]) return;
+  if (threadIdx.x < PF_D / 2) w2pi_s[threadIdx.x] = a.fr.w(threadIdx.x) * kInvTwoPi;
+  const int* __restrict__ tbase = a.tbase;
+  int t;
+  {
+    int lo = 0, hi = hdr[1] - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (tbase[mid] <= slot) hi = mid; else lo = mid + 1;
+    }
+    t = lo;
+  }
+  const SeqInfo sq = a.seqs[a.order[slot - tbase[t]]];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int head = 2 * pair + (wave >> 2);
+  const int g = (2 * pair) / (Hq / Hkv);
+  const int R = a.R;
+
+  Tctx c;
+  c.tid = threadIdx.x;
+  c.hh = (c.tid & 63) >> 5;
+  c.l32 = c.tid & 31;
+  c.q0 = a.qoff + t * PF_BM;
+  c.q1 = min(c.q0 + PF_BM, sq.len) - 1;
+  c.len = sq.len;
+  c.myq = c.q0 + (wave & 3) * 32 + c.l32;
+  c.nkt = c.q1 / PF_BN + 1;
+  c.w0 = a.w0;
+  c.R = R;
+  c.kabs = a.kabs + ((int64_t)g * R + sq.pad_off) * PF_D;
+  c.krem = a.krem + ((int64_t)g * R + sq.pad_off) * PF_D;
+  c.vt = a.vt + (int64_t)g * PF_D * R + sq.pad_off;
+  const bool qvalid = c.myq < sq.len;
+
+  const uint16_t* qp =
+      a.xq + ((int64_t)(sq.start + (qvalid ? c.myq - a.qoff : 0)) * Hq + head) * PF_D + 8 * c.hh;
+  auto rotq = [&](double p, h8v (&out)[8]) __attribute__((always_inline)) {
+    u32x4 raw[8];
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      raw[cc] = qvalid ? *(const u32x4*)(qp + 16 * cc) : u32x4{0, 0, 0, 0};
+    rotate_query(raw, p, c.hh, w2pi_s, out);
+  };
+
+  // first tile that is not all-remote, first tile that is all-local
+  const int nkt = c.nkt;
+  const int j_nr = PASS == PASS_FUSED ? (c.q0 > c.w0 ? (c.q0 - c.w0) / PF_BN : 0) : 0;
+  const int j_loc =
+      PASS == PASS_FUSED ? (c.q1 > c.w0 ? min(nkt, (c.q1 - c.w0 + PF_BN - 1) / PF_BN) : 0) : 0;
+  const int jl0 = max(j_nr, j_loc);
+  auto rem_of = [&](int j) { return j < j_nr; };  // remote tiles stage the remapped keys
+  auto kst = [&](int j) -> uint16_t* {  // stage of tile j: j mod 3
+    const int s3 = j % PAIR_STAGES;
+    return s3 == 0 ? Ks0 : s3 == 1 ? Ks1 : Ks2;
+  };
+  auto vst = [&](int j) -> uint16_t* {
+    const int s3 = j % PAIR_STAGES;
+    return s3 == 0 ? Vs0 : s3 == 1 ? Vs1 : Vs2;
+  };
+
+  RowState st;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.acc[i][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) st.negm[r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  // tiles 0 and 1 in flight; wait for tile 0 (and w2pi_s)
+  tile_dma8(c, 0, rem_of(0), Ks0, Vs0);
+  if (nkt > 1) tile_dma8(c, 1, rem_of(1), Ks1, Vs1);
+  __syncthreads();  // publishes w2pi_s (the fence also waits for both tiles)
+
+  // one tile: prefetch j + 2 into the stage freed at the last barrier,
+  // compute j, wait for j + 1
+  auto step = [&](int j, const h8v (&q)[8], const h8v* qr_b) __attribute__((always_inline)) {
+    const bool ahead = j + 2 < nkt;
+    if (ahead) tile_dma8(c, j + 2, rem_of(j + 2), kst(j + 2), vst(j + 2));
+    f32x16 s[2];
+    qk_lds(c, kst(j), q, st.negm, s);
+    if (qr_b) boundary_select(c, j, *(const h8v(*)[8])qr_b, st.negm, s);
+    softmax_pv_any(c, j, MASK_NONE, vst(j), s, st);
+    pair_sync(ahead);
+  };
+  if (PASS == PASS_FUSED) {
+    {
+      h8v qr[8];
+      rotq(remap_pos(c.myq, sq.G, a.cont), qr);
+      for (int j = 0; j < j_nr; ++j) step(j, qr, nullptr);  // remote phase
+      if (j_nr < j_loc) {                                    // boundary phase
+        h8v qa[8];
+        rotq(c.myq, qa);
+        for (int j = j_nr; j < j_loc; ++j) step(j, qa, &qr[0]);
+      }
+    }
+    h8v qa[8];
+    rotq(c.myq, qa);
+    for (int j = jl0; j < nkt; ++j) step(j, qa, nullptr);  // local phase
+  } else {
+    h8v qa[8];
+    rotq(c.myq, qa);
+    for (int j = 0; j < nkt; ++j) step(j, qa, nullptr);
+  }
+
+  // ---- epilogue
+  const float l_tot = st.l + xor32(st.l);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!qvalid) return;
+  const int64_t row = (int64_t)(sq.start + c.myq - a.qoff);
+  uint16_t* op = (uint16_t*)a.o + (row * Hq + head) * PF_D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const uint32_t lo = (uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 2] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 3] * inv) << 16);
+      *(uint2*)(op + 32 * db + 8 * r4 + 4 * c.hh) = make_uint2(lo, hi);
+    }
+  if (a.lse && c.hh == 0) {
+    const float lse = l_tot > 0.f ? (st.m + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    a.lse[(int64_t)head * a.T + row] = lse;
+  }
+}
+
 hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, int64_t T, int B,
                                int Hq, int Hkv, int64_t w0, int64_t qoff, float scale, int cont,
                                const RopeFreqs& fr, void* ws, const PrefillLayout& lay,
@@ -826,6 +1029,14 @@ hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, in
   (void)scale;  // the score scale is carried by the key operands (pre-pass)
   a.fr = fr;
   const int64_t blocks = lay.max_tiles * Hq;
+  if ((pass == PASS_FUSED || pass == PASS_PLAIN) && (Hq / Hkv) % 2 == 0) {
+    const dim3 grid((unsigned)(lay.max_tiles * (Hq / 2)));
+    if (pass == PASS_FUSED)
+      hipLaunchKernelGGL(prefill_pair_kernel<PASS_FUSED>, grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL(prefill_pair_kernel<PASS_PLAIN>, grid, dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
   switch (pass) {
     case PASS_FUSED:
       hipLaunchKernelGGL(prefill_bf16_kernel<PASS_FUSED>, dim3(blocks), dim3(256), 0, st, a);

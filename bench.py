@@ -185,7 +185,9 @@ def main():
                    "theta": theta, "peaked_key_rows": c["peaked_frac"]},
         "tok_per_s": round(L / (ms_per_step * 1e-3), 1),
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<FUSED>",
+        "roofline": {"bound": "mfma", "kernel": ("prefill_pair_kernel<FUSED>"
+                                                  if (Hq // Hkv) % 2 == 0
+                                                  else "prefill_bf16_kernel<FUSED>"),
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kern_avg, 4),

@@ -126,6 +126,8 @@ SMALL_CASES = [
     (640, 4, 2, 64, 64),       # window edge on a key tile
     (2048, 2, 2, 4096, 512),   # w0 beyond L: every pair local
     (513, 16, 2, 127, 100),    # GQA 8:1, G = 6
+    (300, 6, 2, 40, 128),      # GQA 3:1 (odd: one head per workgroup), G = 3
+    (130, 3, 1, 20, 64),       # odd head count, G = 3
 ]
 
 

@@ -46,13 +46,27 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_lines(text):
+    """Source lines without // comments and blank lines (a line holding a
+    string literal is kept whole), so that comment edits keep the hash."""
+    out = []
+    for line in text.splitlines():
+        if '"' not in line and "//" in line:
+            line = line[:line.index("//")]
+        line = line.rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
 def kernel_source_hash():
-    """Hash of the sources the fused attention kernel is compiled from."""
+    """Hash of the code (comments aside) the fused attention kernel is
+    compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rope_context_extension_jl_amd", "csrc")
     for name in ("jl_internal.hpp", "prefill_bf16.hip"):
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(name.encode() + fh.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            h.update(name.encode() + _code_lines(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

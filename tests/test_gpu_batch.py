@@ -66,7 +66,7 @@ def test_decode_batch_bf16(mode, remap):
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(2, 2, 128), (4, 2, 128), (16, 2, 128), (8, 2, 64),
-                                       (8, 8, 64)])
+                                       (8, 8, 64), (12, 6, 128)])
 def test_decode_batch_heads_and_dims(Hq, Hkv, d):
     w0, w_pre, theta = 64, 256, 1e6
     pos = [63, 1299, 255, 256, 700]

@@ -274,7 +274,7 @@ def test_decode_small_positions(dtype):
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(2, 2, 128), (4, 2, 128), (16, 2, 128), (8, 2, 64),
-                                       (8, 8, 64)])
+                                       (8, 8, 64), (12, 6, 128)])
 def test_decode_bf16_head_ratios_and_dims(Hq, Hkv, d):
     """Every GQA ratio the boundary accepts and both head dims, remote and
     local keys, a ragged last chunk (pos + 1 not a multiple of 64)."""

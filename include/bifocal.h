@@ -130,6 +130,10 @@ size_t jl_prefill_ie_ratio_offset(int64_t T, int B, int Hq, int Hkv, int d, jl_d
  * R_{f(k)-k} gives the same vectors by R_a R_b = R_{a+b}; starting from the
  * raw inputs avoids rounding the absolute vectors twice).
  * Supported: bf16 with d = 128 (all modes); fp32 with d = 64 or 128.
+ * Range (bf16): the QK^T operands are fp16, the keys carrying the score scale
+ * times log2(e), so rotated queries must stay below 65504 in magnitude and
+ * keys below 65504 / (scale log2 e) (about 5.1e5 at d = 128); beyond that the
+ * scores overflow to inf and no error is reported.
  * Workspace: jl_prefill_workspace_size(...) bytes of device memory, any
  * contents, 256-byte aligned; it holds the rotated key tiles, the transposed
  * values and the tile schedule. Errors: JL_EINVAL, JL_EUNSUPPORTED,

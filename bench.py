@@ -87,7 +87,7 @@ def main():
                     help="also run one 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: libbifocal has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(1)
 

@@ -35,39 +35,67 @@ __global__ void __launch_bounds__(256) rope_apply_kernel(void* __restrict__ x, i
 #pragma unroll
   for (int j = 0; j < 8; ++j) rope_cs((double)p, fr.w(8 * c + j), cs[j], sn[j]);
   const int half = d / 2;
-  for (int h = 0; h < H; ++h) {
-    const int64_t base = ((int64_t)t * H + h) * d;
+  // Heads in groups of HG: all loads of a group are issued before its first
+  // store (the rows are distinct, but in place the compiler cannot know that
+  // a store does not feed a later load), so each thread keeps HG rows in
+  // flight instead of one.
+  constexpr int HG = 4;
+  for (int h0 = 0; h0 < H; h0 += HG) {
     if constexpr (F32) {
-      float* xr = (float*)x + base;
-      float4 a0 = *(const float4*)(xr + 8 * c), a1 = *(const float4*)(xr + 8 * c + 4);
-      float4 b0 = *(const float4*)(xr + half + 8 * c), b1 = *(const float4*)(xr + half + 8 * c + 4);
-      float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      float ra[8], rb[8];
+      float4 a[HG][2], b[HG][2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ra[j] = a[j] * cs[j] - b[j] * sn[j];
-        rb[j] = a[j] * sn[j] + b[j] * cs[j];
-      }
-      *(float4*)(xr + 8 * c) = make_float4(ra[0], ra[1], ra[2], ra[3]);
-      *(float4*)(xr + 8 * c + 4) = make_float4(ra[4], ra[5], ra[6], ra[7]);
-      *(float4*)(xr + half + 8 * c) = make_float4(rb[0], rb[1], rb[2], rb[3]);
-      *(float4*)(xr + half + 8 * c + 4) = make_float4(rb[4], rb[5], rb[6], rb[7]);
+      for (int u = 0; u < HG; ++u)
+        if (h0 + u < H) {
+          const float* xr = (const float*)x + ((int64_t)t * H + h0 + u) * d;
+          a[u][0] = *(const float4*)(xr + 8 * c);
+          a[u][1] = *(const float4*)(xr + 8 * c + 4);
+          b[u][0] = *(const float4*)(xr + half + 8 * c);
+          b[u][1] = *(const float4*)(xr + half + 8 * c + 4);
+        }
+#pragma unroll
+      for (int u = 0; u < HG; ++u)
+        if (h0 + u < H) {
+          float* xr = (float*)x + ((int64_t)t * H + h0 + u) * d;
+          const float av[8] = {a[u][0].x, a[u][0].y, a[u][0].z, a[u][0].w,
+                               a[u][1].x, a[u][1].y, a[u][1].z, a[u][1].w};
+          const float bv[8] = {b[u][0].x, b[u][0].y, b[u][0].z, b[u][0].w,
+                               b[u][1].x, b[u][1].y, b[u][1].z, b[u][1].w};
+          float ra[8], rb[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            ra[j] = av[j] * cs[j] - bv[j] * sn[j];
+            rb[j] = av[j] * sn[j] + bv[j] * cs[j];
+          }
+          *(float4*)(xr + 8 * c) = make_float4(ra[0], ra[1], ra[2], ra[3]);
+          *(float4*)(xr + 8 * c + 4) = make_float4(ra[4], ra[5], ra[6], ra[7]);
+          *(float4*)(xr + half + 8 * c) = make_float4(rb[0], rb[1], rb[2], rb[3]);
+          *(float4*)(xr + half + 8 * c + 4) = make_float4(rb[4], rb[5], rb[6], rb[7]);
+        }
     } else {
-      uint16_t* xr = (uint16_t*)x + base;
-      uint4 av = *(const uint4*)(xr + 8 * c);
-      uint4 bv = *(const uint4*)(xr + half + 8 * c);
-      const uint16_t* ap = (const uint16_t*)&av;
-      const uint16_t* bp = (const uint16_t*)&bv;
-      uint16_t ro[8], rq[8];
+      uint4 av[HG], bv[HG];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float a = bf16_bits_to_f32(ap[j]), b = bf16_bits_to_f32(bp[j]);
-        ro[j] = f32_to_bf16_bits(a * cs[j] - b * sn[j]);
-        rq[j] = f32_to_bf16_bits(a * sn[j] + b * cs[j]);
-      }
-      *(uint4*)(xr + 8 * c) = *(const uint4*)ro;
-      *(uint4*)(xr + half + 8 * c) = *(const uint4*)rq;
+      for (int u = 0; u < HG; ++u)
+        if (h0 + u < H) {
+          const uint16_t* xr = (const uint16_t*)x + ((int64_t)t * H + h0 + u) * d;
+          av[u] = *(const uint4*)(xr + 8 * c);
+          bv[u] = *(const uint4*)(xr + half + 8 * c);
+        }
+#pragma unroll
+      for (int u = 0; u < HG; ++u)
+        if (h0 + u < H) {
+          uint16_t* xr = (uint16_t*)x + ((int64_t)t * H + h0 + u) * d;
+          const uint16_t* ap = (const uint16_t*)&av[u];
+          const uint16_t* bp = (const uint16_t*)&bv[u];
+          uint16_t ro[8], rq[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float a = bf16_bits_to_f32(ap[j]), b = bf16_bits_to_f32(bp[j]);
+            ro[j] = f32_to_bf16_bits(a * cs[j] - b * sn[j]);
+            rq[j] = f32_to_bf16_bits(a * sn[j] + b * cs[j]);
+          }
+          *(uint4*)(xr + 8 * c) = *(const uint4*)ro;
+          *(uint4*)(xr + half + 8 * c) = *(const uint4*)rq;
+        }
     }
   }
 }

@@ -23,7 +23,7 @@ BIG = 10 ** 9  # a window wider than any sequence: plain causal RoPE attention
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("T,H,d,pos_offset,lens", [
     (1000, 3, 128, 0, None), (777, 2, 64, 12345, None), (1300, 4, 128, 0, [5, 0, 700, 595]),
-    (64, 1, 256, 131000, None)])
+    (64, 1, 256, 131000, None), (500, 6, 128, 7, None)])
 def test_rope_apply(dtype, T, H, d, pos_offset, lens):
     theta = 1e6
     x, _, _, _ = make_qkv(7, T, H, 1, d, dtype=dtype)

@@ -28,9 +28,10 @@
 //     fp16 range holds them, and fp16 carries 3 more mantissa bits than bf16
 //     at the same MFMA rate); PV uses bf16 P and the raw bf16 V. Accumulation
 //     is fp32 throughout; O is rounded to bf16 once.
-//   * When Hq / Hkv is even, the fused and plain passes run two query heads
-//     of one KV head per workgroup (8 waves, one workgroup per CU) over a
-//     3-stage LDS pipeline; the 4-wave kernel serves odd ratios and Eq. 7.
+//   * When Hq / Hkv is even, every pass (fused, plain, the three of Eq. 7)
+//     runs two query heads of one KV head per workgroup (8 waves, one
+//     workgroup per CU) over a 3-stage LDS pipeline; the 4-wave kernel, one
+//     head per workgroup, serves odd ratios.
 //   * The schedule hands the heaviest query tiles out first (longest causal
 //     key range), and consecutive workgroups of one XCD share a KV head so
 //     the key tiles they stream stay in that XCD's L2.
@@ -919,11 +920,27 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
 
   // first tile that is not all-remote, first tile that is all-local
   const int nkt = c.nkt;
-  const int j_nr = PASS == PASS_FUSED ? (c.q0 > c.w0 ? (c.q0 - c.w0) / PF_BN : 0) : 0;
+  constexpr bool kIE = PASS == PASS_IE_A || PASS == PASS_IE_B;
+  constexpr bool kRoute = PASS != PASS_PLAIN;
+  const int j_nr = kRoute ? (c.q0 > c.w0 ? (c.q0 - c.w0) / PF_BN : 0) : 0;
   const int j_loc =
-      PASS == PASS_FUSED ? (c.q1 > c.w0 ? min(nkt, (c.q1 - c.w0 + PF_BN - 1) / PF_BN) : 0) : 0;
+      kRoute ? (c.q1 > c.w0 ? min(nkt, (c.q1 - c.w0 + PF_BN - 1) / PF_BN) : 0) : 0;
   const int jl0 = max(j_nr, j_loc);
-  auto rem_of = [&](int j) { return j < j_nr; };  // remote tiles stage the remapped keys
+  // key tiles in walk order. Fused and plain: tile n at step n. Eq. 7 passes:
+  // the window tiles j_nr .. nkt - 1 (window mask); pass B (ie_remote) then
+  // the boundary tiles again (remote mask) and the all-remote tiles 0 ..
+  // j_nr - 1, so pass C's softmax state is a bitwise prefix of pass B's.
+  const bool ie_rem = PASS == PASS_IE_B && a.ie_remote;
+  const int n1 = kIE ? nkt - j_nr : nkt;
+  const int n2 = ie_rem ? max(j_loc - j_nr, 0) : 0;
+  const int nwalk = n1 + n2 + (ie_rem ? j_nr : 0);
+  auto tile_of = [&](int n) -> int {
+    if (!kIE) return n;
+    return n < n1 ? j_nr + n : n < n1 + n2 ? j_nr + (n - n1) : n - n1 - n2;
+  };
+  // remote tiles of the fused pass and every tile of passes B / C stage the
+  // remapped keys
+  auto rem_of = [&](int j) { return PASS == PASS_IE_B || (PASS == PASS_FUSED && j < j_nr); };
   auto kst = [&](int j) -> uint16_t* {  // stage of tile j: j mod 3
     const int s3 = j % PAIR_STAGES;
     return s3 == 0 ? Ks0 : s3 == 1 ? Ks1 : Ks2;
@@ -943,9 +960,9 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
   st.m = -INFINITY;
   st.l = 0.f;
 
-  // tiles 0 and 1 in flight; wait for tile 0 (and w2pi_s)
-  tile_dma8(c, 0, rem_of(0), Ks0, Vs0);
-  if (nkt > 1) tile_dma8(c, 1, rem_of(1), Ks1, Vs1);
+  // the walk's first two tiles in flight; wait for them (and w2pi_s)
+  tile_dma8(c, tile_of(0), rem_of(tile_of(0)), Ks0, Vs0);
+  if (nwalk > 1) tile_dma8(c, tile_of(1), rem_of(tile_of(1)), Ks1, Vs1);
   __syncthreads();  // publishes w2pi_s (the fence also waits for both tiles)
 
   // one tile: prefetch j + 2 into the stage freed at the last barrier,
@@ -977,6 +994,27 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
     h8v qa[8];
     rotq(c.myq, qa);
     for (int j = jl0; j < nkt; ++j) step(j, qa, nullptr);  // local phase
+  } else if (kIE) {
+    h8v q[8];
+    rotq(PASS == PASS_IE_B ? remap_pos(c.myq, sq.G, a.cont) : (double)c.myq, q);
+    // one loop per segment, so each has its mask mode at compile time
+    auto step_ie = [&](int n, int j, auto mm) __attribute__((always_inline)) {
+      const bool ahead = n + 2 < nwalk;
+      if (ahead) {
+        const int tn = tile_of(n + 2);
+        tile_dma8(c, tn, rem_of(tn), kst(n + 2), vst(n + 2));
+      }
+      f32x16 s[2];
+      qk_lds(c, kst(n), q, st.negm, s);
+      softmax_pv_any(c, j, decltype(mm)::value, vst(n), s, st);
+      pair_sync(ahead);
+    };
+    for (int n = 0; n < n1; ++n)
+      step_ie(n, j_nr + n, std::integral_constant<int, MASK_WINDOW>{});
+    for (int n = n1; n < n1 + n2; ++n)
+      step_ie(n, j_nr + (n - n1), std::integral_constant<int, MASK_REMOTE>{});
+    for (int n = n1 + n2; n < nwalk; ++n)
+      step_ie(n, n - n1 - n2, std::integral_constant<int, MASK_NONE>{});
   } else {
     h8v qa[8];
     rotq(c.myq, qa);
@@ -988,17 +1026,28 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!qvalid) return;
   const int64_t row = (int64_t)(sq.start + c.myq - a.qoff);
-  uint16_t* op = (uint16_t*)a.o + (row * Hq + head) * PF_D;
+  if constexpr (kIE) {  // Eq. 7 passes keep float32 partial outputs
+    float* op = (float*)a.o + (row * Hq + head) * PF_D;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const uint32_t lo = (uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 2] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 3] * inv) << 16);
-      *(uint2*)(op + 32 * db + 8 * r4 + 4 * c.hh) = make_uint2(lo, hi);
-    }
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(float4*)(op + 32 * db + 8 * r4 + 4 * c.hh) =
+            make_float4(st.acc[db][4 * r4] * inv, st.acc[db][4 * r4 + 1] * inv,
+                        st.acc[db][4 * r4 + 2] * inv, st.acc[db][4 * r4 + 3] * inv);
+  } else {
+    uint16_t* op = (uint16_t*)a.o + (row * Hq + head) * PF_D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 2] * inv) |
+                            ((uint32_t)f32_to_bf16_bits(st.acc[db][4 * r4 + 3] * inv) << 16);
+        *(uint2*)(op + 32 * db + 8 * r4 + 4 * c.hh) = make_uint2(lo, hi);
+      }
+  }
   if (a.lse && c.hh == 0) {
     const float lse = l_tot > 0.f ? (st.m + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
     a.lse[(int64_t)head * a.T + row] = lse;
@@ -1033,12 +1082,22 @@ hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, in
   (void)scale;  // the score scale is carried by the key operands (pre-pass)
   a.fr = fr;
   const int64_t blocks = lay.max_tiles * Hq;
-  if ((pass == PASS_FUSED || pass == PASS_PLAIN) && (Hq / Hkv) % 2 == 0) {
+  if ((Hq / Hkv) % 2 == 0) {
     const dim3 grid((unsigned)(lay.max_tiles * (Hq / 2)));
-    if (pass == PASS_FUSED)
-      hipLaunchKernelGGL(prefill_pair_kernel<PASS_FUSED>, grid, dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL(prefill_pair_kernel<PASS_PLAIN>, grid, dim3(512), 0, st, a);
+    switch (pass) {
+      case PASS_FUSED:
+        hipLaunchKernelGGL(prefill_pair_kernel<PASS_FUSED>, grid, dim3(512), 0, st, a);
+        break;
+      case PASS_PLAIN:
+        hipLaunchKernelGGL(prefill_pair_kernel<PASS_PLAIN>, grid, dim3(512), 0, st, a);
+        break;
+      case PASS_IE_A:
+        hipLaunchKernelGGL(prefill_pair_kernel<PASS_IE_A>, grid, dim3(512), 0, st, a);
+        break;
+      default:  // passes B and C share one instantiation
+        hipLaunchKernelGGL(prefill_pair_kernel<PASS_IE_B>, grid, dim3(512), 0, st, a);
+        break;
+    }
     return hipGetLastError();
   }
   switch (pass) {

@@ -215,6 +215,30 @@ def test_prefill_varlen_small(dtype):
             s += n
 
 
+def test_prefill_varlen_max_sequences():
+    """The largest packed batch the boundary accepts: 4096 sequences of 0..48
+    tokens (every 97th empty), each with its own G (1..6). The plan kernel's
+    per-sequence arrays and its sort are full. Compared over all rows."""
+    rng = np.random.default_rng(4096)
+    lens = rng.integers(0, 49, 4096)
+    lens[::97] = 0
+    Hq, Hkv, w0, w_pre, theta = 4, 2, 5, 8, 1e6
+    T = int(lens.sum())
+    cu_h = np.cumsum([0] + list(lens))
+    xq, xk, v, _ = make_qkv(4097, T, Hq, Hkv, 128, dtype="bf16")
+    cu = torch.tensor(cu_h, dtype=torch.int32, device="cuda")
+    for mode in ("fused", "plain"):
+        note(f"varlen 4096 sequences mode={mode} T={T}")
+        ref = bifocal_varlen(xq, xk, v, cu_h, BIG if mode == "plain" else w0, w_pre, theta)
+        o_ref = np.concatenate([O for _, O, _ in ref if O.shape[0]], axis=0)
+        l_ref = np.concatenate([L for _, _, L in ref if L.shape[-1]], axis=1)
+        o, lse = jl.bifocal_prefill(to_dev(xq), to_dev(xk), to_dev(v), w0, w_pre, theta,
+                                    mode=mode, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        assert_bf16_close(to_host(o), o_ref, f"4096 sequences {mode}")
+        assert errs(to_host(lse), l_ref)[0] <= BF16_LSE_ABS
+
+
 def test_kcache_out_equals_rope_apply_and_inputs_untouched():
     L, Hq, Hkv, theta = 1000, 4, 2, 1e6
     xq, xk, v, _ = make_qkv(5001, L, Hq, Hkv, 128)

@@ -11,7 +11,7 @@ import torch
 
 import rope_context_extension_jl_amd as jl
 from oracle import decode_batch, group_size
-from synth_inputs import make_decode_seq, packed_starts
+from synth_inputs import make_decode_seq, make_qkv, packed_starts
 from tests._gpu_common import (BF16_LSE_ABS, FP32_LSE_ABS, assert_bf16_close, assert_f32_close,
                                errs, note, to_dev, to_host)
 
@@ -184,6 +184,42 @@ def test_decode_batch_many_sequences():
         if pos_b[i] + st_b[i] >= rows or st_b[i] < 0:
             assert np.isnan(oh[i]).all() and np.isnan(lh[i]).all(), i
     sample = sorted(set(rng.choice([i for i in range(B) if i not in bad], 120, replace=False)))
+    ro, rl = decode_batch(xq[sample], k_rows, v_rows, [pos[i] for i in sample],
+                          [starts[i] for i in sample], w0, w_pre, theta)
+    assert_bf16_close(oh[sample], ro, f"decode_batch B={B} sample")
+    assert errs(lh[sample], rl)[0] <= BF16_LSE_ABS
+
+
+def test_decode_batch_max_sequences():
+    """The largest batch the boundary accepts: B = 65535 sequences with caches
+    of 1 .. 16 keys packed back to back, every 997th entry invalid (its start
+    past the buffer); all invalid entries and a sample of the rest checked."""
+    w0, w_pre, theta, Hq, Hkv, d = 3, 4, 1e6, 2, 1, 64
+    rng = np.random.default_rng(65535)
+    B = 65535
+    pos = [int(p) for p in rng.integers(0, 16, B)]
+    starts, rows = packed_starts(pos)
+    _, k_rows, v_rows, _ = make_qkv(65536, rows, 1, Hkv, d, dtype="bf16")
+    xq, _, _, _ = make_qkv(65537, B, Hq, 1, d, dtype="bf16")
+    kc = to_dev(k_rows)
+    jl.rope_apply(kc, theta, cu_seqlens=torch.tensor(starts + [rows], dtype=torch.int32,
+                                                     device="cuda"))
+    bad = list(range(0, B, 997))
+    st_b = list(starts)
+    for i in bad:
+        st_b[i] = rows  # past the buffer
+    note(f"decode_batch B={B} rows={rows}")
+    o, lse = jl.bifocal_decode_batch(to_dev(xq), kc, to_dev(v_rows),
+                                     torch.tensor(pos, dtype=torch.int32, device="cuda"),
+                                     torch.tensor(st_b, dtype=torch.int32, device="cuda"), 16,
+                                     w0, w_pre, theta)
+    torch.cuda.synchronize()
+    oh, lh = to_host(o), to_host(lse)
+    for i in bad:
+        assert np.isnan(oh[i]).all() and np.isnan(lh[i]).all(), i
+    good = np.setdiff1d(np.arange(B), bad)
+    sample = sorted(set(rng.choice(good, 200, replace=False).tolist()) | {int(good[0]),
+                                                                         int(good[-1])})
     ro, rl = decode_batch(xq[sample], k_rows, v_rows, [pos[i] for i in sample],
                           [starts[i] for i in sample], w0, w_pre, theta)
     assert_bf16_close(oh[sample], ro, f"decode_batch B={B} sample")

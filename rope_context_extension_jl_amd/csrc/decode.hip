@@ -406,12 +406,13 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
   using G = DecGeom<D>;
   constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
   // ---- cos / sin of the correction R_{f(k) - k} of the lane's key in both
-  // blocks (pairs (ds, ds + NDS/2), frequencies 32 ds + 8 g16 + j), packed as
-  // fp16 pairs. They depend on the key index only, so they are computed
+  // blocks (pairs (ds, ds + NDS/2), frequencies 32 ds + 8 g16 + j), as fp16
+  // pairs of neighbouring frequencies (j, j + 1), the layout of the key
+  // fragments. They depend on the key index only, so they are computed
   // before the chunk's data is first touched, i.e. while its loads (and the
   // next chunk's) are still in flight.
   typedef _Float16 dh2v __attribute__((ext_vector_type(2)));
-  dh2v rot[2][NDS / 2][8];
+  dh2v rc[2][NDS / 2][4], rs[2][NDS / 2][4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = k0 + 16 * kb + c.r16;
@@ -420,10 +421,12 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float cs, sn;
-          rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + j], cs, sn);
-          rot[kb][ds][j] = dh2v{(_Float16)cs, (_Float16)sn};
+        for (int m = 0; m < 4; ++m) {
+          float c0, s0, c1, s1;
+          rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m], c0, s0);
+          rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m + 1], c1, s1);
+          rc[kb][ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
+          rs[kb][ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
         }
     }
   }
@@ -439,15 +442,24 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
     const int key = kfirst + c.r16;
     dh8v kf[NDS];
     if (c.correct && c.pos - key > c.w0) {
-      // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2)
+      // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2),
+      // in packed fp16 arithmetic on two neighbouring frequencies at a time
+      // (the bf16 key values are exact in fp16)
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float cs = (float)rot[kb][ds][j][0], sn = (float)rot[kb][ds][j][1];
-          const float x0 = bf16_lane(b.k[kb][ds], j), x1 = bf16_lane(b.k[kb][ds + NDS / 2], j);
-          kf[ds][j] = (_Float16)(x0 * cs - x1 * sn);
-          kf[ds + NDS / 2][j] = (_Float16)(x0 * sn + x1 * cs);
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t w0 = b.k[kb][ds][m], w1 = b.k[kb][ds + NDS / 2][m];
+          const dh2v x0 = {(_Float16)__uint_as_float(w0 << 16),
+                           (_Float16)__uint_as_float(w0 & 0xffff0000u)};
+          const dh2v x1 = {(_Float16)__uint_as_float(w1 << 16),
+                           (_Float16)__uint_as_float(w1 & 0xffff0000u)};
+          const dh2v y0 = x0 * rc[kb][ds][m] - x1 * rs[kb][ds][m];
+          const dh2v y1 = x0 * rs[kb][ds][m] + x1 * rc[kb][ds][m];
+          kf[ds][2 * m] = y0[0];
+          kf[ds][2 * m + 1] = y0[1];
+          kf[ds + NDS / 2][2 * m] = y1[0];
+          kf[ds + NDS / 2][2 * m + 1] = y1[1];
         }
     } else {
 #pragma unroll

@@ -278,6 +278,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
 // scores), so the common chunk needs no row max and no cross-lane exchange.
 // ---------------------------------------------------------------------------
 typedef _Float16 dh8v __attribute__((ext_vector_type(8)));
+typedef _Float16 dh2v __attribute__((ext_vector_type(2)));
 typedef __bf16 db8v __attribute__((ext_vector_type(8)));
 typedef __bf16 db2v __attribute__((ext_vector_type(2)));
 typedef short ds4v __attribute__((ext_vector_type(4)));
@@ -402,7 +403,9 @@ template <int D>
 __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<D>& b,
                                           const dh8v (&qa)[D / 32], const dh8v (&qr)[D / 32],
                                           const double* w2pi, const uint8_t* vb,
-                                          DecState<D>& st) {
+                                          DecState<D>& st, bool step16,
+                                          const dh2v (&cst)[D / 64][4],
+                                          const dh2v (&sst)[D / 64][4]) {
   using G = DecGeom<D>;
   constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
   // ---- cos / sin of the correction R_{f(k) - k} of the lane's key in both
@@ -411,23 +414,34 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
   // fragments. They depend on the key index only, so they are computed
   // before the chunk's data is first touched, i.e. while its loads (and the
   // next chunk's) are still in flight.
-  typedef _Float16 dh2v __attribute__((ext_vector_type(2)));
   dh2v rc[2][NDS / 2][4], rs[2][NDS / 2][4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = k0 + 16 * kb + c.r16;
     if (c.correct && c.pos - (k0 + 16 * kb) > c.w0) {  // the block has remote keys
-      const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
+      if (kb == 1 && step16) {
+        // key + 16 (block 0 is remote too): the angle moves by a fixed step,
+        // R_{d + c16} = R_d R_{c16}
 #pragma unroll
-      for (int ds = 0; ds < NDS / 2; ++ds)
+        for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          float c0, s0, c1, s1;
-          rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m], c0, s0);
-          rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m + 1], c1, s1);
-          rc[kb][ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
-          rs[kb][ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
-        }
+          for (int m = 0; m < 4; ++m) {
+            rc[1][ds][m] = rc[0][ds][m] * cst[ds][m] - rs[0][ds][m] * sst[ds][m];
+            rs[1][ds][m] = rs[0][ds][m] * cst[ds][m] + rc[0][ds][m] * sst[ds][m];
+          }
+      } else {
+        const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
+#pragma unroll
+        for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            float c0, s0, c1, s1;
+            rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m], c0, s0);
+            rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m + 1], c1, s1);
+            rc[kb][ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
+            rs[kb][ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
+          }
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -553,7 +567,7 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
 // One work unit of the bf16 decode for one wave: keys [s kps, (s + 1) kps)
 // of KV head kvh of sequence sq, leaving the partial of each query head of
 // the group. vA / vB: this wave's two V stages.
-template <int D>
+template <int D, bool STEP16>
 __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int s, int kvh,
                                          const double* w2pi_s, uint8_t* sA, uint8_t* sB) {
   using G = DecGeom<D>;
@@ -613,6 +627,25 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   c.g16 = g16;
   c.r16 = r16;
 
+  // With G dividing 16 (floor map) or the continuous map, f(k) - k moves by
+  // the same c16 from key k to key k + 16, so a chunk's second block takes
+  // its cos/sin from the first by one rotation R_{c16}.
+  const bool step16 = STEP16 && c.correct && (c.cont || 16 % c.G == 0);
+  dh2v cst[NDS / 2][4], sst[NDS / 2][4];
+  if (step16) {
+    const double c16 = c.cont ? 16.0 * c.fk_rel : (double)(16 / c.G - 16);
+#pragma unroll
+    for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float c0, s0, c1, s1;
+        rope_cs_turns(c16, w2pi_s[32 * ds + 8 * g16 + 2 * m], c0, s0);
+        rope_cs_turns(c16, w2pi_s[32 * ds + 8 * g16 + 2 * m + 1], c1, s1);
+        cst[ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
+        sst[ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
+      }
+  }
+
   DecState<D> st;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) st.acc[db] = df32x4{0.f, 0.f, 0.f, 0.f};
@@ -632,12 +665,12 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
     dec_issue_k<D>(c, k0 + DEC_CHUNK, bB);
     dec_issue_v<D>(c, k0 + DEC_CHUNK, sB);
     __builtin_amdgcn_sched_barrier(0);  // all of the next chunk's loads go out first
-    dec_chunk<D>(c, k0, bA, qa, qr, w2pi_s, sA, st);
+    dec_chunk<D>(c, k0, bA, qa, qr, w2pi_s, sA, st, step16, cst, sst);
     if (k0 + DEC_CHUNK >= c.k_hi) break;
     dec_issue_k<D>(c, k0 + 2 * DEC_CHUNK, bA);
     dec_issue_v<D>(c, k0 + 2 * DEC_CHUNK, sA);
     __builtin_amdgcn_sched_barrier(0);
-    dec_chunk<D>(c, k0 + DEC_CHUNK, bB, qa, qr, w2pi_s, sB, st);
+    dec_chunk<D>(c, k0 + DEC_CHUNK, bB, qa, qr, w2pi_s, sB, st, step16, cst, sst);
     if (k0 + 2 * DEC_CHUNK >= c.k_hi) break;
     k0 += 2 * DEC_CHUNK;
   }
@@ -687,7 +720,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   const int s = blockIdx.x / hgroups, kvh = (blockIdx.x % hgroups) * 4 + wave;
   if (kvh >= a.Hkv) return;
   const DecSeq sq = dec_seq<false>(a, 0, D, 2);
-  dec_unit<D>(a, sq, s, kvh, w2pi_s, vstA[wave], vstB[wave]);
+  dec_unit<D, true>(a, sq, s, kvh, w2pi_s, vstA[wave], vstB[wave]);
 }
 
 // Batch: a fixed grid of workgroups walks the work list the plan kernel
@@ -716,7 +749,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, co
       if (base[mid] <= item) lo = mid; else hi = mid - 1;
     }
     const DecSeq sq = dec_seq<true>(a, lo, D, 2);
-    dec_unit<D>(a, sq, item - base[lo], kvh, w2pi_s, vstA[wave], vstB[wave]);
+    // (the batch kernel has no registers to spare for the step table)
+    dec_unit<D, false>(a, sq, item - base[lo], kvh, w2pi_s, vstA[wave], vstB[wave]);
   }
 }
 

@@ -131,8 +131,11 @@ def test_decode_batch_shared_prefix_and_invalid_entries():
 
 def test_decode_batch_split_invariance_and_single_agreement():
     """num_splits changes only the LSE merge order; each entry agrees with the
-    single-sequence entry point on its own cache slice (bitwise when the
-    plans match: one sequence whose max_keys is its own pos + 1)."""
+    single-sequence entry point on its own cache slice: bitwise when the
+    plans match (one sequence whose max_keys is its own pos + 1) and both
+    evaluate every correction angle directly; to rounding when G divides 16,
+    where the single-sequence kernel derives a chunk's second 16-key block of
+    angles from its first by a fixed rotation."""
     w0, w_pre, theta, Hq, Hkv, d = 100, 512, 1e6, 8, 2, 128
     pos = [2500, 1023, 1024, 7]
     xq, k_rows, v_rows, starts, kc, vc, pos_t, st_t, _ = _batch(8500, pos, Hq, Hkv, d, theta,
@@ -155,7 +158,14 @@ def test_decode_batch_split_invariance_and_single_agreement():
         single, ls = jl.bifocal_decode(to_dev(xq[b]), kc[s0:s0 + p + 1], vc[s0:s0 + p + 1], p,
                                        w0, w_pre, theta)
         torch.cuda.synchronize()
-        assert torch.equal(one[0], single) and torch.equal(l1[0], ls)
+        G = group_size(p + 1, w_pre)
+        if G == 1 or 16 % G:
+            assert torch.equal(one[0], single) and torch.equal(l1[0], ls)
+        else:
+            d_o = np.abs(to_host(one[0]) - to_host(single)).max()
+            d_l = np.abs(to_host(l1[0]) - to_host(ls)).max()
+            note(f"B=1 vs single pos={p} G={G}: |dO| {d_o:.3e} |dLSE| {d_l:.3e}")
+            assert d_o <= 4e-3 and d_l <= 1e-3
 
 
 def test_decode_batch_many_sequences():

@@ -521,13 +521,23 @@ __device__ __forceinline__ float max_with_partner(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+__device__ __forceinline__ void reference_pv(const Tctx& c, const uint16_t* vs, f32x16 (&s)[2],
+                                             b8v (&pb)[4], float psum, RowState& st);
+
 __device__ __forceinline__ void softmax_pv_any(const Tctx& c, int j, int mask_mode,
                                                const uint16_t* vs, f32x16 (&s)[2],
                                                RowState& st) {
   const int cls = tile_cls_of(c, j);
   if (tile_needs_mask(c, j, cls, mask_mode)) mask_scores(c, j, cls, mask_mode, s);
   b8v pb[4];
-  float psum = exp_pack(s, pb);
+  const float psum = exp_pack(s, pb);
+  reference_pv(c, vs, s, pb, psum, st);
+}
+
+// After the exp: move the reference where a row needs it (rare), then the
+// row sum and O^T += V^T P^T.
+__device__ __forceinline__ void reference_pv(const Tctx& c, const uint16_t* vs, f32x16 (&s)[2],
+                                             b8v (&pb)[4], float psum, RowState& st) {
   const bool need = !(psum <= kSumMax) || st.m == -INFINITY;
   if (__any(need)) {
     // Rare: move the reference of the rows that need it to their tile max.
@@ -566,6 +576,59 @@ __device__ __forceinline__ void softmax_pv_any(const Tctx& c, int j, int mask_mo
       st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           *(const b8v*)(vrow + 8 * ((2 * ks + c.hh) ^ y)), pb[ks], st.acc[db], 0, 0, 0);
   }
+}
+
+// An all-remote tile (no mask can apply): the two 32-key blocks are scored
+// one after the other, and the exp of the first block is interleaved with
+// the second block's MFMAs, so the wave's VALU work overlaps its own matrix
+// work. Same operations, in the same order per value, as qk_lds followed by
+// softmax_pv_any.
+__device__ __forceinline__ void tile_remote(const Tctx& c, const uint16_t* ks, const uint16_t* vs,
+                                            const h8v (&q)[8], RowState& st) {
+  const int x = kswz(c.l32);
+  f32x16 s[2];
+  auto chain = [&](int bk) __attribute__((always_inline)) {
+    const uint16_t* krow = ks + (32 * bk + c.l32) * PF_D;
+    s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 8 * (c.hh ^ x)), q[0],
+                                                   st.negm, 0, 0, 0);
+#pragma unroll
+    for (int cc = 1; cc < 8; ++cc)
+      s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          *(const h8v*)(krow + 8 * ((2 * cc + c.hh) ^ x)), q[cc], s[bk], 0, 0, 0);
+  };
+  const b2v one = {(__bf16)1.f, (__bf16)1.f};
+  b8v pb[4];
+  float ps0 = 0.f, ps1 = 0.f;
+  auto expb = [&](int bk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      pb[2 * bk + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(s[bk][r]);
+#pragma unroll
+    for (int ks2 = 2 * bk; ks2 < 2 * bk + 2; ++ks2) {
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks2], pb[ks2], 0, 1), one,
+                                            ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks2], pb[ks2], 2, 3), one,
+                                            ps1, false);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks2], pb[ks2], 4, 5), one,
+                                            ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks2], pb[ks2], 6, 7), one,
+                                            ps1, false);
+    }
+  };
+  chain(0);
+  __builtin_amdgcn_sched_barrier(0);
+  // block 1's reads and MFMAs, each MFMA followed by a share of block 0's exp
+  chain(1);
+  expb(0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  expb(1);
+  reference_pv(c, vs, s, pb, ps0 + ps1, st);
 }
 
 // One key tile from stage (kc, vc) while the next one (if any) streams into
@@ -980,11 +1043,17 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
     softmax_pv_any(c, j, MASK_NONE, vst(j), s, st);
     pair_sync(ahead);
   };
+  auto step_remote = [&](int j, const h8v (&q)[8]) __attribute__((always_inline)) {
+    const bool ahead = j + 2 < nkt;
+    if (ahead) tile_dma8(c, j + 2, rem_of(j + 2), kst(j + 2), vst(j + 2));
+    tile_remote(c, kst(j), vst(j), q, st);
+    pair_sync(ahead);
+  };
   if (PASS == PASS_FUSED) {
     {
       h8v qr[8];
       rotq(remap_pos(c.myq, sq.G, a.cont), qr);
-      for (int j = 0; j < j_nr; ++j) step(j, qr, nullptr);  // remote phase
+      for (int j = 0; j < j_nr; ++j) step_remote(j, qr);  // remote phase
       if (j_nr < j_loc) {                                    // boundary phase
         h8v qa[8];
         rotq(c.myq, qa);

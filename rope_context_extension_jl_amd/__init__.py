@@ -139,6 +139,36 @@ def _dev(t: Optional[torch.Tensor], name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _want(t: Optional[torch.Tensor], name: str, shape, dtype, device=None) -> None:
+    """Raise ValueError unless t (when given) has this shape, dtype and device.
+    The C ABI sees bare pointers, so a mismatch it cannot detect (a float32
+    key tensor beside bfloat16 queries, an int64 cu_seqlens) is caught here,
+    before anything is launched."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _want_cu(cu: Optional[torch.Tensor], name: str, device) -> int:
+    """Number of sequences described by an int32 [B + 1] prefix-offset tensor."""
+    if cu is None:
+        return 1
+    if cu.dim() != 1 or cu.numel() < 2:
+        raise ValueError(f"{name} must be a 1-D tensor of B + 1 >= 2 offsets")
+    _want(cu, name, (cu.numel(),), torch.int32, device)
+    return cu.numel() - 1
+
+
+def _want_rank(t: torch.Tensor, name: str, rank: int) -> None:
+    if t.dim() != rank:
+        raise ValueError(f"{name} must have {rank} dimensions, got shape {tuple(t.shape)}")
+
+
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -198,8 +228,10 @@ def decode_workspace_size(capacity, Hq, d) -> int:
 def rope_apply(x: torch.Tensor, theta: float, cu_seqlens: Optional[torch.Tensor] = None,
                pos_offset: int = 0) -> torch.Tensor:
     """In place: x[t, h, :] <- RoPE(x[t, h, :], position of t). x: [T, H, d]."""
+    _want_rank(x, "x", 3)
     T, H, d = x.shape
-    B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _dtype_code(x)
+    B = _want_cu(cu_seqlens, "cu_seqlens", x.device)
     st = lib().jl_rope_apply(_dev(x, "x"), T, H, d, _dev(cu_seqlens, "cu_seqlens"), B,
                              int(pos_offset), float(theta), _dtype_code(x), _stream(x.device))
     _check("jl_rope_apply", st)
@@ -216,9 +248,18 @@ def bifocal_prefill(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, w0: int
     events: optional (begin, end) torch.cuda.Event pair, recorded around the
     attention kernels only (jl_bifocal_prefill_timed). remap: "floor" or
     "continuous" (remote positions x / G as real numbers)."""
+    _want_rank(xq, "xq", 3)
+    _want_rank(xk, "xk", 3)
     T, Hq, d = xq.shape
     Hkv = xk.shape[1]
-    B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _dtype_code(xq)
+    dv = xq.device
+    _want(xk, "xk", (T, Hkv, d), xq.dtype, dv)
+    _want(v, "v", (T, Hkv, d), xq.dtype, dv)
+    _want(out, "out", (T, Hq, d), xq.dtype, dv)
+    _want(lse, "lse", (Hq, T), torch.float32, dv)
+    _want(kcache_out, "kcache_out", (T, Hkv, d), xq.dtype, dv)
+    B = _want_cu(cu_seqlens, "cu_seqlens", dv)
     if out is None:
         out = torch.empty_like(xq)
     if lse is None and want_lse:
@@ -252,8 +293,16 @@ def bifocal_prefill_cached(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch
     """Chunked prefill: RAW queries xq [Tq, Hq, d] at positions q_off .. q_off+Tq-1
     against the absolute cache [capacity, Hkv, d] (rows up to q_off+Tq-1 filled).
     Returns (o [Tq, Hq, d], lse [Hq, Tq])."""
+    _want_rank(xq, "xq", 3)
+    _want_rank(kcache, "kcache", 3)
     Tq, Hq, d = xq.shape
     C, Hkv, _ = kcache.shape
+    _dtype_code(xq)
+    dv = xq.device
+    _want(kcache, "kcache", (C, Hkv, d), xq.dtype, dv)
+    _want(vcache, "vcache", (C, Hkv, d), xq.dtype, dv)
+    _want(out, "out", (Tq, Hq, d), xq.dtype, dv)
+    _want(lse, "lse", (Hq, Tq), torch.float32, dv)
     if out is None:
         out = torch.empty_like(xq)
     if lse is None and want_lse:
@@ -277,8 +326,16 @@ def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                    want_lse: bool = True, events=None, remap: str = "floor"):
     """One decode step at `pos` with a RAW query xq [Hq, d] against the absolute
     cache [capacity, Hkv, d]. Returns (o [Hq, d], lse [Hq])."""
+    _want_rank(xq, "xq", 2)
+    _want_rank(kcache, "kcache", 3)
     Hq, d = xq.shape
     C, Hkv, _ = kcache.shape
+    _dtype_code(xq)
+    dv = xq.device
+    _want(kcache, "kcache", (C, Hkv, d), xq.dtype, dv)
+    _want(vcache, "vcache", (C, Hkv, d), xq.dtype, dv)
+    _want(out, "out", (Hq, d), xq.dtype, dv)
+    _want(lse, "lse", (Hq,), torch.float32, dv)
     if out is None:
         out = torch.empty_like(xq)
     if lse is None and want_lse:
@@ -311,11 +368,21 @@ def bifocal_decode_batch(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.T
     keys 0 .. positions[b] are rows cache_starts[b] + k of the shared cache
     [rows, Hkv, d]. positions / cache_starts: device int32 [B]; max_keys: a
     host bound on positions[b] + 1. Returns (o [B, Hq, d], lse [B, Hq])."""
+    _want_rank(xq, "xq", 3)
+    _want_rank(kcache, "kcache", 3)
     B, Hq, d = xq.shape
     C, Hkv, _ = kcache.shape
+    _dtype_code(xq)
+    dv = xq.device
+    _want(kcache, "kcache", (C, Hkv, d), xq.dtype, dv)
+    _want(vcache, "vcache", (C, Hkv, d), xq.dtype, dv)
+    _want(out, "out", (B, Hq, d), xq.dtype, dv)
+    _want(lse, "lse", (B, Hq), torch.float32, dv)
     for t, name in ((positions, "positions"), (cache_starts, "cache_starts")):
         if t.dtype != torch.int32 or t.numel() != B or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 tensor of {B} entries")
+        if t.device != dv:
+            raise ValueError(f"{name} must be on {dv}, got {t.device}")
     if out is None:
         out = torch.empty_like(xq)
     if lse is None and want_lse:

@@ -59,3 +59,19 @@ def brute_attention(xq, xk, v, w0, w_pre, theta, scale=None, positions=None, con
                 O[q][h][i] = sum(ws[k] * v[k][g][i] for k in range(q + 1)) / tot
             LSE[h][q] = m + math.log(tot)
     return O, LSE
+
+
+def brute_score(xq_row, q, xk_row, k, w0, G, theta, continuous=False):
+    """Unscaled score of Eq. 1 for ONE query vector at position q and ONE key
+    vector at position k (flat Python lists): the local route rotates at
+    (q, k) when q - k <= w0, the remote route at floor(q / G), floor(k / G)
+    (or q / G, k / G with continuous)."""
+    if q - k <= w0:
+        pq, pk = q, k
+    elif continuous:
+        pq, pk = q / G, k / G
+    else:
+        pq, pk = q // G, k // G
+    a = _rotate(list(xq_row), pq, theta)
+    b = _rotate(list(xk_row), pk, theta)
+    return sum(a[i] * b[i] for i in range(len(a)))

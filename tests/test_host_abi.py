@@ -191,6 +191,58 @@ def test_python_binding_refuses_cpu_tensors():
                            workspace=torch.zeros(1, dtype=torch.uint8))
 
 
+def test_python_binding_checks_shapes_and_dtypes():
+    """Mismatches the C ABI cannot see (bare pointers) raise ValueError in the
+    binding before anything is launched: a key or value tensor of another
+    dtype or shape than the queries, outputs of the wrong shape, an int64
+    cu_seqlens."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    T, Hq, Hkv, d = 8, 4, 2, 128
+    q = torch.zeros(T, Hq, d, dtype=bf)
+    k = torch.zeros(T, Hkv, d, dtype=bf)
+    ws = torch.zeros(1, dtype=torch.uint8)
+    args = (1, 4, 1e4)
+    cases = [
+        (dict(xk=k.float()), "xk must be"),
+        (dict(v=torch.zeros(T, Hkv + 1, d, dtype=bf)), "v must have shape"),
+        (dict(out=torch.zeros(T, Hq, d, dtype=f32)), "out must be"),
+        (dict(lse=torch.zeros(T, Hq, dtype=f32)), "lse must have shape"),
+        (dict(kcache_out=torch.zeros(T, Hkv, d // 2, dtype=bf)), "kcache_out must have shape"),
+        (dict(cu_seqlens=torch.tensor([0, 3, 8], dtype=torch.int64)), "cu_seqlens must be"),
+        (dict(cu_seqlens=torch.tensor([8], dtype=torch.int32)), "cu_seqlens must be a 1-D"),
+    ]
+    for kw, msg in cases:
+        xk = kw.pop("xk", k)
+        v = kw.pop("v", k)
+        with pytest.raises(ValueError, match=msg):
+            jl.bifocal_prefill(q, xk, v, *args, workspace=ws, **kw)
+    with pytest.raises(ValueError, match="cu_seqlens must be"):
+        jl.rope_apply(k, 1e4, cu_seqlens=torch.tensor([0, 8], dtype=torch.int64))
+    C = 16
+    kc = torch.zeros(C, Hkv, d, dtype=bf)
+    with pytest.raises(ValueError, match="vcache must have shape"):
+        jl.bifocal_decode(q[0], kc, kc[:8], 3, *args)
+    with pytest.raises(ValueError, match="kcache must be"):
+        jl.bifocal_decode(q[0], kc.float(), kc, 3, *args)
+    with pytest.raises(ValueError, match="out must have shape"):
+        jl.bifocal_decode(q[0], kc, kc, 3, *args, out=torch.zeros(Hq + 1, d, dtype=bf))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        jl.bifocal_decode(q[0], kc, kc, 3, *args, lse=torch.zeros(Hq, 1, dtype=f32))
+    with pytest.raises(ValueError, match="vcache must be"):
+        jl.bifocal_prefill_cached(q, kc, kc.float(), 0, *args)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        jl.bifocal_prefill_cached(q, kc, kc, 0, *args, lse=torch.zeros(T, Hq, dtype=f32))
+    pos = torch.zeros(2, dtype=torch.int32)
+    qb = torch.zeros(2, Hq, d, dtype=bf)
+    with pytest.raises(ValueError, match="out must have shape"):
+        jl.bifocal_decode_batch(qb, kc, kc, pos, pos, 4, *args, out=torch.zeros(3, Hq, d, dtype=bf))
+    with pytest.raises(ValueError, match="kcache must be"):
+        jl.bifocal_decode_batch(qb, kc.float(), kc, pos, pos, 4, *args)
+    with pytest.raises(ValueError, match="positions must be"):
+        jl.bifocal_decode_batch(qb, kc, kc, pos.long(), pos, 4, *args)
+
+
 def test_calibration_argument_errors():
     f, g = jl.lib().jl_calib_stream_read, jl.lib().jl_calib_mfma_bf16
     assert f(None, 1024, P, 16, None) == -1

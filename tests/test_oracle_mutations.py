@@ -45,6 +45,14 @@ MUTATIONS = {
     "batch_start_ignored": ("k_rows[s0:s0 + p + 1], v_rows[s0:s0 + p + 1]",
                             "k_rows[:p + 1], v_rows[:p + 1]"),
     "batch_bound_inclusive": ("s0 + p >= rows or", "s0 + p > rows or"),
+    "scores_window_strict": ("return np.where(dist <= w0, s_local, s_remote)",
+                             "return np.where(dist < w0, s_local, s_remote)"),
+    "scores_keys_not_remapped": ("kr = rope(xk, remap(k_pos, G, continuous), theta)",
+                                 "kr = rope(xk, k_pos, theta)"),
+    "scores_query_not_remapped": ("qr = rope(xq_rows, remap(q_pos, G, continuous), theta)",
+                                  "qr = rope(xq_rows, q_pos, theta)"),
+    "scores_routes_swapped": ("return np.where(dist <= w0, s_local, s_remote)",
+                              "return np.where(dist <= w0, s_remote, s_local)"),
 }
 
 

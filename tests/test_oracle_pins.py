@@ -16,7 +16,7 @@ import torch
 from oracle import (bifocal_attention, bifocal_scores, bifocal_varlen, decode_batch, decode_row,
                     group_size, ie_merge, ie_pass, remap, rope, rope_frequencies, tile_class,
                     tile_class_map)
-from tests._brute import brute_attention
+from tests._brute import brute_attention, brute_score
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -341,6 +341,26 @@ def test_shift_invariance_local_and_remote():
         np.testing.assert_allclose(r0, r1, atol=1e-10)
     r2 = bifocal_scores(xq, qp + 1, xk, kp + 1, -1, G, theta)
     assert np.abs(r2 - r0).max() > 1e-3
+
+
+@pytest.mark.parametrize("continuous", [False, True])
+def test_scores_match_scalar_brute_force(continuous):
+    """bifocal_scores element by element against the scalar definition of
+    Eq. 1 [Digest/Method, Eq. 1: local when q - k <= w0, else both vectors at
+    f(.)], on positions that put pairs at distances w0 - 1, w0, w0 + 1 and
+    far beyond, with G = 1, 2, 3 and keys after queries (the routing is
+    defined for any pair; the causal mask is applied elsewhere)."""
+    d, theta = 8, 1e4
+    xq, xk = _rand(41, 7, d), _rand(42, 9, d)
+    qp = np.array([0, 5, 6, 7, 12, 40, 41])
+    kp = np.array([0, 1, 2, 3, 4, 5, 6, 11, 39])
+    for G in (1, 2, 3):
+        for w0 in (0, 1, 3, 5):
+            s = bifocal_scores(xq, qp, xk, kp, w0, G, theta, continuous=continuous)
+            for i, q in enumerate(qp):
+                for j, k in enumerate(kp):
+                    ref = brute_score(xq[i], int(q), xk[j], int(k), w0, G, theta, continuous)
+                    assert abs(s[i, j] - ref) <= 1e-12 * max(1.0, abs(ref)), (G, w0, q, k)
 
 
 # ---------------------------------------------------------------- tile classes

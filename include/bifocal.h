@@ -112,6 +112,23 @@ size_t jl_prefill_workspace_size(int64_t T, int B, int Hq, int Hkv, int d, jl_dt
  * pass C can amplify rounding in that row (small values are benign). */
 size_t jl_prefill_ie_ratio_offset(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt);
 
+/* Range flags a bf16 prefill leaves in its workspace (read them with
+ * jl_prefill_flags). The QK^T operands are fp16: a rotated query, or a key
+ * times the score scale times log2(e), outside the fp16 range (|x| > 65504)
+ * becomes infinite and the affected rows come out NaN or wrong. The kernels
+ * detect it and set a bit; they neither stop nor fault. NaN inputs also set
+ * the bit of the operand they reach. */
+#define JL_FLAG_Q_RANGE 1 /* a rotated query operand was not a finite fp16 value */
+#define JL_FLAG_K_RANGE 2 /* a scaled key operand was not a finite fp16 value    */
+
+/* Reads the range flags (JL_FLAG_*) of the last jl_bifocal_prefill or
+ * jl_bifocal_prefill_cached call that used `workspace` (device memory) into
+ * *flags (host). Waits for `stream` to finish first, so call it on the stream
+ * of the prefill. Every bf16 prefill call clears the flags before its kernels
+ * run; fp32 calls (no 16-bit operands) leave them 0. Errors: JL_EINVAL (NULL
+ * pointer), JL_EHIP. */
+int jl_prefill_flags(const void* workspace, uint32_t* flags, void* stream);
+
 /* Causal bifocal attention over a packed batch (Eq. 1; Eq. 7 in IE mode).
  *   xq  [T, Hq, d]  RAW (not yet rotated) queries      bf16 | fp32
  *   xk  [T, Hkv, d] RAW keys                            bf16 | fp32
@@ -133,7 +150,9 @@ size_t jl_prefill_ie_ratio_offset(int64_t T, int B, int Hq, int Hkv, int d, jl_d
  * Range (bf16): the QK^T operands are fp16, the keys carrying the score scale
  * times log2(e), so rotated queries must stay below 65504 in magnitude and
  * keys below 65504 / (scale log2 e) (about 5.1e5 at d = 128); beyond that the
- * scores overflow to inf and no error is reported.
+ * scores overflow, the outputs of the affected rows are undefined (NaN or
+ * wrong) and the call sets JL_FLAG_Q_RANGE / JL_FLAG_K_RANGE in the workspace
+ * (jl_prefill_flags); the status returned is still JL_OK.
  * Workspace: jl_prefill_workspace_size(...) bytes of device memory, any
  * contents, 256-byte aligned; it holds the rotated key tiles, the transposed
  * values and the tile schedule. Errors: JL_EINVAL, JL_EUNSUPPORTED,
@@ -295,6 +314,16 @@ int jl_debug_tile_classes(int64_t L, int64_t w0, int8_t* out_dev, void* stream);
  * floats); one round is 4 * 32768 FLOP per wave. Both only launch on
  * `stream`; time them with the caller's events. JL_EINVAL on bad arguments. */
 int jl_calib_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream);
+/* The same streaming read by one of three kernels, so a caller can report the
+ * best read rate any of them reaches: variant 0 is jl_calib_stream_read
+ * (grid-stride 16-byte loads, four in flight per thread); 1 reads 32 KiB
+ * chunks per workgroup with eight nontemporal 16-byte loads in flight per
+ * thread; 2 moves 64 KiB chunks by direct global -> LDS transfers (sixteen
+ * 1 KiB transfers per wave), the path the bf16 decode streams its values
+ * through. Bytes past the last whole chunk are read by ordinary loads.
+ * JL_EINVAL on bad arguments or an unknown variant. */
+int jl_calib_stream_read_ex(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                            int variant, void* stream);
 int jl_calib_mfma_bf16(float* sink, int blocks, int iters, void* stream);
 
 /* Static English text for a status code; never NULL. */

@@ -19,7 +19,8 @@ __all__ = [
     "decode_workspace_size", "bifocal_decode", "debug_tile_classes", "ie_ratio_view",
     "prefill_cached_workspace_size", "bifocal_prefill_cached",
     "decode_batch_workspace_size", "bifocal_decode_batch",
-    "calib_stream_read", "calib_mfma_bf16", "MODES", "REMAPS",
+    "calib_stream_read", "calib_mfma_bf16", "MODES", "REMAPS", "prefill_flags",
+    "FLAG_Q_RANGE", "FLAG_K_RANGE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbifocal.so")
@@ -75,8 +76,10 @@ _SIGS = {
                                                _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_i64,
                                                _c_i64, _c_dbl, _c_flt, _c_int, _c_int, _c_int,
                                                _c_p, _c_sz, _c_p, _c_p, _c_p]),
+    "jl_prefill_flags": (_c_int, [_c_p, ctypes.POINTER(ctypes.c_uint32), _c_p]),
     "jl_debug_tile_classes": (_c_int, [_c_i64, _c_i64, _c_p, _c_p]),
     "jl_calib_stream_read": (_c_int, [_c_p, _c_sz, _c_p, _c_int, _c_p]),
+    "jl_calib_stream_read_ex": (_c_int, [_c_p, _c_sz, _c_p, _c_int, _c_int, _c_p]),
     "jl_calib_mfma_bf16": (_c_int, [_c_p, _c_int, _c_int, _c_p]),
     "jl_status_string": (ctypes.c_char_p, [_c_int]),
     "jl_last_hip_error": (_c_int, []),
@@ -276,6 +279,19 @@ def bifocal_prefill(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, w0: int
     return out, lse
 
 
+FLAG_Q_RANGE, FLAG_K_RANGE = 1, 2
+
+
+def prefill_flags(workspace: torch.Tensor) -> int:
+    """Range flags (FLAG_Q_RANGE | FLAG_K_RANGE) the last prefill left in
+    `workspace`; waits for the current stream (jl_prefill_flags)."""
+    out = ctypes.c_uint32(0)
+    _check("jl_prefill_flags", lib().jl_prefill_flags(_dev(workspace, "workspace"),
+                                                       ctypes.byref(out),
+                                                       _stream(workspace.device)))
+    return int(out.value)
+
+
 def ie_ratio_view(workspace: torch.Tensor, T, B, Hq, Hkv, d, dtype=torch.bfloat16):
     """[Hq, T] float32 view of the Eq. 7 cancellation ratios an IE prefill left
     in `workspace`."""
@@ -409,16 +425,18 @@ def debug_tile_classes(L: int, w0: int, device="cuda") -> torch.Tensor:
     return out
 
 
-def calib_stream_read(buf: torch.Tensor, events=None, blocks: int = 2048) -> None:
-    """One streaming read of `buf` (device) by the calibration kernel; the
+def calib_stream_read(buf: torch.Tensor, events=None, blocks: int = 2048,
+                      variant: int = 0) -> None:
+    """One streaming read of `buf` (device) by calibration kernel `variant`
+    (0 grid-stride, 1 nontemporal chunks, 2 direct-to-LDS chunks); the
     optional (begin, end) events bracket it on the current stream."""
     sink = torch.empty(1, dtype=torch.int32, device=buf.device)
     s = torch.cuda.current_stream(buf.device)
     if events is not None:
         events[0].record(s)
-    _check("jl_calib_stream_read", lib().jl_calib_stream_read(
+    _check("jl_calib_stream_read_ex", lib().jl_calib_stream_read_ex(
         _dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"), int(blocks),
-        _stream(buf.device)))
+        int(variant), _stream(buf.device)))
     if events is not None:
         events[1].record(s)
 

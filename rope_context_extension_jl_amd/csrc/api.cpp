@@ -213,6 +213,18 @@ int jl_bifocal_prefill(const void* xq, const void* xk, const void* v, void* o, f
                                   nullptr, nullptr);
 }
 
+int jl_prefill_flags(const void* workspace, uint32_t* flags, void* stream) {
+  if (!workspace || !flags) return JL_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, (const char*)workspace + kHdrFlags * sizeof(int),
+                                sizeof(v), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e);
+  *flags = v;
+  return JL_OK;
+}
+
 // ---- prefill continued on an existing absolute cache
 static bool cached_shape_ok(int64_t q_off, int64_t Tq, int Hq, int Hkv) {
   if (q_off < 0 || Tq < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv) return false;
@@ -473,11 +485,17 @@ int jl_debug_tile_classes(int64_t L, int64_t w0, int8_t* out_dev, void* stream) 
   return hip_status(launch_tile_dump(L, w0, out_dev, (hipStream_t)stream));
 }
 
-int jl_calib_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
-                         void* stream) {
+int jl_calib_stream_read_ex(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                            int variant, void* stream) {
   if (!src || !sink || bytes < 16 || (bytes & 15) || (((uintptr_t)src) & 15) || blocks < 1)
     return JL_EINVAL;
-  return hip_status(launch_calib_read(src, bytes, sink, blocks, (hipStream_t)stream));
+  if (variant < 0 || variant > 2) return JL_EINVAL;
+  return hip_status(launch_calib_read(src, bytes, sink, blocks, variant, (hipStream_t)stream));
+}
+
+int jl_calib_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                         void* stream) {
+  return jl_calib_stream_read_ex(src, bytes, sink, blocks, 0, stream);
 }
 
 int jl_calib_mfma_bf16(float* sink, int blocks, int iters, void* stream) {

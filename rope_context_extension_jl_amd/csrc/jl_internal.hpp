@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bifocal.h"
+
 namespace jl {
 
 // ---------------------------------------------------------------------------
@@ -38,6 +40,10 @@ struct RopeFreqs {
   __host__ __device__ double w(int i) const { return exp2((double)i * nl2t); }
 };
 void make_freqs(RopeFreqs& f, int d, double theta);
+
+// Word of the prefill workspace header (int32 index) that holds the range
+// flags of the last call (JL_FLAG_* of bifocal.h); the plan kernel clears it.
+constexpr int kHdrFlags = 3;
 
 // Per-sequence record built on the device by the plan kernel.
 struct SeqInfo {
@@ -122,8 +128,11 @@ hipError_t launch_decode_batch(const void* xq, const void* kc, const void* vc, v
 
 hipError_t launch_tile_dump(int64_t L, int64_t w0, int8_t* out, hipStream_t st);
 
+// variant 0: grid-stride 16-byte loads, 4 in flight per thread; 1: 32 KiB
+// chunks per workgroup, 8 nontemporal loads in flight per thread; 2: 64 KiB
+// chunks by direct global -> LDS transfers.
 hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
-                             hipStream_t st);
+                             int variant, hipStream_t st);
 hipError_t launch_calib_mfma(float* sink, int blocks, int iters, hipStream_t st);
 
 // ---------------------------------------------------------------------------
@@ -179,6 +188,10 @@ __device__ inline uint16_t f32_to_bf16_bits(float x) {
 __device__ inline uint16_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;  // round to nearest even
   return __builtin_bit_cast(uint16_t, h);
+}
+// 1 when the fp16 bit pattern is an infinity or a NaN (all exponent bits set).
+__device__ __forceinline__ uint32_t f16_nonfinite(uint16_t b) {
+  return (b & 0x7c00u) == 0x7c00u ? 1u : 0u;
 }
 #endif
 

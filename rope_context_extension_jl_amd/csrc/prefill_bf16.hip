@@ -70,7 +70,8 @@ __device__ __forceinline__ int vperm(int q) {
 //   tbase[t]  = sum of tact[t'] over t' > t
 // Slot s of the schedule is tile depth t (smallest t with tbase[t] <= s) of
 // sequence order[s - tbase[t]]: deepest (heaviest) tiles first.
-// hdr[0] = number of tiles, hdr[1] = deepest tile count, hdr[2] = padded rows.
+// hdr[0] = number of tiles, hdr[1] = deepest tile count, hdr[2] = padded rows,
+// hdr[3] = range flags of this call (cleared here, OR-ed by the later kernels).
 // ---------------------------------------------------------------------------
 constexpr int PLAN_THREADS = 1024;
 
@@ -103,7 +104,10 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(
   __shared__ int sh[PLAN_THREADS + 1];
   __shared__ int maxnt_s;
   const int tid = threadIdx.x;
-  if (tid == 0) maxnt_s = 0;
+  if (tid == 0) {
+    maxnt_s = 0;
+    hdr[kHdrFlags] = 0;
+  }
   __syncthreads();
   for (int b = tid; b < B; b += PLAN_THREADS) {
     const int s = cu ? cu[b] : 0;
@@ -206,10 +210,11 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
     const uint16_t* __restrict__ xk, const uint16_t* __restrict__ v, uint16_t* __restrict__ kcache,
     const SeqInfo* __restrict__ seqs, const int* __restrict__ hdr, int B, int Hkv, int R,
     int need_rem, int from_abs, float kscale, int cont, uint16_t* __restrict__ kabs,
-    uint16_t* __restrict__ krem, uint16_t* __restrict__ vt, RopeFreqs fr) {
+    uint16_t* __restrict__ krem, uint16_t* __restrict__ vt, RopeFreqs fr, int* __restrict__ flags) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * (PF_D + 8)];
   const int r0 = blockIdx.x * 64;
   if (r0 >= hdr[2]) return;
+  uint32_t nonfinite = 0;  // OR of (fp16 bits & 0x7c00) == 0x7c00 over the key operands
   const int b = seq_of_padded_row(seqs, B, r0);
   const SeqInfo sq = seqs[b];
   const int tid = threadIdx.x;
@@ -250,7 +255,9 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
         if (need_rem) {
           ra[j] = f32_to_f16_bits((x0 * cr[j] - x1 * sr[j]) * kscale);
           rb[j] = f32_to_f16_bits((x0 * sr[j] + x1 * cr[j]) * kscale);
+          nonfinite |= f16_nonfinite(ra[j]) | f16_nonfinite(rb[j]);
         }
+        nonfinite |= f16_nonfinite(oa[j]) | f16_nonfinite(ob[j]);
       }
       uint16_t* da = kabs + ((int64_t)g * R + r) * PF_D;
       *(uint4*)(da + 8 * c) = *(const uint4*)oa;
@@ -267,6 +274,7 @@ __global__ void __launch_bounds__(256) prefill_prep_bf16_kernel(
       }
     }
   }
+  if (nonfinite) atomicOr(flags, JL_FLAG_K_RANGE);
   // values: transpose 64 rows x 128 per KV head through LDS
   for (int g = 0; g < Hkv; ++g) {
 #pragma unroll
@@ -303,7 +311,8 @@ hipError_t launch_prefill_prep_bf16(const void* xk, const void* v, void* kcache_
                      (const uint16_t*)xk, (const uint16_t*)v, (uint16_t*)kcache_out,
                      (const SeqInfo*)(w + lay.seqs), (const int*)(w + lay.hdr), B, Hkv,
                      (int)lay.R, need_rem, from_abs, kscale, cont, (uint16_t*)(w + lay.kabs),
-                     (uint16_t*)(w + lay.krem), (uint16_t*)(w + lay.vt), fr);
+                     (uint16_t*)(w + lay.krem), (uint16_t*)(w + lay.vt), fr,
+                     (int*)(w + lay.hdr) + kHdrFlags);
   (void)T;
   return hipGetLastError();
 }
@@ -328,6 +337,7 @@ struct PfArgs {
   int ie_remote;  // pass B of Eq. 7 (1) or pass C (0)
   int cont;       // remote map x / G (real) instead of floor(x / G)
   RopeFreqs fr;
+  int* flags;     // range flags word of the workspace header
 };
 
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
@@ -578,12 +588,13 @@ __device__ __forceinline__ void reference_pv(const Tctx& c, const uint16_t* vs, 
   }
 }
 
-// An all-remote tile (no mask can apply): the two 32-key blocks are scored
-// one after the other, and the exp of the first block is interleaved with
-// the second block's MFMAs, so the wave's VALU work overlaps its own matrix
-// work. Same operations, in the same order per value, as qk_lds followed by
+// A tile no mask can touch (all-remote, or wholly below the causal diagonal
+// in a local or plain walk): the two 32-key blocks are scored one after the
+// other, and the exp of the first block is interleaved with the second
+// block's MFMAs, so the wave's VALU work overlaps its own matrix work. Same
+// operations, in the same order per value, as qk_lds followed by
 // softmax_pv_any.
-__device__ __forceinline__ void tile_remote(const Tctx& c, const uint16_t* ks, const uint16_t* vs,
+__device__ __forceinline__ void tile_nomask(const Tctx& c, const uint16_t* ks, const uint16_t* vs,
                                             const h8v (&q)[8], RowState& st) {
   const int x = kswz(c.l32);
   f32x16 s[2];
@@ -684,8 +695,10 @@ __device__ __forceinline__ void walk_boundary(const Tctx& c, int j0, int j1, int
 // RoPE(x_q, p) of the lane's raw query row as the fp16 QK^T operand. The lane
 // holds d = 16c + 8hh + j (c = 0..7, j = 0..7); the rotation pairs (d, d+64)
 // are chunks (c, c+4) of the same lane. w2pi: omega_i / (2 pi) in LDS.
+// Sets JL_FLAG_Q_RANGE in *flags when an operand is not a finite fp16 value.
 __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], double p, int hh,
-                                             const double* w2pi, h8v (&out)[8]) {
+                                             const double* w2pi, h8v (&out)[8], int* flags) {
+  uint32_t nonfinite = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -695,8 +708,11 @@ __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], double p, in
       rope_cs_turns(p, w2pi[16 * c + 8 * hh + j], cs, sn);
       out[c][j] = (_Float16)(x0 * cs - x1 * sn);
       out[c + 4][j] = (_Float16)(x0 * sn + x1 * cs);
+      nonfinite |= f16_nonfinite(__builtin_bit_cast(uint16_t, out[c][j])) |
+                   f16_nonfinite(__builtin_bit_cast(uint16_t, out[c + 4][j]));
     }
   }
+  if (nonfinite) atomicOr(flags, JL_FLAG_Q_RANGE);
 }
 
 template <int PASS>
@@ -763,7 +779,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
       raw[cc] = qvalid ? *(const u32x4*)(qp + 16 * cc) : u32x4{0, 0, 0, 0};
-    rotate_query(raw, p, c.hh, w2pi_s, out);
+    rotate_query(raw, p, c.hh, w2pi_s, out, a.flags);
   };
 
   // first tile that is not all-remote, first tile that is all-local
@@ -978,7 +994,7 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
       raw[cc] = qvalid ? *(const u32x4*)(qp + 16 * cc) : u32x4{0, 0, 0, 0};
-    rotate_query(raw, p, c.hh, w2pi_s, out);
+    rotate_query(raw, p, c.hh, w2pi_s, out, a.flags);
   };
 
   // first tile that is not all-remote, first tile that is all-local
@@ -1043,17 +1059,20 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
     softmax_pv_any(c, j, MASK_NONE, vst(j), s, st);
     pair_sync(ahead);
   };
-  auto step_remote = [&](int j, const h8v (&q)[8]) __attribute__((always_inline)) {
+  auto step_nomask = [&](int j, const h8v (&q)[8]) __attribute__((always_inline)) {
     const bool ahead = j + 2 < nkt;
     if (ahead) tile_dma8(c, j + 2, rem_of(j + 2), kst(j + 2), vst(j + 2));
-    tile_remote(c, kst(j), vst(j), q, st);
+    tile_nomask(c, kst(j), vst(j), q, st);
     pair_sync(ahead);
   };
+  // tiles wholly below the causal diagonal: every key <= q0 <= every row of
+  // the tile (and inside the sequence), so no mask can apply
+  const int j_free = min(nkt, (c.q0 + 1) / PF_BN);
   if (PASS == PASS_FUSED) {
     {
       h8v qr[8];
       rotq(remap_pos(c.myq, sq.G, a.cont), qr);
-      for (int j = 0; j < j_nr; ++j) step_remote(j, qr);  // remote phase
+      for (int j = 0; j < j_nr; ++j) step_nomask(j, qr);  // remote phase
       if (j_nr < j_loc) {                                    // boundary phase
         h8v qa[8];
         rotq(c.myq, qa);
@@ -1062,7 +1081,9 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
     }
     h8v qa[8];
     rotq(c.myq, qa);
-    for (int j = jl0; j < nkt; ++j) step(j, qa, nullptr);  // local phase
+    // local phase: mask-free tiles, then the diagonal ones
+    for (int j = jl0; j < j_free; ++j) step_nomask(j, qa);
+    for (int j = max(jl0, j_free); j < nkt; ++j) step(j, qa, nullptr);
   } else if (kIE) {
     h8v q[8];
     rotq(PASS == PASS_IE_B ? remap_pos(c.myq, sq.G, a.cont) : (double)c.myq, q);
@@ -1085,9 +1106,12 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
     for (int n = n1 + n2; n < nwalk; ++n)
       step_ie(n, n - n1 - n2, std::integral_constant<int, MASK_NONE>{});
   } else {
+    // plain causal RoPE attention (the baseline): the same mask-free step as
+    // the fused pass on every tile below the diagonal
     h8v qa[8];
     rotq(c.myq, qa);
-    for (int j = 0; j < nkt; ++j) step(j, qa, nullptr);
+    for (int j = 0; j < j_free; ++j) step_nomask(j, qa);
+    for (int j = j_free; j < nkt; ++j) step(j, qa, nullptr);
   }
 
   // ---- epilogue
@@ -1150,6 +1174,7 @@ hipError_t launch_prefill_bf16(int pass, const void* xq, void* o, float* lse, in
   a.cont = cont;
   (void)scale;  // the score scale is carried by the key operands (pre-pass)
   a.fr = fr;
+  a.flags = (int*)(w + lay.hdr) + kHdrFlags;
   const int64_t blocks = lay.max_tiles * Hq;
   if ((Hq / Hkv) % 2 == 0) {
     const dim3 grid((unsigned)(lay.max_tiles * (Hq / 2)));

@@ -402,3 +402,39 @@ def test_prefill_cached_agrees_with_prefill_and_decode():
         torch.cuda.synchronize()
         assert np.abs(to_host(o_1)[0] - to_host(o_d)).max() <= 1.6e-2
         assert np.abs(to_host(l_1)[:, 0] - to_host(l_d)).max() <= 1.6e-2
+
+
+# ------------------------------------------------------------------ fp16 range
+@pytest.mark.parametrize("where", ["none", "query", "key", "both"])
+def test_prefill_range_flags(where):
+    """Operands outside the fp16 range are reported, not faulted on: a raw
+    query row of 2e5 (rotated components reach ~2.8e5 > 65504) sets
+    FLAG_Q_RANGE, a key row of 1e6 (times the score scale log2(e)/sqrt(128),
+    1.3e5 > 65504) sets FLAG_K_RANGE; in-range inputs leave both clear. The
+    same holds for the prefill continued on a cache (keys taken from it)."""
+    L, Hq, Hkv, w0, w_pre, theta = 300, 4, 2, 40, 128, 1e6
+    xq, xk, v, _ = make_qkv(5001, L, Hq, Hkv, 128)
+    if where in ("query", "both"):
+        xq[200, 1, :] = 2e5
+    if where in ("key", "both"):
+        xk[17, 0, :] = 1e6
+    want = {"none": 0, "query": jl.FLAG_Q_RANGE, "key": jl.FLAG_K_RANGE,
+            "both": jl.FLAG_Q_RANGE | jl.FLAG_K_RANGE}[where]
+    q, k, vv = to_dev(xq), to_dev(xk), to_dev(v)
+    ws = torch.empty(jl.prefill_workspace_size(L, 1, Hq, Hkv, 128), dtype=torch.uint8,
+                     device="cuda")
+    ws.fill_(0xff)  # stale contents: every call clears the flags first
+    kc = torch.empty_like(k)
+    note(f"prefill range flags, out-of-range {where}")
+    o, _ = jl.bifocal_prefill(q, k, vv, w0, w_pre, theta, workspace=ws, kcache_out=kc)
+    torch.cuda.synchronize()
+    assert jl.prefill_flags(ws) == want
+    if where == "none":
+        assert torch.isfinite(o.float()).all()
+    note(f"cached prefill range flags, out-of-range {where}")
+    wsc = torch.empty(jl.prefill_cached_workspace_size(100, L - 100, Hq, Hkv, 128),
+                      dtype=torch.uint8, device="cuda")
+    wsc.fill_(0xff)
+    jl.bifocal_prefill_cached(q[100:].contiguous(), kc, vv, 100, w0, w_pre, theta, workspace=wsc)
+    torch.cuda.synchronize()
+    assert jl.prefill_flags(wsc) == want

@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the timed prefill steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--legs", default="all",
+                    help="comma list of the extra legs to run (plain, ie, cached, rope, sweep, "
+                         "cont, decode, batch, others; default all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: libbifocal has no multi-GPU path "
@@ -230,283 +233,301 @@ def main():
     del ev
 
     cpu_per = {}  # CPU oracle per workload (filled where the host inputs exist)
+    legs = None if args.legs == "all" else set(args.legs.split(","))
+
+    def want(name):
+        return legs is None or name in legs
     if not args.no_extras:
         extras = {}
-        # ---------------------------------------------------- plain baseline
-        log("plain causal RoPE attention at the same shape")
-        ws_plain = torch.empty(jl.prefill_workspace_size(L, 1, Hq, Hkv, d, mode="plain"),
-                               dtype=torch.uint8, device=dev)
+        plain_ms = None
         pe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        prefill("plain", workspace=ws_plain)
-        torch.cuda.synchronize()
-        pk = []
-        for _ in range(3):
-            prefill("plain", events=pe, workspace=ws_plain)
+        call = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        # ---------------------------------------------------- plain baseline
+        if want("plain"):
+            log("plain causal RoPE attention at the same shape")
+            ws_plain = torch.empty(jl.prefill_workspace_size(L, 1, Hq, Hkv, d, mode="plain"),
+                                   dtype=torch.uint8, device=dev)
+            pe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            prefill("plain", workspace=ws_plain)
             torch.cuda.synchronize()
-            pk.append(pe[0].elapsed_time(pe[1]))
-        del ws_plain
-        plain_ms = float(np.median(pk))
-        extras["plain_128k"] = {"kernel_ms": round(plain_ms, 4),
-                                "tflops": round(flops / plain_ms / 1e9, 2),
-                                "overhead_ratio_kernel": round(kern_avg / plain_ms, 4)}
+            pk = []
+            for _ in range(3):
+                prefill("plain", events=pe, workspace=ws_plain)
+                torch.cuda.synchronize()
+                pk.append(pe[0].elapsed_time(pe[1]))
+            del ws_plain
+            plain_ms = float(np.median(pk))
+            extras["plain_128k"] = {"kernel_ms": round(plain_ms, 4),
+                                    "tflops": round(flops / plain_ms / 1e9, 2),
+                                    "overhead_ratio_kernel": round(kern_avg / plain_ms, 4)}
         # ---------------------------------------------------- IE alternative
-        log("inclusion-exclusion alternative")
-        ws_ie = torch.empty(jl.prefill_workspace_size(L, 1, Hq, Hkv, d, mode="ie"),
-                            dtype=torch.uint8, device=dev)
-        prefill("ie", workspace=ws_ie)
-        torch.cuda.synchronize()
-        ik = []
-        for _ in range(2):
-            prefill("ie", events=pe, workspace=ws_ie)
+        if want("ie"):
+            log("inclusion-exclusion alternative")
+            ws_ie = torch.empty(jl.prefill_workspace_size(L, 1, Hq, Hkv, d, mode="ie"),
+                                dtype=torch.uint8, device=dev)
+            prefill("ie", workspace=ws_ie)
             torch.cuda.synchronize()
-            ik.append(pe[0].elapsed_time(pe[1]))
-        ratio = jl.ie_ratio_view(ws_ie, L, 1, Hq, Hkv, d)
-        kept["ie"] = o.index_select(0, rows_t).float().cpu().numpy()
-        kept["ie_ratio"] = ratio[:, rows_t].cpu().numpy().T  # [rows, Hq]
-        extras["ie_128k"] = {"kernels_ms": round(float(np.median(ik)), 4),
-                             "vs_fused": round(float(np.median(ik)) / kern_avg, 4),
-                             "worst_cancellation_ratio": float(ratio.max()),
-                             "rows_ratio_over_1e3": float((ratio > 1e3).float().mean())}
-        del ws_ie, ratio
-        prefill()  # restore the fused output and cache for the legs below
-        torch.cuda.empty_cache()
+            ik = []
+            for _ in range(2):
+                prefill("ie", events=pe, workspace=ws_ie)
+                torch.cuda.synchronize()
+                ik.append(pe[0].elapsed_time(pe[1]))
+            ratio = jl.ie_ratio_view(ws_ie, L, 1, Hq, Hkv, d)
+            kept["ie"] = o.index_select(0, rows_t).float().cpu().numpy()
+            kept["ie_ratio"] = ratio[:, rows_t].cpu().numpy().T  # [rows, Hq]
+            extras["ie_128k"] = {"kernels_ms": round(float(np.median(ik)), 4),
+                                 "vs_fused": round(float(np.median(ik)) / kern_avg, 4),
+                                 "worst_cancellation_ratio": float(ratio.max()),
+                                 "rows_ratio_over_1e3": float((ratio > 1e3).float().mean())}
+            del ws_ie, ratio
+            prefill()  # restore the fused output and cache for the legs below
+            torch.cuda.empty_cache()
 
         # ---------------------------------------------------- chunked prefill
-        log("prefill continued on the cache: last 8192 rows of the 128K sequence")
-        Tq = 8192
-        q_off = L - Tq
-        qc = q[q_off:].contiguous()
-        ws_c = torch.empty(jl.prefill_cached_workspace_size(q_off, Tq, Hq, Hkv, d),
-                           dtype=torch.uint8, device=dev)
-        oc = torch.empty_like(qc)
-        lc = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
-        fl_c = sum(4.0 * (p + 1) * d * Hq for p in range(q_off, L))
-        call = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        jl.bifocal_prefill_cached(qc, kcache, vv, q_off, w0, w_pre, theta, out=oc, lse=lc,
-                                  workspace=ws_c)
-        torch.cuda.synchronize()
-        ck, cc_ = [], []
-        for _ in range(5):
-            call[0].record(stream)
+        if want("cached"):
+            log("prefill continued on the cache: last 8192 rows of the 128K sequence")
+            Tq = 8192
+            q_off = L - Tq
+            qc = q[q_off:].contiguous()
+            ws_c = torch.empty(jl.prefill_cached_workspace_size(q_off, Tq, Hq, Hkv, d),
+                               dtype=torch.uint8, device=dev)
+            oc = torch.empty_like(qc)
+            lc = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+            fl_c = sum(4.0 * (p + 1) * d * Hq for p in range(q_off, L))
+            call = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             jl.bifocal_prefill_cached(qc, kcache, vv, q_off, w0, w_pre, theta, out=oc, lse=lc,
-                                      workspace=ws_c, events=pe)
-            call[1].record(stream)
+                                      workspace=ws_c)
             torch.cuda.synchronize()
-            ck.append(pe[0].elapsed_time(pe[1]))
-            cc_.append(call[0].elapsed_time(call[1]))
-        extras["prefill_cached_128k_last8k"] = {
-            "q_off": q_off, "rows": Tq, "kernel_ms": round(float(np.median(ck)), 4),
-            "tflops": round(fl_c / float(np.median(ck)) / 1e9, 2),
-            "call_ms": round(float(np.median(cc_)), 4),
-            "note": "call_ms adds the plan and the pre-pass that rotates all 131072 cached keys"}
-        del ws_c, oc, lc, qc
-        torch.cuda.empty_cache()
-
-        # ---------------------------------------------------- absolute RoPE
-        log("absolute RoPE (jl_rope_apply) of the 128K query and key tensors, in place")
-        rope_x = {"queries": q.clone(), "keys": k.clone()}
-        rope_res = {}
-        for nm, xt in rope_x.items():
-            jl.rope_apply(xt, theta)
-            torch.cuda.synchronize()
-            rt = []
+            ck, cc_ = [], []
             for _ in range(5):
                 call[0].record(stream)
-                jl.rope_apply(xt, theta)
+                jl.bifocal_prefill_cached(qc, kcache, vv, q_off, w0, w_pre, theta, out=oc, lse=lc,
+                                          workspace=ws_c, events=pe)
                 call[1].record(stream)
                 torch.cuda.synchronize()
-                rt.append(call[0].elapsed_time(call[1]))
-            rm = float(np.median(rt))
-            nb = 2.0 * xt.numel() * xt.element_size()  # read and written once
-            rope_res[nm] = {"shape": list(xt.shape), "ms": round(rm, 4),
-                            "GBps": round(nb / (rm * 1e-3) / 1e9, 1),
-                            "pct_hbm_peak": round(100 * nb / (rm * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
-        extras["rope_apply_128k"] = rope_res
-        del rope_x
-        torch.cuda.empty_cache()
+                ck.append(pe[0].elapsed_time(pe[1]))
+                cc_.append(call[0].elapsed_time(call[1]))
+            extras["prefill_cached_128k_last8k"] = {
+                "q_off": q_off, "rows": Tq, "kernel_ms": round(float(np.median(ck)), 4),
+                "tflops": round(fl_c / float(np.median(ck)) / 1e9, 2),
+                "call_ms": round(float(np.median(cc_)), 4),
+                "note": "call_ms adds the plan and the pre-pass that rotates all 131072 cached keys"}
+            del ws_c, oc, lc, qc
+            torch.cuda.empty_cache()
+
+        # ---------------------------------------------------- absolute RoPE
+        if want("rope"):
+            log("absolute RoPE (jl_rope_apply) of the 128K query and key tensors, in place")
+            rope_x = {"queries": q.clone(), "keys": k.clone()}
+            rope_res = {}
+            for nm, xt in rope_x.items():
+                jl.rope_apply(xt, theta)
+                torch.cuda.synchronize()
+                rt = []
+                for _ in range(5):
+                    call[0].record(stream)
+                    jl.rope_apply(xt, theta)
+                    call[1].record(stream)
+                    torch.cuda.synchronize()
+                    rt.append(call[0].elapsed_time(call[1]))
+                rm = float(np.median(rt))
+                nb = 2.0 * xt.numel() * xt.element_size()  # read and written once
+                rope_res[nm] = {"shape": list(xt.shape), "ms": round(rm, 4),
+                                "GBps": round(nb / (rm * 1e-3) / 1e9, 1),
+                                "pct_hbm_peak": round(100 * nb / (rm * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+            extras["rope_apply_128k"] = rope_res
+            del rope_x
+            torch.cuda.empty_cache()
 
         # ---------------------------------------------------- w0 sweep
-        log("window sweep at 128K (fused attention kernel)")
-        sweep = {}
-        for w in (0, 512, 1024, 2048, 4096):
-            jl.bifocal_prefill(q, k, vv, w, w_pre, theta, out=o, lse=lse, workspace=ws)
-            torch.cuda.synchronize()
-            wt = []
-            for _ in range(2):
-                jl.bifocal_prefill(q, k, vv, w, w_pre, theta, out=o, lse=lse, workspace=ws,
-                                   events=pe)
+        if want("sweep"):
+            log("window sweep at 128K (fused attention kernel)")
+            sweep = {}
+            for w in (0, 512, 1024, 2048, 4096):
+                jl.bifocal_prefill(q, k, vv, w, w_pre, theta, out=o, lse=lse, workspace=ws)
                 torch.cuda.synchronize()
-                wt.append(pe[0].elapsed_time(pe[1]))
-            wm = float(np.median(wt))
-            sweep[str(w)] = {"kernel_ms": round(wm, 4), "tflops": round(flops / wm / 1e9, 2),
-                             "vs_plain": round(wm / plain_ms, 4)}
-        extras["w0_sweep_128k"] = sweep
+                wt = []
+                for _ in range(2):
+                    jl.bifocal_prefill(q, k, vv, w, w_pre, theta, out=o, lse=lse, workspace=ws,
+                                       events=pe)
+                    torch.cuda.synchronize()
+                    wt.append(pe[0].elapsed_time(pe[1]))
+                wm = float(np.median(wt))
+                sweep[str(w)] = {"kernel_ms": round(wm, 4), "tflops": round(flops / wm / 1e9, 2),
+                                 "vs_plain": round(wm / plain_ms, 4) if plain_ms else None}
+            extras["w0_sweep_128k"] = sweep
 
         # ---------------------------------------------------- continuous remote map
-        log("continuous remote map x/G at 128K (fused attention kernel)")
-        jl.bifocal_prefill(q, k, vv, w0, w_pre, theta, out=o, lse=lse, workspace=ws,
-                           remap="continuous")
-        torch.cuda.synchronize()
-        ct = []
-        for _ in range(3):
+        if want("cont"):
+            log("continuous remote map x/G at 128K (fused attention kernel)")
             jl.bifocal_prefill(q, k, vv, w0, w_pre, theta, out=o, lse=lse, workspace=ws,
-                               events=pe, remap="continuous")
+                               remap="continuous")
             torch.cuda.synchronize()
-            ct.append(pe[0].elapsed_time(pe[1]))
-        cm = float(np.median(ct))
-        extras["continuous_map_128k"] = {"kernel_ms": round(cm, 4),
-                                         "tflops": round(flops / cm / 1e9, 2),
-                                         "vs_floor_map": round(cm / kern_avg, 4),
-                                         "vs_plain": round(cm / plain_ms, 4)}
+            ct = []
+            for _ in range(3):
+                jl.bifocal_prefill(q, k, vv, w0, w_pre, theta, out=o, lse=lse, workspace=ws,
+                                   events=pe, remap="continuous")
+                torch.cuda.synchronize()
+                ct.append(pe[0].elapsed_time(pe[1]))
+            cm = float(np.median(ct))
+            extras["continuous_map_128k"] = {"kernel_ms": round(cm, 4),
+                                             "tflops": round(flops / cm / 1e9, 2),
+                                             "vs_floor_map": round(cm / kern_avg, 4),
+                                             "vs_plain": round(cm / plain_ms, 4) if plain_ms else None}
 
-        # ---------------------------------------------------- decode
-        log("decode on the 131072-key absolute cache (L2/MALL evicted by a clean read per step)")
-        cdec = WORKLOADS["decode_128k"]
-        # Two cache states between steps: a clean 1 GiB read (evicts L2 and the
-        # memory-side cache and leaves no dirty lines) and a 1 GiB zero-fill
-        # (evicts too, but leaves dirty lines whose write-back the timed step
-        # then pays for). The clean read is the headline state.
+        # evicts L2 and the memory-side cache between decode steps
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        wsd = torch.empty(jl.decode_workspace_size(L, Hq, d), dtype=torch.uint8, device=dev)
-        od = torch.empty((Hq, d), dtype=torch.bfloat16, device=dev)
-        ld = torch.empty((Hq,), dtype=torch.float32, device=dev)
         de = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        dec = {}
-        for pos in cdec["decode_positions"]:
-            qd = q[pos].contiguous()
-            row = {}
-            for mode in ("fused", "plain", "continuous"):
-                for evict in (("read",) if mode == "continuous" else ("read", "write")):
-                    ts = []
-                    for it in range(args.decode_iters + 3):
-                        if evict == "read":
-                            flush.sum()
-                        else:
-                            flush.zero_()
-                        jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta,
-                                          mode="fused" if mode == "continuous" else mode,
-                                          remap="continuous" if mode == "continuous" else "floor",
-                                          out=od, lse=ld, workspace=wsd, events=de)
-                        torch.cuda.synchronize()
-                        if it >= 3:
-                            ts.append(de[0].elapsed_time(de[1]) * 1e3)  # us
-                    nbytes = 4.0 * (pos + 1) * Hkv * d
-                    med = float(np.median(ts))
-                    key = mode if evict == "read" else mode + "_after_zero_fill"
-                    row[key] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
-                                "us_p90": round(pct(ts, 90), 2),
-                                "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
-                                "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 /
-                                                      PEAK_HBM_GBS, 2),
-                                "pct_calibrated_read": round(100 * nbytes / (med * 1e-6) / 1e9 /
-                                                             read_gbs, 2)}
-            row["G"] = jl.group_size(pos + 1, w_pre)
-            row["overhead_ratio"] = round(row["fused"]["us_median"] / row["plain"]["us_median"],
-                                          4)
-            dec[str(pos)] = row
-            log(f"decode pos={pos}: {row['fused']['us_median']} us "
-                f"({row['fused']['pct_hbm_peak']}% HBM, {row['fused']['pct_calibrated_read']}% "
-                f"of the calibrated read rate), plain {row['plain']['us_median']} us")
-        result["decode"] = dec
-        del wsd
+        # ---------------------------------------------------- decode
+        if want("decode"):
+            log("decode on the 131072-key absolute cache (L2/MALL evicted by a clean read per step)")
+            cdec = WORKLOADS["decode_128k"]
+            # Two cache states between steps: a clean 1 GiB read (evicts L2 and the
+            # memory-side cache and leaves no dirty lines) and a 1 GiB zero-fill
+            # (evicts too, but leaves dirty lines whose write-back the timed step
+            # then pays for). The clean read is the headline state.
+            wsd = jl.decode_workspace(L, Hq, d, dev)
+            od = torch.empty((Hq, d), dtype=torch.bfloat16, device=dev)
+            ld = torch.empty((Hq,), dtype=torch.float32, device=dev)
+            dec = {}
+            for pos in cdec["decode_positions"]:
+                qd = q[pos].contiguous()
+                row = {}
+                for mode in ("fused", "plain", "continuous"):
+                    for evict in (("read",) if mode == "continuous" else ("read", "write")):
+                        ts = []
+                        for it in range(args.decode_iters + 3):
+                            if evict == "read":
+                                flush.sum()
+                            else:
+                                flush.zero_()
+                            jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta,
+                                              mode="fused" if mode == "continuous" else mode,
+                                              remap="continuous" if mode == "continuous" else "floor",
+                                              out=od, lse=ld, workspace=wsd, events=de)
+                            torch.cuda.synchronize()
+                            if it >= 3:
+                                ts.append(de[0].elapsed_time(de[1]) * 1e3)  # us
+                        nbytes = 4.0 * (pos + 1) * Hkv * d
+                        med = float(np.median(ts))
+                        key = mode if evict == "read" else mode + "_after_zero_fill"
+                        row[key] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
+                                    "us_p90": round(pct(ts, 90), 2),
+                                    "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                    "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 /
+                                                          PEAK_HBM_GBS, 2),
+                                    "pct_calibrated_read": round(100 * nbytes / (med * 1e-6) / 1e9 /
+                                                                 read_gbs, 2)}
+                row["G"] = jl.group_size(pos + 1, w_pre)
+                row["overhead_ratio"] = round(row["fused"]["us_median"] / row["plain"]["us_median"],
+                                              4)
+                dec[str(pos)] = row
+                log(f"decode pos={pos}: {row['fused']['us_median']} us "
+                    f"({row['fused']['pct_hbm_peak']}% HBM, {row['fused']['pct_calibrated_read']}% "
+                    f"of the calibrated read rate), plain {row['plain']['us_median']} us")
+            result["decode"] = dec
+            del wsd
 
         # ---------------------------------------------------- batched decode
-        cb = WORKLOADS["decode_batch_16"]
-        bpos = cb["positions"]
-        log(f"batched decode: {len(bpos)} sequences in one launch (L2/MALL evicted per step)")
-        bst, brows = packed_starts(bpos)
-        kb = torch.empty((brows, Hkv, d), dtype=torch.bfloat16, device=dev)
-        vb = torch.empty_like(kb)
-        xb = torch.empty((len(bpos), Hq, d), dtype=torch.bfloat16, device=dev)
-        for b, (p, s0) in enumerate(zip(bpos, bst)):
-            qn, kn, vn = make_decode_seq(cb["seed"], b, p + 1, Hq, Hkv, d, cb["std"], cb["dtype"])
-            xb[b] = up(qn)
-            kb[s0:s0 + p + 1] = up(kn)
-            vb[s0:s0 + p + 1] = up(vn)
-            jl.rope_apply(kb[s0:s0 + p + 1], cb["theta"])
-            del qn, kn, vn
-        pos_t = torch.tensor(bpos, dtype=torch.int32, device=dev)
-        st_t = torch.tensor(bst, dtype=torch.int32, device=dev)
-        mk = max(bpos) + 1
-        wsb = torch.empty(jl.decode_batch_workspace_size(len(bpos), mk, Hq, d), dtype=torch.uint8,
-                          device=dev)
-        ob = torch.empty_like(xb)
-        lb = torch.empty((len(bpos), Hq), dtype=torch.float32, device=dev)
-        bbytes = sum(4.0 * (p + 1) * Hkv * d for p in bpos)
-        brow = {"B": len(bpos), "keys": int(sum(p + 1 for p in bpos)), "max_keys": mk}
-        for mode in ("fused", "plain"):
-            ts = []
-            for it in range(args.decode_iters + 3):
-                flush.sum()
-                jl.bifocal_decode_batch(xb, kb, vb, pos_t, st_t, mk, cb["w0"], cb["w_pre"],
-                                        cb["theta"], mode=mode, out=ob, lse=lb, workspace=wsb,
-                                        events=de)
-                torch.cuda.synchronize()
-                if it >= 3:
-                    ts.append(de[0].elapsed_time(de[1]) * 1e3)
-            med = float(np.median(ts))
-            brow[mode] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
-                          "us_p90": round(pct(ts, 90), 2),
-                          "tokens_per_s": round(len(bpos) / (med * 1e-6), 1),
-                          "GBps": round(bbytes / (med * 1e-6) / 1e9, 1),
-                          "pct_hbm_peak": round(100 * bbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                                                2),
-                          "pct_calibrated_read": round(100 * bbytes / (med * 1e-6) / 1e9 /
-                                                       read_gbs, 2)}
-        brow["overhead_ratio"] = round(brow["fused"]["us_median"] / brow["plain"]["us_median"], 4)
-        extras["decode_batch_16"] = brow
-        log(f"batched decode: {brow['fused']['us_median']} us per step "
-            f"({brow['fused']['pct_calibrated_read']}% of the calibrated read rate)")
-        del kb, vb, xb, wsb, ob, lb, flush
-        torch.cuda.empty_cache()
-
-        # ---------------------------------------------------- other workloads
-        for name in ("prefill_64k", "varlen_4seq"):
-            cw = WORKLOADS[name]
-            lens = cw["lengths"]
-            T = sum(lens)
-            log(f"{name}")
-            a, b_, cc, _ = make_qkv(cw["seed"], T, cw["Hq"], cw["Hkv"], cw["d"], cw["std"],
-                                    cw["dtype"])
-            qa, ka, va = up(a), up(b_), up(cc)
-            cu = None
-            if len(lens) > 1:
-                cu = torch.tensor(np.cumsum([0] + lens), dtype=torch.int32, device=dev)
-            wsw = torch.empty(jl.prefill_workspace_size(T, len(lens), cw["Hq"], cw["Hkv"], cw["d"]),
-                              dtype=torch.uint8, device=dev)
-            ow = torch.empty_like(qa)
-            fw = sum(2.0 * n * n * cw["d"] * cw["Hq"] for n in lens)
-            jl.bifocal_prefill(qa, ka, va, cw["w0"], cw["w_pre"], cw["theta"], cu_seqlens=cu,
-                               out=ow, workspace=wsw, want_lse=False)
-            torch.cuda.synchronize()
-            ks = []
-            for _ in range(3):
-                jl.bifocal_prefill(qa, ka, va, cw["w0"], cw["w_pre"], cw["theta"], cu_seqlens=cu,
-                                   out=ow, workspace=wsw, want_lse=False, events=pe)
-                torch.cuda.synchronize()
-                ks.append(pe[0].elapsed_time(pe[1]))
-            km = float(np.median(ks))
-            extras[name] = {"kernel_ms": round(km, 4), "tflops": round(fw / km / 1e9, 2),
-                            "pct_mfma_peak": round(100 * fw / km / 1e9 / PEAK_BF16_TFLOPS, 2)}
-            if not args.no_cpu_baseline:
-                # the oracle on this workload's parity subset: 512 seeded rows
-                # per sequence, every head
-                from oracle import bifocal_varlen
-                rr = np.random.default_rng(7)
-                rps = [np.sort(rr.choice(n, min(n, args.cpu_rows), replace=False)) for n in lens]
-                log(f"CPU oracle on {name}: {sum(len(r) for r in rps)} rows x {cw['Hq']} heads")
-                t0 = time.perf_counter()
-                bifocal_varlen(a, b_, cc, np.cumsum([0] + lens), cw["w0"], cw["w_pre"],
-                               cw["theta"], rows_per_seq=rps)
-                dt = time.perf_counter() - t0
-                nrh = sum(len(r) for r in rps) * cw["Hq"]
-                flc = float(sum(4.0 * (int(x) + 1) * cw["d"] * cw["Hq"] for r in rps for x in r))
-                cpu_per[name] = {"seconds": round(dt, 3), "rows_per_s": round(nrh / dt, 2),
-                                 "TFLOPs": round(flc / dt / 1e12, 6),
-                                 "sample": f"{args.cpu_rows} seeded rows per sequence x "
-                                           f"{cw['Hq']} heads, all keys of each row"}
-            del qa, ka, va, wsw, ow, a, b_, cc
+        if want("batch"):
+            cb = WORKLOADS["decode_batch_16"]
+            bpos = cb["positions"]
+            log(f"batched decode: {len(bpos)} sequences in one launch (L2/MALL evicted per step)")
+            bst, brows = packed_starts(bpos)
+            kb = torch.empty((brows, Hkv, d), dtype=torch.bfloat16, device=dev)
+            vb = torch.empty_like(kb)
+            xb = torch.empty((len(bpos), Hq, d), dtype=torch.bfloat16, device=dev)
+            for b, (p, s0) in enumerate(zip(bpos, bst)):
+                qn, kn, vn = make_decode_seq(cb["seed"], b, p + 1, Hq, Hkv, d, cb["std"], cb["dtype"])
+                xb[b] = up(qn)
+                kb[s0:s0 + p + 1] = up(kn)
+                vb[s0:s0 + p + 1] = up(vn)
+                jl.rope_apply(kb[s0:s0 + p + 1], cb["theta"])
+                del qn, kn, vn
+            pos_t = torch.tensor(bpos, dtype=torch.int32, device=dev)
+            st_t = torch.tensor(bst, dtype=torch.int32, device=dev)
+            mk = max(bpos) + 1
+            wsb = jl.decode_batch_workspace(len(bpos), mk, Hq, d, dev)
+            ob = torch.empty_like(xb)
+            lb = torch.empty((len(bpos), Hq), dtype=torch.float32, device=dev)
+            bbytes = sum(4.0 * (p + 1) * Hkv * d for p in bpos)
+            brow = {"B": len(bpos), "keys": int(sum(p + 1 for p in bpos)), "max_keys": mk}
+            for mode in ("fused", "plain"):
+                ts = []
+                for it in range(args.decode_iters + 3):
+                    flush.sum()
+                    jl.bifocal_decode_batch(xb, kb, vb, pos_t, st_t, mk, cb["w0"], cb["w_pre"],
+                                            cb["theta"], mode=mode, out=ob, lse=lb, workspace=wsb,
+                                            events=de)
+                    torch.cuda.synchronize()
+                    if it >= 3:
+                        ts.append(de[0].elapsed_time(de[1]) * 1e3)
+                med = float(np.median(ts))
+                brow[mode] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
+                              "us_p90": round(pct(ts, 90), 2),
+                              "tokens_per_s": round(len(bpos) / (med * 1e-6), 1),
+                              "GBps": round(bbytes / (med * 1e-6) / 1e9, 1),
+                              "pct_hbm_peak": round(100 * bbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                                    2),
+                              "pct_calibrated_read": round(100 * bbytes / (med * 1e-6) / 1e9 /
+                                                           read_gbs, 2)}
+            brow["overhead_ratio"] = round(brow["fused"]["us_median"] / brow["plain"]["us_median"], 4)
+            extras["decode_batch_16"] = brow
+            log(f"batched decode: {brow['fused']['us_median']} us per step "
+                f"({brow['fused']['pct_calibrated_read']}% of the calibrated read rate)")
+            del kb, vb, xb, wsb, ob, lb
             torch.cuda.empty_cache()
+
+        del flush
+        torch.cuda.empty_cache()
+        # ---------------------------------------------------- other workloads
+        if want("others"):
+            for name in ("prefill_64k", "varlen_4seq"):
+                cw = WORKLOADS[name]
+                lens = cw["lengths"]
+                T = sum(lens)
+                log(f"{name}")
+                a, b_, cc, _ = make_qkv(cw["seed"], T, cw["Hq"], cw["Hkv"], cw["d"], cw["std"],
+                                        cw["dtype"])
+                qa, ka, va = up(a), up(b_), up(cc)
+                cu = None
+                if len(lens) > 1:
+                    cu = torch.tensor(np.cumsum([0] + lens), dtype=torch.int32, device=dev)
+                wsw = torch.empty(jl.prefill_workspace_size(T, len(lens), cw["Hq"], cw["Hkv"], cw["d"]),
+                                  dtype=torch.uint8, device=dev)
+                ow = torch.empty_like(qa)
+                fw = sum(2.0 * n * n * cw["d"] * cw["Hq"] for n in lens)
+                jl.bifocal_prefill(qa, ka, va, cw["w0"], cw["w_pre"], cw["theta"], cu_seqlens=cu,
+                                   out=ow, workspace=wsw, want_lse=False)
+                torch.cuda.synchronize()
+                ks = []
+                for _ in range(3):
+                    jl.bifocal_prefill(qa, ka, va, cw["w0"], cw["w_pre"], cw["theta"], cu_seqlens=cu,
+                                       out=ow, workspace=wsw, want_lse=False, events=pe)
+                    torch.cuda.synchronize()
+                    ks.append(pe[0].elapsed_time(pe[1]))
+                km = float(np.median(ks))
+                extras[name] = {"kernel_ms": round(km, 4), "tflops": round(fw / km / 1e9, 2),
+                                "pct_mfma_peak": round(100 * fw / km / 1e9 / PEAK_BF16_TFLOPS, 2)}
+                if not args.no_cpu_baseline:
+                    # the oracle on this workload's parity subset: 512 seeded rows
+                    # per sequence, every head
+                    from oracle import bifocal_varlen
+                    rr = np.random.default_rng(7)
+                    rps = [np.sort(rr.choice(n, min(n, args.cpu_rows), replace=False)) for n in lens]
+                    log(f"CPU oracle on {name}: {sum(len(r) for r in rps)} rows x {cw['Hq']} heads")
+                    t0 = time.perf_counter()
+                    bifocal_varlen(a, b_, cc, np.cumsum([0] + lens), cw["w0"], cw["w_pre"],
+                                   cw["theta"], rows_per_seq=rps)
+                    dt = time.perf_counter() - t0
+                    nrh = sum(len(r) for r in rps) * cw["Hq"]
+                    flc = float(sum(4.0 * (int(x) + 1) * cw["d"] * cw["Hq"] for r in rps for x in r))
+                    cpu_per[name] = {"seconds": round(dt, 3), "rows_per_s": round(nrh / dt, 2),
+                                     "TFLOPs": round(flc / dt / 1e12, 6),
+                                     "sample": f"{args.cpu_rows} seeded rows per sequence x "
+                                               f"{cw['Hq']} heads, all keys of each row"}
+                del qa, ka, va, wsw, ow, a, b_, cc
+                torch.cuda.empty_cache()
         result["extras"] = extras
 
     if args.copy_calibration:

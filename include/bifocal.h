@@ -345,7 +345,8 @@ int jl_calib_stream_read(const void* src, size_t bytes, uint32_t* sink, int bloc
  * chunks per workgroup with eight nontemporal 16-byte loads in flight per
  * thread; 2 moves 64 KiB chunks by direct global -> LDS transfers (sixteen
  * 1 KiB transfers per wave), the path the bf16 decode streams its values
- * through. Bytes past the last whole chunk are read by ordinary loads.
+ * through; 3 is variant 1 without the nontemporal hint and 4 is variant 2
+ * with it. Bytes past the last whole chunk are read by ordinary loads.
  * JL_EINVAL on bad arguments or an unknown variant. */
 int jl_calib_stream_read_ex(const void* src, size_t bytes, uint32_t* sink, int blocks,
                             int variant, void* stream);

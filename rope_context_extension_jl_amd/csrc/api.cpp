@@ -513,7 +513,7 @@ int jl_calib_stream_read_ex(const void* src, size_t bytes, uint32_t* sink, int b
                             int variant, void* stream) {
   if (!src || !sink || bytes < 16 || (bytes & 15) || (((uintptr_t)src) & 15) || blocks < 1)
     return JL_EINVAL;
-  if (variant < 0 || variant > 2) return JL_EINVAL;
+  if (variant < 0 || variant > 4) return JL_EINVAL;
   return hip_status(launch_calib_read(src, bytes, sink, blocks, variant, (hipStream_t)stream));
 }
 

@@ -28,9 +28,10 @@ __global__ void __launch_bounds__(256) calib_read_kernel(const cu32x4* __restric
 
 // Contiguous chunks: workgroup b reads chunks b, b + grid, ... of 256 x 8
 // 16-byte vectors (32 KiB); each thread issues its eight loads (each wave's
-// load covers 1 KiB contiguously) before using any, with the nontemporal
-// hint, so every CU keeps 8 KiB per wave in flight without allocating the
-// streamed lines in the caches.
+// load covers 1 KiB contiguously) before using any, so every CU keeps 8 KiB
+// per wave in flight; NT adds the nontemporal hint (streamed lines are not
+// kept in the caches).
+template <bool NT>
 __global__ void __launch_bounds__(256) calib_read_chunk_kernel(const cu32x4* __restrict__ p,
                                                                size_t n16, uint32_t* sink) {
   constexpr int U = 8;
@@ -41,7 +42,7 @@ __global__ void __launch_bounds__(256) calib_read_chunk_kernel(const cu32x4* __r
     const cu32x4* q = p + cidx * chunk + threadIdx.x;
     cu32x4 v[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) v[k] = __builtin_nontemporal_load(q + 256 * k);
+    for (int k = 0; k < U; ++k) v[k] = NT ? __builtin_nontemporal_load(q + 256 * k) : q[256 * k];
 #pragma unroll
     for (int k = 0; k < U; ++k) acc ^= v[k];
   }
@@ -57,7 +58,8 @@ __global__ void __launch_bounds__(256) calib_read_chunk_kernel(const cu32x4* __r
 // blocks of its workgroup's chunk into its own LDS window; the transfers are
 // never read back except one word at the end (so the work stays), and the
 // memory counter limits how many are in flight. Chunk c (64 KiB) is read by
-// workgroup c mod grid.
+// workgroup c mod grid. NT: with the nontemporal hint.
+template <bool NT>
 __global__ void __launch_bounds__(256) calib_read_lds_kernel(const cu32x4* __restrict__ p,
                                                              size_t n16, uint32_t* sink) {
   __shared__ __attribute__((aligned(16))) uint8_t win[4][16 * 1024];
@@ -72,7 +74,7 @@ __global__ void __launch_bounds__(256) calib_read_lds_kernel(const cu32x4* __res
       __builtin_amdgcn_global_load_lds((const void*)(q + 64 * k),
                                        (__attribute__((address_space(3))) void*)(win[wave] +
                                                                                  1024 * k),
-                                       16, 0, 0);
+                                       16, 0, NT ? 2 : 0);  // 2: the nontemporal hint
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -107,12 +109,16 @@ __global__ void __launch_bounds__(256) calib_mfma_kernel(float* sink, int iters)
 hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
                              int variant, hipStream_t st) {
   const cu32x4* p = (const cu32x4*)src;
+  const size_t n = bytes / 16;
   if (variant == 1)
-    hipLaunchKernelGGL(calib_read_chunk_kernel, dim3(blocks), dim3(256), 0, st, p, bytes / 16,
-                       sink);
+    hipLaunchKernelGGL(calib_read_chunk_kernel<true>, dim3(blocks), dim3(256), 0, st, p, n, sink);
   else if (variant == 2)
-    hipLaunchKernelGGL(calib_read_lds_kernel, dim3(blocks), dim3(256), 0, st, p, bytes / 16,
+    hipLaunchKernelGGL(calib_read_lds_kernel<false>, dim3(blocks), dim3(256), 0, st, p, n, sink);
+  else if (variant == 3)
+    hipLaunchKernelGGL(calib_read_chunk_kernel<false>, dim3(blocks), dim3(256), 0, st, p, n,
                        sink);
+  else if (variant == 4)
+    hipLaunchKernelGGL(calib_read_lds_kernel<true>, dim3(blocks), dim3(256), 0, st, p, n, sink);
   else
     hipLaunchKernelGGL(calib_read_kernel, dim3(blocks), dim3(256), 0, st, p, bytes / 16, sink);
   return hipGetLastError();

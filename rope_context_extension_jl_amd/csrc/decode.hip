@@ -339,17 +339,32 @@ __device__ __forceinline__ int dec_vswz(int r) {
 }
 
 // Workgroup memory of the bf16 kernels (under 80 KiB at D = 128, so two
-// workgroups share a CU). The prologue's operand tables live in the second
-// V stage of every wave, which no transfer touches before the key loop.
+// workgroups share a CU), as separate LDS arrays: the compiler then sees
+// that the reads of one V stage, of the tables or of the query cannot alias
+// the direct transfers in flight into the other stage, and does not wait for
+// those. The prologue's operand tables live in the second V stages (vB),
+// which no transfer touches before the key loop.
 template <int D>
-struct __attribute__((aligned(16))) DecShared {
-  uint8_t vst[2][DEC_NW][DecGeom<D>::VBYTES];  // V stages [stage][wave]; merge scratch later
-  float qraw[8][D];         // raw query rows of the group x scale log2 e (rows >= R zero)
-  float2 cs[DEC_NW][D / 2]; // DEC_FACT: the chunk's query rotation per wave;
-                            // DEC_GEN: the two R_{c16} tables as fp16
-  double w2pi[D / 2];       // omega_i / (2 pi)
-  int flag, last;
+struct DecLds {
+  uint8_t* vA;   // [DEC_NW][VBYTES] first V stage of each wave; merge scratch after the loop
+  uint8_t* vB;   // [DEC_NW][VBYTES] second V stage of each wave
+  float* qraw;   // [8][D] raw query rows of the group x scale log2 e (rows >= R zero)
+  float2* cs;    // [DEC_NW][D / 2] DEC_FACT: the chunk's query rotation per wave;
+                 // DEC_GEN: the two R_{c16} tables as fp16
+  double* w2pi;  // [D / 2] omega_i / (2 pi)
+  int* flag;     // [2]: a range's non-finite flag, the last-arrival flag
 };
+
+template <int D>
+__device__ __forceinline__ DecLds<D> dec_lds() {
+  __shared__ __attribute__((aligned(16))) uint8_t vA[DEC_NW * DecGeom<D>::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vB[DEC_NW * DecGeom<D>::VBYTES];
+  __shared__ __attribute__((aligned(16))) float qraw[8 * D];
+  __shared__ __attribute__((aligned(16))) float2 cs[DEC_NW * D / 2];
+  __shared__ double w2pi[D / 2];
+  __shared__ int flag[2];
+  return DecLds<D>{vA, vB, qraw, cs, w2pi, flag};
+}
 
 // Per-wave constants of the key loop (all wave-uniform except the lane ids).
 struct DecCtx {
@@ -405,7 +420,7 @@ __device__ __forceinline__ void dec_issue_k(const DecCtx& c, int k0, DecBuf<D>& 
     const int key = min(k0 + 16 * kb + c.r16, c.k_hi - 1);
 #pragma unroll
     for (int ds = 0; ds < G::NDS; ++ds)
-      b.k[kb][ds] = *(const du32x4*)(c.kbase + key * c.rstride + 32 * ds);
+      b.k[kb][ds] = __builtin_nontemporal_load((const du32x4*)(c.kbase + key * c.rstride + 32 * ds));
   }
 }
 
@@ -423,7 +438,7 @@ __device__ __forceinline__ void dec_issue_v(const DecCtx& c, int k0, uint8_t* st
     const int key = min(k0 + row, c.k_hi - 1);
     __builtin_amdgcn_global_load_lds(
         (const void*)(c.vbase + key * c.rstride + 8 * ch),
-        (__attribute__((address_space(3))) void*)(stage + 1024 * i), 16, 0, 0);
+        (__attribute__((address_space(3))) void*)(stage + 1024 * i), 16, 0, 2);  // 2: nontemporal
   }
 }
 
@@ -455,7 +470,7 @@ template <int D, int PATH>
 __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<D>& b,
                                           const dh8v (&qa)[D / 32], dh8v (&qr)[D / 32],
                                           const dh2v (&tcr)[2][D / 64][4],
-                                          const dh2v (&tsr)[2][D / 64][4], DecShared<D>& sh,
+                                          const dh2v (&tsr)[2][D / 64][4], const DecLds<D>& sh,
                                           int wave, const uint8_t* vb, DecState<D>& st,
                                           float& chk) {
   using G = DecGeom<D>;
@@ -472,18 +487,18 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
                               : (double)(c.pos / c.G - k0 / c.G + k0);
       float cc, ss;
       rope_cs_turns(P, sh.w2pi[c.lane], cc, ss);
-      sh.cs[wave][c.lane] = make_float2(cc, ss);
+      sh.cs[wave * HALF + c.lane] = make_float2(cc, ss);
     }
     dec_wait_lds();
     __builtin_amdgcn_wave_barrier();
     const bool qv = c.r16 < 8;
-    const float* qrow = sh.qraw[c.r16 & 7];
+    const float* qrow = sh.qraw + (c.r16 & 7) * D;
 #pragma unroll
     for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int f = 32 * ds + 8 * c.g16 + j;
-        const float2 t = sh.cs[wave][f];
+        const float2 t = sh.cs[wave * HALF + f];
         const float x0 = qv ? qrow[f] : 0.f, x1 = qv ? qrow[f + HALF] : 0.f;
         qr[ds][j] = (_Float16)(x0 * t.x - x1 * t.y);
         qr[ds + NDS / 2][j] = (_Float16)(x0 * t.y + x1 * t.x);
@@ -509,7 +524,7 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
       // R_d R_{c16}, c16 = f(key + 16) - f(key) - 16 takes the larger of its
       // two values when the key's residue carries (continuous map: one value)
       const int t = !c.cont && (key % c.G) + (16 % c.G) >= c.G ? 1 : 0;
-      const _Float16* tt = (const _Float16*)&sh.cs[0][0] + 2 * t * HALF;
+      const _Float16* tt = (const _Float16*)sh.cs + 2 * t * HALF;
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
@@ -665,7 +680,7 @@ __device__ __forceinline__ void dec_write_nan(const DecArgs& a, int b, int g) {
 // of the workgroup calls it; it returns with the LDS free for the next unit.
 template <int D, int PATH>
 __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int b, int g, int s,
-                                         int nrange, DecShared<D>& sh) {
+                                         int nrange, const DecLds<D>& sh) {
   using Gm = DecGeom<D>;
   constexpr int NDS = Gm::NDS, NDB = Gm::NDB, HALF = D / 2;
   const int tid = threadIdx.x;
@@ -695,8 +710,8 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   constexpr int kstep = DEC_CHUNK * DEC_NW;
   int k0 = k_lo + DEC_CHUNK * wave;
   const bool active = k0 < c.k_hi;  // the range holds a chunk for this wave
-  uint8_t* sA = sh.vst[0][wave];
-  uint8_t* sB = sh.vst[1][wave];
+  uint8_t* sA = sh.vA + wave * Gm::VBYTES;
+  uint8_t* sB = sh.vB + wave * Gm::VBYTES;
   DecBuf<D> bA, bB;
   // the wave's first chunk is in flight during the prologue
   if (active) {
@@ -707,21 +722,21 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   // ---- prologue: frequencies, the group's raw query, operand tables. The
   // tables read once go to the second V stages (free until the key loop).
   if (tid < HALF) sh.w2pi[tid] = a.fr.w(tid) * kInvTwoPi;
-  if (tid == 0) sh.flag = 0;
+  if (tid == 0) sh.flag[0] = 0;
   {
     const uint16_t* xq = (const uint16_t*)sq.xq + (int64_t)h0 * D;
     for (int idx = tid; idx < 8 * D; idx += blockDim.x)
-      sh.qraw[idx / D][idx % D] = idx / D < R ? bf16_bits_to_f32(xq[idx]) * a.scale_log2 : 0.f;
+      sh.qraw[idx] = idx / D < R ? bf16_bits_to_f32(xq[idx]) * a.scale_log2 : 0.f;
   }
   __syncthreads();
-  _Float16* pqa = (_Float16*)&sh.vst[1][0][0];  // [16][D] query at pos
+  _Float16* pqa = (_Float16*)sh.vB;  // [16][D] query at pos
   _Float16* pq2 = pqa + 16 * D;                  // GEN: [16][D] query at f(pos);
                                                  // FACT: [2][32][HALF] in-chunk cos, sin
   for (int idx = tid; idx < 16 * HALF; idx += blockDim.x) {
     const int h = idx / HALF, i = idx % HALF;
     float y0 = 0.f, y1 = 0.f, z0 = 0.f, z1 = 0.f;
     if (h < R) {
-      const float x0 = sh.qraw[h][i], x1 = sh.qraw[h][i + HALF];
+      const float x0 = sh.qraw[h * D + i], x1 = sh.qraw[h * D + i + HALF];
       float cs, sn;
       rope_cs_turns((double)sq.pos, sh.w2pi[i], cs, sn);
       y0 = x0 * cs - x1 * sn;
@@ -754,7 +769,7 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   if (PATH == DEC_GEN) {
     // R_{c16} for both values of c16 = f(k + 16) - f(k) - 16 (continuous
     // map: 16 (1 / G - 1) in both)
-    _Float16* tt = (_Float16*)&sh.cs[0][0];  // [2 steps][cos, sin][HALF]
+    _Float16* tt = (_Float16*)sh.cs;  // [2 steps][cos, sin][HALF]
     for (int idx = tid; idx < 2 * HALF; idx += blockDim.x) {
       const int t = idx / HALF, f = idx % HALF;
       const double c16 = a.cont ? 16.0 * sq.fk_rel : (double)(16 / sq.G + t - 16);
@@ -782,8 +797,11 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
         const du32x4 sv = *(const du32x4*)(pq2 + 32 * HALF + off);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          tcr[kb][ds][m] = __builtin_bit_cast(dh2v, cv[m]);
-          tsr[kb][ds][m] = __builtin_bit_cast(dh2v, sv[m]);
+          // (the element is copied first: a bit cast of a vector element
+          // expression reads element 0 whatever the index)
+          const uint32_t cw = cv[m], sw = sv[m];
+          tcr[kb][ds][m] = __builtin_bit_cast(dh2v, cw);
+          tsr[kb][ds][m] = __builtin_bit_cast(dh2v, sw);
         }
       }
   }
@@ -819,12 +837,12 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   // no transfer into the LDS stages may outlive the loop
   __builtin_amdgcn_s_waitcnt(0);
   if (__any(!(chk - chk == 0.f))) {  // chk is inf or NaN
-    if (lane == 0) atomicOr(&sh.flag, 1);
+    if (lane == 0) atomicOr(&sh.flag[0], 1);
   }
   __syncthreads();  // every wave is past its V stages
 
   // ---- merge the waves' states through LDS into the range's record
-  float* red = (float*)&sh.vst[0][0][0];
+  float* red = (float*)sh.vA;
   float* red_m = red;                  // [NW][16]
   float* red_l = red + DEC_NW * 16;    // [NW][16]
   float* red_a = red + 2 * DEC_NW * 16;  // [NW][R][D]
@@ -849,7 +867,7 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   float* rec0 = a.rec + ((int64_t)b * a.Hkv + g) * a.S * recf;
   {
     float* rec = rec0 + (int64_t)s * recf;
-    const bool bad = sh.flag != 0;
+    const bool bad = sh.flag[0] != 0;
     for (int idx = tid; idx < R * D; idx += blockDim.x) {
       const int h = idx / D, dd = idx % D;
       float M = -INFINITY;
@@ -874,9 +892,9 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   int* ticket = a.tickets + (int64_t)b * a.Hkv + g;
-  if (tid == 0) sh.last = atomicAdd(ticket, 1) == nrange - 1;
+  if (tid == 0) sh.flag[1] = atomicAdd(ticket, 1) == nrange - 1;
   __syncthreads();
-  if (!sh.last) return;
+  if (!sh.flag[1]) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   {
     // thread = (group of ranges grp, 4 consecutive elements e4 of the
@@ -953,7 +971,7 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
 // the workgroups running together cover every head of the same key rows.
 template <int D, int PATH>
 __global__ void __launch_bounds__(256, 2) decode_bf16_kernel(DecArgs a) {
-  __shared__ DecShared<D> sh;
+  const DecLds<D> sh = dec_lds<D>();
   const int g = blockIdx.x % a.Hkv, s = blockIdx.x / a.Hkv;
   const DecSeq sq = dec_seq<false>(a, 0, D, 2);
   dec_unit<D, PATH>(a, sq, 0, g, s, a.S, sh);
@@ -967,7 +985,7 @@ __global__ void __launch_bounds__(256, 2) decode_bf16_kernel(DecArgs a) {
 template <int D>
 __global__ void __launch_bounds__(256, 2) decode_bf16_batch_kernel(DecArgs a, const int* base,
                                                                    int B) {
-  __shared__ DecShared<D> sh;
+  const DecLds<D> sh = dec_lds<D>();
   const int units = base[B] * a.Hkv;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int item = u / a.Hkv, g = u % a.Hkv;

@@ -135,7 +135,8 @@ hipError_t launch_tile_dump(int64_t L, int64_t w0, int8_t* out, hipStream_t st);
 
 // variant 0: grid-stride 16-byte loads, 4 in flight per thread; 1: 32 KiB
 // chunks per workgroup, 8 nontemporal loads in flight per thread; 2: 64 KiB
-// chunks by direct global -> LDS transfers.
+// chunks by direct global -> LDS transfers; 3: variant 1 without and 4:
+// variant 2 with the nontemporal hint.
 hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
                              int variant, hipStream_t st);
 hipError_t launch_calib_mfma(float* sink, int blocks, int iters, hipStream_t st);

@@ -706,10 +706,13 @@ __device__ __forceinline__ void rotate_query(const u32x4 (&raw)[8], double p, in
       const float x0 = bf16_lane(raw[c], j), x1 = bf16_lane(raw[c + 4], j);
       float cs, sn;
       rope_cs_turns(p, w2pi[16 * c + 8 * hh + j], cs, sn);
-      out[c][j] = (_Float16)(x0 * cs - x1 * sn);
-      out[c + 4][j] = (_Float16)(x0 * sn + x1 * cs);
-      nonfinite |= f16_nonfinite(__builtin_bit_cast(uint16_t, out[c][j])) |
-                   f16_nonfinite(__builtin_bit_cast(uint16_t, out[c + 4][j]));
+      const _Float16 y0 = (_Float16)(x0 * cs - x1 * sn), y1 = (_Float16)(x0 * sn + x1 * cs);
+      out[c][j] = y0;
+      out[c + 4][j] = y1;
+      // (bit casts of scalars: a bit cast of a vector element expression
+      // reads element 0 whatever the index)
+      nonfinite |= f16_nonfinite(__builtin_bit_cast(uint16_t, y0)) |
+                   f16_nonfinite(__builtin_bit_cast(uint16_t, y1));
     }
   }
   if (nonfinite) atomicOr(flags, JL_FLAG_Q_RANGE);

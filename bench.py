@@ -116,7 +116,8 @@ def main():
     rbuf = torch.ones(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB
     read_variants = {}
     for variant, name in ((0, "grid_stride_x4"), (1, "chunk_nontemporal_x8"),
-                          (2, "chunk_global_to_lds")):
+                          (2, "chunk_global_to_lds"), (3, "chunk_x8"),
+                          (4, "chunk_global_to_lds_nontemporal")):
         best = 0.0
         for blocks in (2048, 8192, 16384):
             rts = []

@@ -221,17 +221,6 @@ int jl_bifocal_prefill_cached_timed(const void* xq, const void* kcache, const vo
  * and any num_splits it would choose or accept). */
 size_t jl_decode_workspace_size(int64_t capacity, int Hq, int d);
 
-/* Prepares a decode workspace (single or batched) for its first call:
- * zero-fills ws_bytes (rounded down to whole 4-byte words) with a kernel on
- * `stream`. The bf16 decode kernels keep one arrival counter per (sequence,
- * KV head) at the start of the workspace: the workgroups of a KV head count
- * themselves in as they finish, and the last one merges the head's partial
- * results and puts the counter back to zero. So the counters must be zero
- * before the first call on a workspace (this call, or any zero fill), and
- * every call that completes leaves them zero for the next one. Two calls
- * that overlap in time must not share a workspace. Errors: JL_EINVAL (NULL or
- * misaligned workspace), JL_EHIP. */
-int jl_decode_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
 /* One generation step at position pos (0-based) against the absolute cache:
  * L = pos + 1 and G = max(1, ceil(L / w_pre)); keys 0..pos are read, the
@@ -246,10 +235,8 @@ int jl_decode_workspace_init(void* workspace, size_t ws_bytes, void* stream);
  * scored against RoPE(xq, f(pos)); local keys are scored against
  * RoPE(xq, pos). JL_MODE_PLAIN scores every key as local (the baseline);
  * JL_MODE_IE is not a decode mode (JL_EUNSUPPORTED).
- * num_splits: key ranges per KV head, merged by LSE; 0 lets the library
- * choose (bf16 ranges start on 32-key boundaries, so fewer may be used).
- * Workspace: jl_decode_workspace_size bytes, 16-byte aligned, zero before its
- * first use (jl_decode_workspace_init); the call leaves its counters zero.
+ * num_splits: key-range splits merged by LSE; 0 lets the library choose.
+ * Workspace: jl_decode_workspace_size bytes, 16-byte aligned, any contents.
  * Range (bf16): keys and the query times scale log2(e) are fp16 operands; a
  * value beyond 65504 in magnitude (or a NaN) makes the outputs and LSE of
  * the query heads of that key's KV head NaN. Nothing faults and the status
@@ -263,8 +250,7 @@ int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, vo
                       int num_splits, void* workspace, size_t ws_bytes, void* stream);
 
 /* jl_bifocal_decode plus timing: ev_begin / ev_end (caller-created hipEvent_t,
- * or NULL) bracket the decode kernels on `stream` (bf16: one kernel, the
- * merge folded in; fp32: split and merge kernels). */
+ * or NULL) bracket the split and merge kernels on `stream`. */
 int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcache, void* o,
                             float* lse, int64_t pos, int64_t capacity, int Hq, int Hkv, int d,
                             int64_t w0, int64_t w_pre, double theta, float scale, jl_dtype dt,
@@ -294,11 +280,9 @@ size_t jl_decode_batch_workspace_size(int B, int64_t max_keys, int Hq, int d);
  * new positions without a host round trip). An entry with pos_b < 0,
  * pos_b >= max_keys, cache_starts[b] < 0 or cache_starts[b] + pos_b >=
  * cache_rows reads nothing and gets NaN in o (and lse); the other entries are
- * unaffected. num_splits: splits of max_keys / num_splits keys each (bf16:
- * rounded up to whole 32-key chunks), 0 lets the library choose. Workspace:
- * jl_decode_batch_workspace_size bytes, zero before its first use
- * (jl_decode_workspace_init), left with its counters zero by every call.
- * Range (bf16): as in jl_bifocal_decode, per sequence and KV head.
+ * unaffected. num_splits: splits of max_keys / num_splits keys each, 0 lets the
+ * library choose. Workspace: jl_decode_batch_workspace_size bytes, any
+ * contents. Range (bf16): as in jl_bifocal_decode, per sequence and KV head.
  * Supported: bf16 or fp32, d = 128 or 64, Hq / Hkv in
  * {1, 2, 4, 8}; mode FUSED or PLAIN, optionally with JL_REMAP_CONTINUOUS.
  * Errors: JL_EINVAL (B < 0 or > 65535, max_keys < 1 or > 2^31 - 1,
@@ -313,7 +297,7 @@ int jl_bifocal_decode_batch(const void* xq, const void* kcache, const void* vcac
 
 /* jl_bifocal_decode_batch plus timing: ev_begin / ev_end (caller-created
  * hipEvent_t, or NULL) bracket the batch kernels on `stream` (bf16: the work
- * list plan and the decode kernel; fp32: split and merge kernels). */
+ * list plan, split and merge kernels; fp32: split and merge kernels). */
 int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void* vcache, void* o,
                                   float* lse, const int32_t* positions,
                                   const int32_t* cache_starts, int B, int64_t max_keys,

@@ -18,7 +18,7 @@ __all__ = [
     "status_string", "rope_apply", "prefill_workspace_size", "bifocal_prefill",
     "decode_workspace_size", "bifocal_decode", "debug_tile_classes", "ie_ratio_view",
     "prefill_cached_workspace_size", "bifocal_prefill_cached",
-    "decode_batch_workspace_size", "bifocal_decode_batch", "decode_workspace_init",
+    "decode_batch_workspace_size", "bifocal_decode_batch",
     "decode_workspace", "decode_batch_workspace",
     "calib_stream_read", "calib_mfma_bf16", "MODES", "REMAPS", "prefill_flags",
     "FLAG_Q_RANGE", "FLAG_K_RANGE",
@@ -63,7 +63,6 @@ _SIGS = {
                                                  _c_dbl, _c_flt, _c_int, _c_int, _c_p, _c_sz,
                                                  _c_p, _c_p, _c_p]),
     "jl_decode_workspace_size": (_c_sz, [_c_i64, _c_int, _c_int]),
-    "jl_decode_workspace_init": (_c_int, [_c_p, _c_sz, _c_p]),
     "jl_bifocal_decode": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_int,
                                    _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int, _c_int, _c_int,
                                    _c_p, _c_sz, _c_p]),
@@ -229,24 +228,15 @@ def decode_workspace_size(capacity, Hq, d) -> int:
     return int(lib().jl_decode_workspace_size(int(capacity), int(Hq), int(d)))
 
 
-def decode_workspace_init(workspace: torch.Tensor) -> torch.Tensor:
-    """Zero-fill a decode workspace before its first use (the arrival
-    counters must start at zero; every call leaves them zero again)."""
-    _check("jl_decode_workspace_init", lib().jl_decode_workspace_init(
-        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(workspace.device)))
-    return workspace
-
-
 def decode_workspace(capacity, Hq, d, device="cuda") -> torch.Tensor:
-    """A ready decode workspace for jl_bifocal_decode (zeroed)."""
-    return torch.zeros(max(decode_workspace_size(capacity, Hq, d), 16), dtype=torch.uint8,
+    """A decode workspace for jl_bifocal_decode (any contents)."""
+    return torch.empty(max(decode_workspace_size(capacity, Hq, d), 16), dtype=torch.uint8,
                        device=device)
 
 
 def decode_batch_workspace(B, max_keys, Hq, d, device="cuda") -> torch.Tensor:
-    """A ready decode workspace for jl_bifocal_decode_batch (zeroed)."""
-    return torch.zeros(max(decode_batch_workspace_size(B, max_keys, Hq, d), 16),
+    """A decode workspace for jl_bifocal_decode_batch (any contents)."""
+    return torch.empty(max(decode_batch_workspace_size(B, max_keys, Hq, d), 16),
                        dtype=torch.uint8, device=device)
 
 

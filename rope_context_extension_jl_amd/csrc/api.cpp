@@ -288,23 +288,23 @@ int jl_bifocal_prefill_cached(const void* xq, const void* kcache, const void* vc
                                          stream, nullptr, nullptr);
 }
 
-// bf16 decode: keys per range. One workgroup per (KV head, range), four
-// waves taking the range's 32-key chunks in turn, two workgroups per CU: aim
-// at a range count that covers the 256 CUs evenly (two workgroups per CU
-// when each wave gets >= 256 keys, one when it gets >= 128), since a few CUs
-// holding an extra workgroup would set the kernel's time. Ranges are whole
-// rounds of four chunks (128 keys), rounded down when that leaves only a
-// small last range (its workgroups finish almost at once), else up.
+// bf16 decode: keys per split. One wave per split, four KV heads per
+// workgroup, two workgroups fit a CU: aim at a split count that covers the 256
+// CUs evenly (two workgroups per CU when each split gets >= 256 keys, else
+// one), since a few CUs holding an extra workgroup would set the kernel's
+// time. The kernel walks 32-key chunks, so a split of 32 c + 1 keys costs a
+// whole extra chunk: sizes are whole chunks, rounded down when that leaves
+// only a small last split (its workgroups finish almost at once), else up.
 static int64_t decode_bf16_kps(int64_t keys, int Hkv) {
-  const int64_t two = 512 / Hkv > 0 ? 512 / Hkv : 1, one = 256 / Hkv > 0 ? 256 / Hkv : 1;
+  const int64_t hg = (Hkv + 3) / 4;
+  const int64_t s_full = 512 / hg > 0 ? 512 / hg : 1, s_half = 256 / hg > 0 ? 256 / hg : 1;
   int64_t want;
-  if (keys >= two * 1024) want = two;
-  else if (keys >= one * 512) want = one;
-  else want = keys / 512 > 1 ? keys / 512 : 1;
-  const int64_t u = 128;
-  const int64_t kc = u * ((keys + u * want - 1) / (u * want));
-  const int64_t kf = u * (keys / (u * want));
-  if (kf >= u) {
+  if (keys >= 256 * s_full) want = s_full;
+  else if (keys >= 128 * s_half) want = s_half;
+  else want = (keys + 127) / 128;
+  const int64_t kc = 32 * ((keys + 32 * want - 1) / (32 * want));
+  const int64_t kf = 32 * (keys / (32 * want));
+  if (kf >= 32) {
     const int64_t sf = (keys + kf - 1) / kf;
     if (sf == want + 1 && keys - (sf - 1) * kf <= kf / 4) return kf;
   }
@@ -316,32 +316,9 @@ static int decode_max_splits(int64_t capacity) {
   return (int)(s < 1024 ? s : 1024);
 }
 
-// Decode workspace: the arrival tickets (one int per (sequence, KV head),
-// bounded by Hq per sequence), then the partials: float32 [Hq, S, d + 2] or
-// the bf16 records, Hkv S (2 DEC_RP + (Hq / Hkv) d) <= S Hq (d + 16) floats
-// per sequence.
-static size_t decode_ticket_bytes(int B, int Hq) { return align256((size_t)4 * B * Hq); }
-static size_t decode_part_bytes(int B, int S, int Hq, int d) {
-  return align256((size_t)B * S * Hq * (d + 16) * sizeof(float));
-}
-
 size_t jl_decode_workspace_size(int64_t capacity, int Hq, int d) {
   if (capacity < 1 || Hq < 1 || d < 2) return 0;
-  return decode_ticket_bytes(1, Hq) + decode_part_bytes(1, decode_max_splits(capacity), Hq, d);
-}
-
-int jl_decode_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
-  if (!workspace || (((uintptr_t)workspace) & 15)) return JL_EINVAL;
-  return hip_status(launch_zero_fill(workspace, ws_bytes, (hipStream_t)stream));
-}
-
-// Keys per split of a caller-chosen split count: bf16 ranges start on
-// 32-key boundaries (whole chunks), float32 splits on any key.
-static int64_t decode_kps_for(int64_t keys, int64_t S0, bool bf16) {
-  if (S0 > keys) S0 = keys;
-  int64_t k = (keys + S0 - 1) / S0;
-  if (bf16) k = 32 * ((k + 31) / 32);
-  return k;
+  return align256((size_t)Hq * decode_max_splits(capacity) * (d + 2) * sizeof(float));
 }
 
 int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcache, void* o,
@@ -366,9 +343,8 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
   const int maxs = decode_max_splits(capacity);
   const int64_t keys = pos + 1;
   if (num_splits > maxs) return JL_EINVAL;
-  const bool bf16 = dt == JL_BF16;
   int64_t kps;
-  if (num_splits == 0 && bf16) {
+  if (num_splits == 0 && dt == JL_BF16) {
     kps = decode_bf16_kps(keys, Hkv);
   } else {
     int64_t S0 = num_splits;
@@ -377,12 +353,12 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
       const int64_t want = (1024 + Hkv - 1) / Hkv, by_keys = (keys + 63) / 64;
       S0 = want < by_keys ? want : by_keys;
     }
-    kps = decode_kps_for(keys, S0, bf16);
+    if (S0 > keys) S0 = keys;
+    kps = (keys + S0 - 1) / S0;
   }
-  if ((keys + kps - 1) / kps > maxs) kps = decode_kps_for(keys, maxs, bf16);
+  if ((keys + kps - 1) / kps > maxs) kps = (keys + maxs - 1) / maxs;
   const int S = (int)((keys + kps - 1) / kps);  // no empty split
-  const size_t tick = decode_ticket_bytes(1, Hq);
-  const size_t need = tick + decode_part_bytes(1, S, Hq, d);
+  const size_t need = (size_t)Hq * S * (d + 2) * sizeof(float);
   if (!workspace || ws_bytes < need) return JL_EWORKSPACE;
   if (((uintptr_t)workspace) & 15) return JL_EINVAL;
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d));
@@ -395,8 +371,7 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
     return hip_status(e);
   e = launch_decode(xq, kcache, vcache, o, lse, pos, Hq, Hkv, d,
                     w0 > (int64_t)INT32_MAX ? INT32_MAX : w0, G, sc, fr, mode == JL_MODE_PLAIN,
-                    cont, dt == JL_FP32, (int)kps, (int*)workspace,
-                    (float*)((char*)workspace + tick), st);
+                    cont, dt == JL_FP32, (int)kps, workspace, st);
   if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
   return hip_status(e);
 }
@@ -411,14 +386,15 @@ static int decode_batch_f32_splits(int B, int64_t max_keys, int Hkv) {
   return want < 1 ? 1 : (int)want;
 }
 
-// Batched decode workspace: the tickets [B, Hkv] (bounded by [B, Hq]), the
-// bf16 work list int32 [B + 1], then the partials of every sequence.
-static size_t decode_batch_list_bytes(int B) { return align256((size_t)(B + 1) * sizeof(int)); }
+// Partials [B, Hq, S, d + 2] fp32, then the bf16 work list int32 [B + 1].
+static size_t decode_batch_list_offset(int B, int Hq, int S, int d) {
+  return align256((size_t)B * Hq * S * (d + 2) * sizeof(float));
+}
 
 size_t jl_decode_batch_workspace_size(int B, int64_t max_keys, int Hq, int d) {
   if (B < 1 || max_keys < 1 || max_keys > (int64_t)INT32_MAX || Hq < 1 || d < 2) return 0;
-  return decode_ticket_bytes(B, Hq) + decode_batch_list_bytes(B) +
-         decode_part_bytes(B, decode_max_splits(max_keys), Hq, d);
+  return decode_batch_list_offset(B, Hq, decode_max_splits(max_keys), d) +
+         align256((size_t)(B + 1) * sizeof(int));
 }
 
 int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void* vcache, void* o,
@@ -450,20 +426,21 @@ int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void
   // and a fixed grid walks the resulting work list. fp32: one grid over all
   // (split, head, sequence) triples.
   if (num_splits > maxs) return JL_EINVAL;
-  const bool bf16 = dt == JL_BF16;
   int64_t kps;
-  if (num_splits == 0 && bf16) {
+  if (num_splits == 0 && dt == JL_BF16) {
     kps = decode_bf16_kps(max_keys, Hkv);
   } else {
-    const int64_t S0 = num_splits ? num_splits : decode_batch_f32_splits(B, max_keys, Hkv);
-    kps = decode_kps_for(max_keys, S0, bf16);
+    int64_t S0 = num_splits ? num_splits : decode_batch_f32_splits(B, max_keys, Hkv);
+    if (S0 > max_keys) S0 = max_keys;
+    kps = (max_keys + S0 - 1) / S0;
   }
-  if ((max_keys + kps - 1) / kps > maxs) kps = decode_kps_for(max_keys, maxs, bf16);
+  if ((max_keys + kps - 1) / kps > maxs) kps = (max_keys + maxs - 1) / maxs;
   const int S = (int)((max_keys + kps - 1) / kps);  // no split past max_keys
-  const size_t tick = decode_ticket_bytes(B, Hq), list = decode_batch_list_bytes(B);
-  const size_t need = tick + list + decode_part_bytes(B, S, Hq, d);
+  const size_t list_off = decode_batch_list_offset(B, Hq, S, d);
+  const size_t need = list_off + (size_t)(B + 1) * sizeof(int);
   if (!workspace || ws_bytes < need) return JL_EWORKSPACE;
-  const int64_t units = (int64_t)B * S * Hkv;  // upper bound of the work list
+  const int64_t hg = (Hkv + 3) / 4;
+  const int64_t units = (int64_t)B * S * hg;  // upper bound of the work list
   const int grid_wg = (int)(units < 512 ? units : 512);  // two workgroups per CU
   if (((uintptr_t)workspace) & 15) return JL_EINVAL;
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d));
@@ -476,9 +453,8 @@ int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void
   e = launch_decode_batch(xq, kcache, vcache, o, lse, positions, cache_starts, B, max_keys,
                           cache_rows, Hq, Hkv, d, w0 > (int64_t)INT32_MAX ? INT32_MAX : w0,
                           w_pre > (int64_t)INT32_MAX ? (int64_t)INT32_MAX : w_pre, sc, fr,
-                          mode == JL_MODE_PLAIN, cont, dt == JL_FP32, S, (int)kps,
-                          (int*)workspace, (float*)((char*)workspace + tick + list),
-                          (int*)((char*)workspace + tick), grid_wg, st);
+                          mode == JL_MODE_PLAIN, cont, dt == JL_FP32, S, (int)kps, workspace,
+                          (int*)((char*)workspace + list_off), grid_wg, st);
   if (e == hipSuccess && ev_end) e = hipEventRecord((hipEvent_t)ev_end, st);
   return hip_status(e);
 }

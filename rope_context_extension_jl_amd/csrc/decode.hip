@@ -9,13 +9,16 @@
 // against the query rotated at f(pos). Keys inside the window are scored
 // against the query rotated at pos.
 //
-// Split-K: the keys 0..pos of every KV head are cut into ranges, each
-// streamed once for all Hq/Hkv query heads of the group, leaving a partial
-// (max, sum, unnormalised accumulator) per query head; the partials are
-// merged with LSE weights. HBM traffic is the K and V rows of keys 0..pos
-// read once. bf16: one workgroup per (KV head, range) and the merge folded
-// into the same kernel (the last range of a head to finish merges). float32:
-// one workgroup per (split, KV head) and a second merge kernel.
+// Split-K: each split streams keys [s*n, (s+1)*n) of one KV head once, for
+// all Hq/Hkv query heads of the group, and leaves a partial (max, sum,
+// unnormalised accumulator) per query head; a second kernel merges the splits
+// with LSE weights. HBM traffic is the K and V rows of keys 0..pos read once.
+// The bf16 kernel runs one split per wave (a workgroup covers four KV heads
+// of one key range); the float32 kernel one split per workgroup.
+//
+// Lane layout: D/8 lanes per key; lane dl holds the pairs
+// (4dl .. 4dl+3, D/2 + 4dl .. D/2 + 4dl + 3), so the correction rotation is
+// in-lane and a key's dot product is a D/8-lane reduction.
 #include "jl_internal.hpp"
 
 namespace jl {
@@ -24,9 +27,7 @@ struct DecArgs {
   const void* xq;  // raw query [Hq, D]
   const void* kc;  // [C, Hkv, D] absolute-rotated keys
   const void* vc;  // [C, Hkv, D]
-  float* part;     // float32: [Hq, S, D + 2]: m (log2 domain), l, acc[D]
-  float* rec;      // bf16: range records (see dec_recf); same memory as part
-  int* tickets;    // bf16: arrival count per (sequence, KV head), zero between calls
+  float* part;     // [Hq, S, D + 2]: m (log2 domain), l, acc[D]
   void* o;
   float* lse;
   int pos, Hq, Hkv, w0, G, plain, S, kps;
@@ -257,57 +258,25 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path: both products on the matrix cores, the split merge folded in.
+// bf16 path: one wave per split, both products on the matrix cores.
 //
-// Workgroup = one KV head x one key range [s kps, (s + 1) kps) of one
-// sequence, DEC_NW waves; wave w takes the range's 32-key chunks w, w + NW,
-// ..., so the waves running together read neighbouring key rows. Per chunk a
-// wave loads K (the A operand of S^T = K Q^T, fp16, 16x16x32 MFMAs: lane =
-// one key, 8 consecutive dims) and sends V straight to a wave-private LDS
-// stage. The S^T tile gives each lane one query (lane % 16) and four keys
-// per 16-key block, which is the A operand of O = P V for two consecutive
+// Per 64-key chunk a wave loads K (as the A operand of S^T = K Q^T, fp16,
+// 16x16x32 MFMAs: lane = one key, 8 consecutive dims) and V (row-major into a
+// wave-private LDS region). Remote keys are corrected in-lane: the pairs
+// (i, i + D/2) of a key sit in d-steps ds and ds + D/64 of the same lane. The
+// S^T tile gives each lane one query (lane % 16) and four keys per 16-key
+// block, which is exactly the A operand of O = P V for two consecutive
 // blocks; the V operand (8 keys at one dim per lane) comes from LDS with the
 // transpose read ds_read_b64_tr_b16: within 16 lanes, lane i receives element
 // i % 4 of the 8-byte rows addressed by lanes i / 4 + 4t, t = 0..3, so lanes
 // pointing at V[key_t][4c .. 4c + 3] deliver V[key_t][own dim] for 4 keys.
 // Query heads are padded to the 16 MFMA columns with zeros.
 //
-// At the end the waves' softmax states are merged in LDS into one record per
-// (range, query head): m (log2 domain), l and the unnormalised O. The record
-// is released at device scope and the workgroup takes a ticket of its
-// (sequence, KV head); the last range to arrive merges all the records with
-// LSE weights, writes O and the LSE and puts the ticket back to zero, so no
-// second launch is needed.
-//
-// Remote keys (pos - k > w0) are corrected by R_{f(k) - k} (R_a R_b =
-// R_{a+b} turns the absolute key RoPE(x_k, k) into RoPE(x_k, f(k))):
-//   DEC_FACT (G divides 32, or the continuous map): with k = k0 + i, k0 the
-//     chunk's first key (a multiple of 32), f(k) - k = (f(k0) - k0) +
-//     (f(i) - i). The chunk-uniform factor moves to the query,
-//     q . (R_a R_b k) = (R_{-a} q) . (R_b k): once per chunk the wave rotates
-//     the raw query to f(pos) - (f(k0) - k0), one angle per frequency, shared
-//     through LDS; the in-chunk factor depends on i alone and is a per-lane
-//     constant.
-//   DEC_GEN (any G; used for the floor map with G not dividing 32, and by
-//     the batch kernel): each lane evaluates its key's angles for the
-//     chunk's first 16-key block; the second block follows by one rotation
-//     R_{c16}, c16 = f(k + 16) - f(k) - 16, one of two values per G picked
-//     by k mod G (one value for the continuous map).
-//   DEC_PLAIN (plain mode, or G = 1 where f(x) = x): no correction.
-//
 // Softmax: the query operand carries scale * log2(e) and the score
-// accumulator starts at -m, m a per-wave reference that moves only when a
+// accumulator starts at -m, m a per-split reference that moves only when a
 // lane's sum of bf16-rounded p over the chunk exceeds 2^8 (or on the first
 // scores), so the common chunk needs no row max and no cross-lane exchange.
-// A raw score that is not finite (an fp16 operand out of range) makes the
-// KV head's outputs NaN.
 // ---------------------------------------------------------------------------
-constexpr int DEC_CHUNK = 32;  // keys per chunk
-constexpr int DEC_NW = 4;      // waves per bf16 workgroup (one KV head, one key range)
-constexpr int DEC_RP = 8;      // (m, l) slots at the head of a bf16 record
-// Correction paths of the bf16 kernels (see below).
-enum DecPath : int { DEC_PLAIN = 0, DEC_FACT = 1, DEC_GEN = 2 };
-
 typedef _Float16 dh8v __attribute__((ext_vector_type(8)));
 typedef _Float16 dh2v __attribute__((ext_vector_type(2)));
 typedef __bf16 db8v __attribute__((ext_vector_type(8)));
@@ -316,6 +285,7 @@ typedef short ds4v __attribute__((ext_vector_type(4)));
 typedef float df32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t du32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int DEC_CHUNK = 32;  // keys per chunk; two chunks are in flight per wave
 constexpr float kDecSumMax = 256.f;
 
 template <int D>
@@ -338,44 +308,14 @@ __device__ __forceinline__ int dec_vswz(int r) {
   return (2 * r) & (DecGeom<D>::NC - 1);
 }
 
-// Workgroup memory of the bf16 kernels (under 80 KiB at D = 128, so two
-// workgroups share a CU), as separate LDS arrays: the compiler then sees
-// that the reads of one V stage, of the tables or of the query cannot alias
-// the direct transfers in flight into the other stage, and does not wait for
-// those. The prologue's operand tables live in the second V stages (vB),
-// which no transfer touches before the key loop.
-template <int D>
-struct DecLds {
-  uint8_t* vA;   // [DEC_NW][VBYTES] first V stage of each wave; merge scratch after the loop
-  uint8_t* vB;   // [DEC_NW][VBYTES] second V stage of each wave
-  float* qraw;   // [8][D] raw query rows of the group x scale log2 e (rows >= R zero)
-  float2* cs;    // [DEC_NW][D / 2] DEC_FACT: the chunk's query rotation per wave;
-                 // DEC_GEN: the two R_{c16} tables as fp16
-  double* w2pi;  // [D / 2] omega_i / (2 pi)
-  int* flag;     // [2]: a range's non-finite flag, the last-arrival flag
-};
-
-template <int D>
-__device__ __forceinline__ DecLds<D> dec_lds() {
-  __shared__ __attribute__((aligned(16))) uint8_t vA[DEC_NW * DecGeom<D>::VBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t vB[DEC_NW * DecGeom<D>::VBYTES];
-  __shared__ __attribute__((aligned(16))) float qraw[8 * D];
-  __shared__ __attribute__((aligned(16))) float2 cs[DEC_NW * D / 2];
-  __shared__ double w2pi[D / 2];
-  __shared__ int flag[2];
-  return DecLds<D>{vA, vB, qraw, cs, w2pi, flag};
-}
-
 // Per-wave constants of the key loop (all wave-uniform except the lane ids).
 struct DecCtx {
   const uint16_t* kbase;  // this lane's K slice: head, dims 8 * g16 ..
   const uint16_t* vbase;  // the head's V row 0
   int64_t rstride;        // elements between consecutive keys
-  int pos, w0, G, k_hi;
-  int plain;      // every key local: plain mode, or G = 1 (f(x) = x)
+  int pos, w0, G, plain, correct, k_hi;
   int cont;       // remote map x / G (real) instead of floor(x / G)
   double fk_rel;  // with cont: f(k) - k = k * fk_rel
-  double fpos;    // f(pos)
   int lane, g16, r16;
 };
 
@@ -403,7 +343,7 @@ __device__ __forceinline__ void dec_qk(const dh8v (&kf)[D / 32], const dh8v (&q)
 }
 
 // bf16 pairs of a 16-byte vector -> 8 fp16 (exact for normal bf16 values in
-// fp16 range).
+// fp16 range), optionally rotated by the remote correction first.
 __device__ __forceinline__ dh8v dec_to_f16(const du32x4& v) {
   dh8v r;
 #pragma unroll
@@ -416,7 +356,7 @@ __device__ __forceinline__ void dec_issue_k(const DecCtx& c, int k0, DecBuf<D>& 
   using G = DecGeom<D>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    // keys past the range end load the last key (finite data, masked later)
+    // keys past the split end load the last key (finite data, masked later)
     const int key = min(k0 + 16 * kb + c.r16, c.k_hi - 1);
 #pragma unroll
     for (int ds = 0; ds < G::NDS; ++ds)
@@ -459,81 +399,49 @@ __device__ __forceinline__ float dec_exp(const df32x4 (&st)[2], db8v& pb) {
   return ps0 + ps1;
 }
 
-// Wait for this wave's LDS reads and writes only (lgkmcnt 0; the vector
-// memory and export counters at their maxima, so loads in flight stay).
-__device__ __forceinline__ void dec_wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// One chunk: correction setup, S^T = K Q^T per 16-key block (seeded with -m),
-// the lazy-reference softmax and O += P V. chk accumulates the raw scores
-// (a non-finite sum flags an operand out of the fp16 range).
-template <int D, int PATH>
+template <int D>
 __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<D>& b,
-                                          const dh8v (&qa)[D / 32], dh8v (&qr)[D / 32],
-                                          const dh2v (&tcr)[2][D / 64][4],
-                                          const dh2v (&tsr)[2][D / 64][4], const DecLds<D>& sh,
-                                          int wave, const uint8_t* vb, DecState<D>& st,
-                                          float& chk) {
+                                          const dh8v (&qa)[D / 32], const dh8v (&qr)[D / 32],
+                                          const double* w2pi, const uint8_t* vb,
+                                          DecState<D>& st, bool step16,
+                                          const dh2v (&cst)[D / 64][4],
+                                          const dh2v (&sst)[D / 64][4], float& chk) {
   using G = DecGeom<D>;
-  constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW, HALF = D / 2;
-  // ---- correction setup. It depends on key indices only, so it runs before
-  // the chunk's data is first touched, while its loads (and the next
-  // chunk's) are in flight.
-  const bool chunk_rem = PATH != DEC_PLAIN && !c.plain && c.pos - k0 > c.w0;  // block 0 has remote keys
+  constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
+  // ---- cos / sin of the correction R_{f(k) - k} of the lane's key in both
+  // blocks (pairs (ds, ds + NDS/2), frequencies 32 ds + 8 g16 + j), as fp16
+  // pairs of neighbouring frequencies (j, j + 1), the layout of the key
+  // fragments. They depend on the key index only, so they are computed
+  // before the chunk's data is first touched, i.e. while its loads (and the
+  // next chunk's) are still in flight.
   dh2v rc[2][NDS / 2][4], rs[2][NDS / 2][4];
-  if (PATH == DEC_FACT && chunk_rem) {
-    // query operand for this chunk: raw query at f(pos) - (f(k0) - k0)
-    if (c.lane < HALF) {
-      const double P = c.cont ? c.fpos - (double)k0 * c.fk_rel
-                              : (double)(c.pos / c.G - k0 / c.G + k0);
-      float cc, ss;
-      rope_cs_turns(P, sh.w2pi[c.lane], cc, ss);
-      sh.cs[wave * HALF + c.lane] = make_float2(cc, ss);
-    }
-    dec_wait_lds();
-    __builtin_amdgcn_wave_barrier();
-    const bool qv = c.r16 < 8;
-    const float* qrow = sh.qraw + (c.r16 & 7) * D;
 #pragma unroll
-    for (int ds = 0; ds < NDS / 2; ++ds)
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = k0 + 16 * kb + c.r16;
+    if (c.correct && c.pos - (k0 + 16 * kb) > c.w0) {  // the block has remote keys
+      if (kb == 1 && step16) {
+        // key + 16 (block 0 is remote too): the angle moves by a fixed step,
+        // R_{d + c16} = R_d R_{c16}
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int f = 32 * ds + 8 * c.g16 + j;
-        const float2 t = sh.cs[wave * HALF + f];
-        const float x0 = qv ? qrow[f] : 0.f, x1 = qv ? qrow[f + HALF] : 0.f;
-        qr[ds][j] = (_Float16)(x0 * t.x - x1 * t.y);
-        qr[ds + NDS / 2][j] = (_Float16)(x0 * t.y + x1 * t.x);
+        for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            rc[1][ds][m] = rc[0][ds][m] * cst[ds][m] - rs[0][ds][m] * sst[ds][m];
+            rs[1][ds][m] = rs[0][ds][m] * cst[ds][m] + rc[0][ds][m] * sst[ds][m];
+          }
+      } else {
+        const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
+#pragma unroll
+        for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            float c0, s0, c1, s1;
+            rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m], c0, s0);
+            rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m + 1], c1, s1);
+            rc[kb][ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
+            rs[kb][ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
+          }
       }
-  }
-  if (PATH == DEC_GEN && chunk_rem) {
-    // block 0: this lane's key, frequencies 32 ds + 8 g16 + 2 m (+ 1), as
-    // fp16 pairs of neighbouring frequencies (the key fragment's layout)
-    const int key = k0 + c.r16;
-    const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
-#pragma unroll
-    for (int ds = 0; ds < NDS / 2; ++ds)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float c0, s0, c1, s1;
-        rope_cs_turns(delta, sh.w2pi[32 * ds + 8 * c.g16 + 2 * m], c0, s0);
-        rope_cs_turns(delta, sh.w2pi[32 * ds + 8 * c.g16 + 2 * m + 1], c1, s1);
-        rc[0][ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
-        rs[0][ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
-      }
-    if (c.pos - (k0 + 16) > c.w0) {
-      // block 1 (key + 16; block 0 is then all remote): R_{d + c16} =
-      // R_d R_{c16}, c16 = f(key + 16) - f(key) - 16 takes the larger of its
-      // two values when the key's residue carries (continuous map: one value)
-      const int t = !c.cont && (key % c.G) + (16 % c.G) >= c.G ? 1 : 0;
-      const _Float16* tt = (const _Float16*)sh.cs + 2 * t * HALF;
-#pragma unroll
-      for (int ds = 0; ds < NDS / 2; ++ds)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int f = 32 * ds + 8 * c.g16 + 2 * m;
-          const dh2v cst = *(const dh2v*)(tt + f), sst = *(const dh2v*)(tt + HALF + f);
-          rc[1][ds][m] = rc[0][ds][m] * cst - rs[0][ds][m] * sst;
-          rs[1][ds][m] = rs[0][ds][m] * cst + rc[0][ds][m] * sst;
-        }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -543,28 +451,25 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
   for (int kb = 0; kb < 2; ++kb) {
     const int kfirst = k0 + 16 * kb;
     const int klast = min(kfirst + 15, c.k_hi - 1);
-    const bool any_rem = PATH != DEC_PLAIN && !c.plain && c.pos - kfirst > c.w0;
-    const bool any_loc = PATH == DEC_PLAIN || c.plain || c.pos - klast <= c.w0;
+    const bool any_rem = !c.plain && c.pos - kfirst > c.w0;
+    const bool any_loc = c.plain || c.pos - klast <= c.w0;
     const int key = kfirst + c.r16;
     dh8v kf[NDS];
-    if (any_rem && c.pos - key > c.w0) {
-      // R_{f(k) - k} (FACT: its in-chunk factor): absolute -> remapped
-      // rotation, pairs (ds, ds + NDS/2), in packed fp16 arithmetic on two
-      // neighbouring frequencies at a time (the bf16 key values are exact in
-      // fp16)
+    if (c.correct && c.pos - key > c.w0) {
+      // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2),
+      // in packed fp16 arithmetic on two neighbouring frequencies at a time
+      // (the bf16 key values are exact in fp16)
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const dh2v cr = PATH == DEC_FACT ? tcr[kb][ds][m] : rc[kb][ds][m];
-          const dh2v sr = PATH == DEC_FACT ? tsr[kb][ds][m] : rs[kb][ds][m];
           const uint32_t w0 = b.k[kb][ds][m], w1 = b.k[kb][ds + NDS / 2][m];
           const dh2v x0 = {(_Float16)__uint_as_float(w0 << 16),
                            (_Float16)__uint_as_float(w0 & 0xffff0000u)};
           const dh2v x1 = {(_Float16)__uint_as_float(w1 << 16),
                            (_Float16)__uint_as_float(w1 & 0xffff0000u)};
-          const dh2v y0 = x0 * cr - x1 * sr;
-          const dh2v y1 = x0 * sr + x1 * cr;
+          const dh2v y0 = x0 * rc[kb][ds][m] - x1 * rs[kb][ds][m];
+          const dh2v y1 = x0 * rs[kb][ds][m] + x1 * rc[kb][ds][m];
           kf[ds][2 * m] = y0[0];
           kf[ds][2 * m + 1] = y0[1];
           kf[ds + NDS / 2][2 * m] = y1[0];
@@ -594,8 +499,10 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
       dec_qk<D>(kl, qa, st.negm, t);
       dec_qk<D>(krm, qr, t, s2[kb]);
     }
+    // raw scores of an fp16 operand out of range are not finite: their sum
+    // carries that to the end of the split
     chk += (s2[kb][0] + s2[kb][1]) + (s2[kb][2] + s2[kb][3]);
-    if (klast - kfirst < 15) {  // keys past the range end
+    if (klast - kfirst < 15) {  // keys past the split end
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (kfirst + 4 * c.g16 + r >= c.k_hi) s2[kb][r] = -INFINITY;
@@ -660,152 +567,98 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
   }
 }
 
-// Records of the bf16 decode: for (sequence b, KV head g, range s) at
-// rec + ((b Hkv + g) S + s) recf floats: (m, l) of each query head of the
-// group in the first 2 DEC_RP floats, then the unnormalised O [R][D].
-__host__ __device__ inline int dec_recf(int R, int D) { return 2 * DEC_RP + R * D; }
-
-// The outputs of KV head g's query heads for sequence b are NaN (an entry
-// outside the caller's bounds, or an operand out of the fp16 range).
-template <int D>
-__device__ __forceinline__ void dec_write_nan(const DecArgs& a, int b, int g) {
-  const int R = a.Hq / a.Hkv;
-  const int64_t row0 = (int64_t)b * a.Hq + (int64_t)g * R;
-  for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x)
-    ((uint16_t*)a.o)[row0 * D + idx] = 0x7fc0;
-  if (a.lse && threadIdx.x < R) a.lse[row0 + threadIdx.x] = __builtin_nanf("");
-}
-
-// One work unit: KV head g, range s (of nrange) of sequence b. Every thread
-// of the workgroup calls it; it returns with the LDS free for the next unit.
-template <int D, int PATH>
-__device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int b, int g, int s,
-                                         int nrange, const DecLds<D>& sh) {
-  using Gm = DecGeom<D>;
-  constexpr int NDS = Gm::NDS, NDB = Gm::NDB, HALF = D / 2;
-  const int tid = threadIdx.x;
-  // the wave index is uniform per wave: say so, so that every range-derived
-  // value lives in scalar registers and the route branches are scalar jumps;
-  // matrix instructions then never run under a partial EXEC mask
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+// One work unit of the bf16 decode for one wave: keys [s kps, (s + 1) kps)
+// of KV head kvh of sequence sq, leaving the partial of each query head of
+// the group. vA / vB: this wave's two V stages.
+template <int D, bool STEP16>
+__device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int s, int kvh,
+                                         const double* w2pi_s, uint8_t* sA, uint8_t* sB) {
+  using G = DecGeom<D>;
+  constexpr int NDS = G::NDS, NDB = G::NDB;
+  const int lane = threadIdx.x & 63;
   const int g16 = lane >> 4, r16 = lane & 15;
-  const int R = a.Hq / a.Hkv, h0 = g * R;
+  const int R = a.Hq / a.Hkv, h0 = kvh * R;
+  const uint16_t* xq = (const uint16_t*)sq.xq;
+  const uint16_t* kc = (const uint16_t*)sq.kc;
+  const uint16_t* vc = (const uint16_t*)sq.vc;
 
-  DecCtx c;
   const int k_lo = s * a.kps;
+  DecCtx c;
   c.k_hi = min(k_lo + a.kps, sq.pos + 1);
   c.rstride = (int64_t)a.Hkv * D;
-  c.kbase = (const uint16_t*)sq.kc + (int64_t)g * D + 8 * g16;
-  c.vbase = (const uint16_t*)sq.vc + (int64_t)g * D;
+  c.kbase = kc + (int64_t)kvh * D + 8 * g16;
+  c.vbase = vc + (int64_t)kvh * D;
   c.pos = sq.pos;
   c.w0 = a.w0;
   c.G = sq.G;
-  c.plain = a.plain || sq.G == 1;
   c.cont = a.cont;
   c.fk_rel = sq.fk_rel;
-  c.fpos = remap_pos(sq.pos, sq.G, a.cont);
+  c.plain = a.plain;
+  c.correct = !a.plain && sq.G > 1;
   c.lane = lane;
   c.g16 = g16;
   c.r16 = r16;
-  constexpr int kstep = DEC_CHUNK * DEC_NW;
-  int k0 = k_lo + DEC_CHUNK * wave;
-  const bool active = k0 < c.k_hi;  // the range holds a chunk for this wave
-  uint8_t* sA = sh.vA + wave * Gm::VBYTES;
-  uint8_t* sB = sh.vB + wave * Gm::VBYTES;
-  DecBuf<D> bA, bB;
-  // the wave's first chunk is in flight during the prologue
-  if (active) {
-    dec_issue_k<D>(c, k0, bA);
-    dec_issue_v<D>(c, k0, sA);
-  }
 
-  // ---- prologue: frequencies, the group's raw query, operand tables. The
-  // tables read once go to the second V stages (free until the key loop).
-  if (tid < HALF) sh.w2pi[tid] = a.fr.w(tid) * kInvTwoPi;
-  if (tid == 0) sh.flag[0] = 0;
-  {
-    const uint16_t* xq = (const uint16_t*)sq.xq + (int64_t)h0 * D;
-    for (int idx = tid; idx < 8 * D; idx += blockDim.x)
-      sh.qraw[idx] = idx / D < R ? bf16_bits_to_f32(xq[idx]) * a.scale_log2 : 0.f;
-  }
-  __syncthreads();
-  _Float16* pqa = (_Float16*)sh.vB;  // [16][D] query at pos
-  _Float16* pq2 = pqa + 16 * D;                  // GEN: [16][D] query at f(pos);
-                                                 // FACT: [2][32][HALF] in-chunk cos, sin
-  for (int idx = tid; idx < 16 * HALF; idx += blockDim.x) {
-    const int h = idx / HALF, i = idx % HALF;
-    float y0 = 0.f, y1 = 0.f, z0 = 0.f, z1 = 0.f;
-    if (h < R) {
-      const float x0 = sh.qraw[h * D + i], x1 = sh.qraw[h * D + i + HALF];
-      float cs, sn;
-      rope_cs_turns((double)sq.pos, sh.w2pi[i], cs, sn);
-      y0 = x0 * cs - x1 * sn;
-      y1 = x0 * sn + x1 * cs;
-      if (PATH == DEC_GEN) {
-        rope_cs_turns(c.fpos, sh.w2pi[i], cs, sn);
-        z0 = x0 * cs - x1 * sn;
-        z1 = x0 * sn + x1 * cs;
-      }
-    }
-    pqa[h * D + i] = (_Float16)y0;
-    pqa[h * D + i + HALF] = (_Float16)y1;
-    if (PATH == DEC_GEN) {
-      pq2[h * D + i] = (_Float16)z0;
-      pq2[h * D + i + HALF] = (_Float16)z1;
-    }
-  }
-  if (PATH == DEC_FACT) {
-    // in-chunk factor R_{f(i) - i}, i = 0..31 (f(k0 + i) - f(k0) = f(i) as
-    // G divides k0, or the map is linear)
-    for (int idx = tid; idx < 32 * HALF; idx += blockDim.x) {
-      const int i = idx / HALF, f = idx % HALF;
-      const double din = a.cont ? (double)i * sq.fk_rel : (double)(i / sq.G - i);
-      float cs, sn;
-      rope_cs_turns(din, sh.w2pi[f], cs, sn);
-      pq2[idx] = (_Float16)cs;
-      pq2[32 * HALF + idx] = (_Float16)sn;
-    }
-  }
-  if (PATH == DEC_GEN) {
-    // R_{c16} for both values of c16 = f(k + 16) - f(k) - 16 (continuous
-    // map: 16 (1 / G - 1) in both)
-    _Float16* tt = (_Float16*)sh.cs;  // [2 steps][cos, sin][HALF]
-    for (int idx = tid; idx < 2 * HALF; idx += blockDim.x) {
-      const int t = idx / HALF, f = idx % HALF;
-      const double c16 = a.cont ? 16.0 * sq.fk_rel : (double)(16 / sq.G + t - 16);
-      float cs, sn;
-      rope_cs_turns(c16, sh.w2pi[f], cs, sn);
-      tt[2 * t * HALF + f] = (_Float16)cs;
-      tt[(2 * t + 1) * HALF + f] = (_Float16)sn;
-    }
-  }
-  __syncthreads();
+  // the first chunk is in flight while the query operands and tables are
+  // computed
+  DecBuf<D> bA, bB;
+  int k0 = k_lo;
+  dec_issue_k<D>(c, k0, bA);
+  dec_issue_v<D>(c, k0, sA);
+
+  // query operands (B of S^T = K Q^T): lane holds dims 32 ds + 8 g16 + j of
+  // query head r16, rotated at pos (qa) and at f(pos) (qr), times scale*log2 e
   dh8v qa[NDS], qr[NDS];
+  {
+    // the lane's dims 32 ds + 8 g16 .. + 8 and their partners + D/2, as
+    // 16-byte loads of a valid row (head r16 clamped), zeroed past R heads
+    const bool qv = r16 < R;
+    const uint16_t* qp = xq + (int64_t)(h0 + (qv ? r16 : 0)) * D;
+    du32x4 raw0[NDS / 2], raw1[NDS / 2];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    qa[ds] = *(const dh8v*)(pqa + r16 * D + 32 * ds + 8 * g16);
-    qr[ds] = PATH == DEC_GEN ? *(const dh8v*)(pq2 + r16 * D + 32 * ds + 8 * g16) : dh8v{};
-  }
-  dh2v tcr[2][NDS / 2][4], tsr[2][NDS / 2][4];
-  if (PATH == DEC_FACT) {
+    for (int ds = 0; ds < NDS / 2; ++ds) {
+      raw0[ds] = *(const du32x4*)(qp + 32 * ds + 8 * g16);
+      raw1[ds] = *(const du32x4*)(qp + 32 * ds + 8 * g16 + D / 2);
+    }
+    const double fpos = remap_pos(sq.pos, sq.G, a.cont);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
-      for (int ds = 0; ds < NDS / 2; ++ds) {
-        const int off = (16 * kb + r16) * HALF + 32 * ds + 8 * g16;
-        const du32x4 cv = *(const du32x4*)(pq2 + off);
-        const du32x4 sv = *(const du32x4*)(pq2 + 32 * HALF + off);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // (the element is copied first: a bit cast of a vector element
-          // expression reads element 0 whatever the index)
-          const uint32_t cw = cv[m], sw = sv[m];
-          tcr[kb][ds][m] = __builtin_bit_cast(dh2v, cw);
-          tsr[kb][ds][m] = __builtin_bit_cast(dh2v, sw);
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * ds + 8 * g16 + j;
+        const float x0 = qv ? bf16_lane(raw0[ds], j) : 0.f;
+        const float x1 = qv ? bf16_lane(raw1[ds], j) : 0.f;
+        float cs, sn;
+        rope_cs_turns((double)sq.pos, w2pi_s[i], cs, sn);
+        qa[ds][j] = (_Float16)((x0 * cs - x1 * sn) * a.scale_log2);
+        qa[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * cs) * a.scale_log2);
+        if (!a.plain) {  // plain mode has no remapped route
+          rope_cs_turns(fpos, w2pi_s[i], cs, sn);
+          qr[ds][j] = (_Float16)((x0 * cs - x1 * sn) * a.scale_log2);
+          qr[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * cs) * a.scale_log2);
+        } else {
+          qr[ds][j] = qr[ds + NDS / 2][j] = (_Float16)0.f;
         }
       }
   }
-  __syncthreads();  // the second V stages are free from here on
+  // With G dividing 16 (floor map) or the continuous map, f(k) - k moves by
+  // the same c16 from key k to key k + 16, so a chunk's second block takes
+  // its cos/sin from the first by one rotation R_{c16}.
+  const bool step16 = STEP16 && c.correct && (c.cont || 16 % c.G == 0);
+  dh2v cst[NDS / 2][4], sst[NDS / 2][4];
+  if (step16) {
+    const double c16 = c.cont ? 16.0 * c.fk_rel : (double)(16 / c.G - 16);
+#pragma unroll
+    for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float c0, s0, c1, s1;
+        rope_cs_turns(c16, w2pi_s[32 * ds + 8 * g16 + 2 * m], c0, s0);
+        rope_cs_turns(c16, w2pi_s[32 * ds + 8 * g16 + 2 * m + 1], c1, s1);
+        cst[ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
+        sst[ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
+      }
+  }
 
   DecState<D> st;
 #pragma unroll
@@ -815,205 +668,115 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   st.lsum = 0.f;
   float chk = 0.f;
 
-  // chunk n + 1 (K in registers, V in the other LDS stage) is in flight
-  // while chunk n is computed. The next chunk is always issued: its keys are
-  // clamped to the range, so past the end it re-reads the last key (from L2)
+  // chunk i + 1 (K in registers, V in the other LDS stage) is in flight
+  // while chunk i is computed. The next chunk is always issued: its keys are
+  // clamped to the split, so past the end it re-reads the last key (from L2)
   // and the loads need no branch.
-  if (active) {
-    for (;;) {
-      dec_issue_k<D>(c, k0 + kstep, bB);
-      dec_issue_v<D>(c, k0 + kstep, sB);
-      __builtin_amdgcn_sched_barrier(0);  // all of the next chunk's loads go out first
-      dec_chunk<D, PATH>(c, k0, bA, qa, qr, tcr, tsr, sh, wave, sA, st, chk);
-      if (k0 + kstep >= c.k_hi) break;
-      dec_issue_k<D>(c, k0 + 2 * kstep, bA);
-      dec_issue_v<D>(c, k0 + 2 * kstep, sA);
-      __builtin_amdgcn_sched_barrier(0);
-      dec_chunk<D, PATH>(c, k0 + kstep, bB, qa, qr, tcr, tsr, sh, wave, sB, st, chk);
-      if (k0 + 2 * kstep >= c.k_hi) break;
-      k0 += 2 * kstep;
-    }
+  for (;;) {
+    dec_issue_k<D>(c, k0 + DEC_CHUNK, bB);
+    dec_issue_v<D>(c, k0 + DEC_CHUNK, sB);
+    __builtin_amdgcn_sched_barrier(0);  // all of the next chunk's loads go out first
+    dec_chunk<D>(c, k0, bA, qa, qr, w2pi_s, sA, st, step16, cst, sst, chk);
+    if (k0 + DEC_CHUNK >= c.k_hi) break;
+    dec_issue_k<D>(c, k0 + 2 * DEC_CHUNK, bA);
+    dec_issue_v<D>(c, k0 + 2 * DEC_CHUNK, sA);
+    __builtin_amdgcn_sched_barrier(0);
+    dec_chunk<D>(c, k0 + DEC_CHUNK, bB, qa, qr, w2pi_s, sB, st, step16, cst, sst, chk);
+    if (k0 + 2 * DEC_CHUNK >= c.k_hi) break;
+    k0 += 2 * DEC_CHUNK;
   }
-  // no transfer into the LDS stages may outlive the loop
+  // no transfer into these LDS stages may outlive the unit
   __builtin_amdgcn_s_waitcnt(0);
-  if (__any(!(chk - chk == 0.f))) {  // chk is inf or NaN
-    if (lane == 0) atomicOr(&sh.flag[0], 1);
+  const float m = st.m, lsum = st.lsum;
+  df32x4 (&acc)[NDB] = st.acc;
+  // ---- split partial: m (log2 domain), l, unnormalised O for each query head
+  float lt = lsum + __shfl_xor(lsum, 16);
+  lt += __shfl_xor(lt, 32);
+  // an operand out of the fp16 range: the sum l of every query head of this
+  // KV head becomes NaN, and with it their merged outputs and LSE
+  if (__any(!(chk - chk == 0.f))) lt = __builtin_nanf("");
+  float* part = sq.part;
+  if (g16 == 0 && r16 < R) {
+    float* pp = part + ((int64_t)(h0 + r16) * a.S + s) * (D + 2);
+    pp[0] = m;
+    pp[1] = lt;
   }
-  __syncthreads();  // every wave is past its V stages
-
-  // ---- merge the waves' states through LDS into the range's record
-  float* red = (float*)sh.vA;
-  float* red_m = red;                  // [NW][16]
-  float* red_l = red + DEC_NW * 16;    // [NW][16]
-  float* red_a = red + 2 * DEC_NW * 16;  // [NW][R][D]
-  {
-    float lt = st.lsum + __shfl_xor(st.lsum, 16);
-    lt += __shfl_xor(lt, 32);
-    if (g16 == 0) {
-      red_m[wave * 16 + r16] = st.m;
-      red_l[wave * 16 + r16] = lt;
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int q = 4 * g16 + r;
-      if (q < R) {
+  for (int r = 0; r < 4; ++r) {
+    const int q = 4 * g16 + r;
+    if (q < R) {
+      float* pp = part + ((int64_t)(h0 + q) * a.S + s) * (D + 2) + 2;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) red_a[(wave * R + q) * D + 16 * db + r16] = st.acc[db][r];
-      }
+      for (int db = 0; db < NDB; ++db) pp[16 * db + r16] = acc[db][r];
     }
   }
-  __syncthreads();
-  const int recf = dec_recf(R, D);
-  float* rec0 = a.rec + ((int64_t)b * a.Hkv + g) * a.S * recf;
-  {
-    float* rec = rec0 + (int64_t)s * recf;
-    const bool bad = sh.flag[0] != 0;
-    for (int idx = tid; idx < R * D; idx += blockDim.x) {
-      const int h = idx / D, dd = idx % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < DEC_NW; ++w) M = fmaxf(M, red_m[w * 16 + h]);
-      float L = 0.f, A = 0.f;
-#pragma unroll
-      for (int w = 0; w < DEC_NW; ++w) {
-        const float mw = red_m[w * 16 + h];
-        const float sc = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        L += red_l[w * 16 + h] * sc;
-        A += red_a[(w * R + h) * D + dd] * sc;
-      }
-      rec[2 * DEC_RP + idx] = A;
-      if (dd == 0) {
-        rec[2 * h] = M;
-        rec[2 * h + 1] = bad ? __builtin_nanf("") : L;
-      }
-    }
-  }
-  // ---- release the record, take the ticket; the last range merges
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  int* ticket = a.tickets + (int64_t)b * a.Hkv + g;
-  if (tid == 0) sh.flag[1] = atomicAdd(ticket, 1) == nrange - 1;
-  __syncthreads();
-  if (!sh.flag[1]) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  {
-    // thread = (group of ranges grp, 4 consecutive elements e4 of the
-    // [R][D] output); batches of 16 ranges, all loads issued before use
-    const int e4n = R * D / 4;
-    const int ng = blockDim.x / e4n;  // e4n divides 256 for R in {1, 2, 4, 8}
-    const int grp = tid / e4n, e4 = tid % e4n;
-    const int h = 4 * e4 / D;
-    float M = -INFINITY, L = 0.f;
-    df32x4 A = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = grp; s0 < nrange; s0 += 16 * ng) {
-      float2 ml[16];
-      df32x4 av[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int sj = s0 + j * ng;
-        const float* r = rec0 + (int64_t)(sj < nrange ? sj : s0) * recf;
-        ml[j] = *(const float2*)(r + 2 * h);
-        av[j] = *(const df32x4*)(r + 2 * DEC_RP + 4 * e4);
-        if (sj >= nrange) ml[j].x = -INFINITY;
-      }
-      float mb = M;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mb = fmaxf(mb, ml[j].x);
-      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mb);
-      L *= sc;
-      A *= sc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float w = ml[j].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[j].x - mb);
-        L += w * ml[j].y;
-        A += w * av[j];
-      }
-      M = mb;
-    }
-    // combine the groups through LDS (the records' merge scratch is free)
-    __syncthreads();
-    float* gm = red;                  // [ng][e4n]
-    float* gl = red + 256;            // [ng][e4n]
-    df32x4* ga = (df32x4*)(red + 512);  // [ng][e4n]
-    if (grp < ng) {
-      gm[tid] = M;
-      gl[tid] = L;
-      ga[tid] = A;
-    }
-    __syncthreads();
-    if (tid < e4n) {
-      float Mt = -INFINITY;
-      for (int q = 0; q < ng; ++q) Mt = fmaxf(Mt, gm[q * e4n + e4]);
-      float Lt = 0.f;
-      df32x4 At = {0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q < ng; ++q) {
-        const float mq = gm[q * e4n + e4];
-        const float w = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - Mt);
-        Lt += w * gl[q * e4n + e4];
-        At += w * ga[q * e4n + e4];
-      }
-      const int64_t orow = (int64_t)b * a.Hq + h0 + h;
-      const int dd = 4 * e4 - h * D;
-      const float inv = 1.f / Lt;
-      const uint32_t lo = (uint32_t)f32_to_bf16_bits(At[0] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(At[1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_bits(At[2] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(At[3] * inv) << 16);
-      *(uint2*)((uint16_t*)a.o + orow * D + dd) = make_uint2(lo, hi);
-      if (a.lse && dd == 0) a.lse[orow] = (Mt + __log2f(Lt)) * 0.69314718055994530942f;
-    }
-  }
-  if (tid == 0) atomicExch(ticket, 0);  // every range of this head has arrived: ready for the next call
-  __syncthreads();
 }
 
-// Single sequence: workgroup (range s, KV head g) = blockIdx (s Hkv + g), so
-// the workgroups running together cover every head of the same key rows.
-template <int D, int PATH>
-__global__ void __launch_bounds__(256, 2) decode_bf16_kernel(DecArgs a) {
-  const DecLds<D> sh = dec_lds<D>();
-  const int g = blockIdx.x % a.Hkv, s = blockIdx.x / a.Hkv;
+// Single sequence: workgroup = one split of four KV heads (wave w: head
+// 4 hg + w), so the waves running together read neighbouring head slices of
+// the same key rows.
+template <int D>
+__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
+  using G = DecGeom<D>;
+  // two V stages per wave, as separate arrays so that reads of one are known
+  // not to alias the transfers in flight into the other
+  __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
+  __shared__ double w2pi_s[D / 2];
+  // the wave index is uniform per wave: say so, so that every split-derived
+  // value (key range, route of a key block) lives in scalar registers and the
+  // route branches are scalar jumps; matrix instructions then never run under
+  // a partial or empty EXEC mask
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
+  __syncthreads();
+  const int hgroups = (a.Hkv + 3) >> 2;
+  const int s = blockIdx.x / hgroups, kvh = (blockIdx.x % hgroups) * 4 + wave;
+  if (kvh >= a.Hkv) return;
   const DecSeq sq = dec_seq<false>(a, 0, D, 2);
-  dec_unit<D, PATH>(a, sq, 0, g, s, a.S, sh);
+  dec_unit<D, true>(a, sq, s, kvh, w2pi_s, vstA[wave], vstB[wave]);
 }
 
 // Batch: a fixed grid of workgroups walks the work list the plan kernel
-// built (unit u = (entry u / Hkv of the list, KV head u % Hkv); the list
-// holds the ranges s * kps <= pos_b of every valid sequence b, base[b] ..
-// base[b + 1] - 1, and one entry per invalid sequence), round robin, so the
-// work spreads evenly over the CUs whatever the mix of lengths.
+// built (unit u = (entry of the list, KV-head group); the list holds the
+// splits s * kps <= pos_b of every valid sequence b, base[b] .. base[b+1] -
+// 1), round robin, so the work spreads evenly over the CUs whatever the mix
+// of sequence lengths.
 template <int D>
-__global__ void __launch_bounds__(256, 2) decode_bf16_batch_kernel(DecArgs a, const int* base,
+__global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, const int* base,
                                                                    int B) {
-  const DecLds<D> sh = dec_lds<D>();
-  const int units = base[B] * a.Hkv;
+  using G = DecGeom<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
+  __shared__ double w2pi_s[D / 2];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
+  __syncthreads();
+  const int hgroups = (a.Hkv + 3) >> 2;
+  const int units = base[B] * hgroups;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int item = u / a.Hkv, g = u % a.Hkv;
+    const int item = u / hgroups, kvh = (u % hgroups) * 4 + wave;
+    if (kvh >= a.Hkv) continue;
     int lo = 0, hi = B - 1;  // the sequence b with base[b] <= item < base[b + 1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (base[mid] <= item) lo = mid; else hi = mid - 1;
     }
     const DecSeq sq = dec_seq<true>(a, lo, D, 2);
-    if (!sq.ok) {  // an entry outside the caller's bounds reads nothing
-      dec_write_nan<D>(a, lo, g);
-      continue;
-    }
-    // one path (a second would not fit the registers): the general
-    // correction, skipped at run time for plain mode and G = 1
-    dec_unit<D, DEC_GEN>(a, sq, lo, g, item - base[lo], (sq.pos + a.kps) / a.kps, sh);
+    // (the batch kernel has no registers to spare for the step table)
+    dec_unit<D, false>(a, sq, item - base[lo], kvh, w2pi_s, vstA[wave], vstB[wave]);
   }
 }
 
-// Ranges of batch entry b that hold keys (s * kps <= pos); an entry the
-// kernels skip takes one list entry (which writes its NaN outputs).
+// Splits of batch entry b that hold keys (s * kps <= pos), 0 for an entry
+// the kernels skip.
 __device__ __forceinline__ int dec_batch_nsplit(const DecArgs& a, int b) {
   const DecSeq sq = dec_seq<true>(a, b, 0, 0);
-  return sq.ok ? (sq.pos + a.kps) / a.kps : 1;
+  return sq.ok ? (sq.pos + a.kps) / a.kps : 0;
 }
 
-// Work list of a batched decode: base[b] = number of list entries of the
-// entries before b; base[B] = their total. One workgroup.
+// Work list of a batched decode: base[b] = number of splits of the entries
+// before b; base[B] = their total. One workgroup.
 __global__ void __launch_bounds__(1024) decode_batch_plan_kernel(DecArgs a, int* base, int B) {
   __shared__ int part[1024];
   const int tid = threadIdx.x;
@@ -1037,14 +800,7 @@ __global__ void __launch_bounds__(1024) decode_batch_plan_kernel(DecArgs a, int*
   if (tid == 1023) base[B] = part[1023];
 }
 
-// Zero fill (the arrival tickets of a fresh workspace): a kernel rather than
-// a memset, so the call is safe to record in a graph.
-__global__ void __launch_bounds__(256) dec_zero_kernel(uint32_t* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
-    p[i] = 0u;
-}
-
-// float32 merge of the split partials of one query head with LSE weights:
+// Merge of the split partials of one query head with LSE weights:
 // workgroup (head h, 16 output dims), thread (split group g of 16, dim):
 // each thread takes the splits s = g, g + 16, ... sixteen at a time, all of a
 // batch's loads issued before any is used (one memory round trip for up to
@@ -1119,41 +875,49 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecArgs a) {
   }
 }
 
-
-template <int D, bool BATCH>
-static void launch_decode_f32(int R, int B, hipStream_t st, const DecArgs& a) {
-  const dim3 grid(a.S, a.Hkv, B);
-  switch (R) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<true, D, 1, BATCH>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<true, D, 2, BATCH>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<true, D, 4, BATCH>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<true, D, 8, BATCH>), grid, dim3(256), 0, st, a); break;
+template <bool F32, int D, bool BATCH>
+static void launch_decode_t(int R, int B, int* base, int grid_wg, hipStream_t st,
+                            const DecArgs& a) {
+  if constexpr (F32) {
+    const dim3 grid(a.S, a.Hkv, B);
+    switch (R) {
+      case 1: hipLaunchKernelGGL((decode_split_kernel<F32, D, 1, BATCH>), grid, dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((decode_split_kernel<F32, D, 2, BATCH>), grid, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((decode_split_kernel<F32, D, 4, BATCH>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((decode_split_kernel<F32, D, 8, BATCH>), grid, dim3(256), 0, st, a); break;
+    }
+  } else if constexpr (BATCH) {
+    hipLaunchKernelGGL(decode_batch_plan_kernel, dim3(1), dim3(1024), 0, st, a, base, B);
+    hipLaunchKernelGGL((decode_mfma_batch_kernel<D>), dim3(grid_wg), dim3(256), 0, st, a,
+                       (const int*)base, B);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<D>), dim3(a.S * ((a.Hkv + 3) / 4)), dim3(256), 0, st,
+                       a);
   }
-  hipLaunchKernelGGL((decode_merge_kernel<true, D, BATCH>), dim3(a.Hq, D / 16, B), dim3(256), 0,
-                     st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<F32, D, BATCH>), dim3(a.Hq, D / 16, B), dim3(256), 0, st,
+                     a);
 }
 
-template <int D>
-static void launch_decode_bf16(int path, hipStream_t st, const DecArgs& a) {
-  const dim3 grid((unsigned)(a.S * a.Hkv));
-  if (path == DEC_PLAIN)
-    hipLaunchKernelGGL((decode_bf16_kernel<D, DEC_PLAIN>), grid, dim3(256), 0, st, a);
-  else if (path == DEC_FACT)
-    hipLaunchKernelGGL((decode_bf16_kernel<D, DEC_FACT>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_bf16_kernel<D, DEC_GEN>), grid, dim3(256), 0, st, a);
+template <bool BATCH>
+static void launch_decode_any(int is_f32, int d, int R, int B, int* base, int grid_wg,
+                              hipStream_t st, const DecArgs& a) {
+  if (is_f32) {
+    if (d == 64) launch_decode_t<true, 64, BATCH>(R, B, base, grid_wg, st, a);
+    else launch_decode_t<true, 128, BATCH>(R, B, base, grid_wg, st, a);
+  } else {
+    if (d == 64) launch_decode_t<false, 64, BATCH>(R, B, base, grid_wg, st, a);
+    else launch_decode_t<false, 128, BATCH>(R, B, base, grid_wg, st, a);
+  }
 }
 
 static DecArgs decode_args(const void* xq, const void* kc, const void* vc, void* o, float* lse,
                            int Hq, int Hkv, int64_t w0, float scale, const RopeFreqs& fr,
-                           int plain, int cont, int* tickets, float* part) {
+                           int plain, int cont, void* ws) {
   DecArgs a;
   a.xq = xq;
   a.kc = kc;
   a.vc = vc;
-  a.part = part;
-  a.rec = part;
-  a.tickets = tickets;
+  a.part = (float*)ws;
   a.o = o;
   a.lse = lse;
   a.Hq = Hq;
@@ -1177,22 +941,15 @@ static DecArgs decode_args(const void* xq, const void* kc, const void* vc, void*
 hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
                          int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
                          const RopeFreqs& fr, int plain, int cont, int is_f32, int kps,
-                         int* tickets, float* part, hipStream_t st) {
-  DecArgs a = decode_args(xq, kc, vc, o, lse, Hq, Hkv, w0, scale, fr, plain, cont, tickets, part);
+                         void* ws, hipStream_t st) {
+  DecArgs a = decode_args(xq, kc, vc, o, lse, Hq, Hkv, w0, scale, fr, plain, cont, ws);
   a.pos = (int)pos;
   a.G = (int)G;
   a.fk_rel = 1.0 / (double)G - 1.0;
   const int keys = (int)pos + 1;
   a.S = (keys + kps - 1) / kps;  // no empty split
   a.kps = kps;
-  if (is_f32) {
-    if (d == 64) launch_decode_f32<64, false>(Hq / Hkv, 1, st, a);
-    else launch_decode_f32<128, false>(Hq / Hkv, 1, st, a);
-  } else {
-    const int path = (plain || G == 1) ? DEC_PLAIN : (cont || 32 % G == 0) ? DEC_FACT : DEC_GEN;
-    if (d == 64) launch_decode_bf16<64>(path, st, a);
-    else launch_decode_bf16<128>(path, st, a);
-  }
+  launch_decode_any<false>(is_f32, d, Hq / Hkv, 1, nullptr, 0, st, a);
   return hipGetLastError();
 }
 
@@ -1200,9 +957,9 @@ hipError_t launch_decode_batch(const void* xq, const void* kc, const void* vc, v
                                const int32_t* positions, const int32_t* starts, int B,
                                int64_t max_keys, int64_t cap_rows, int Hq, int Hkv, int d,
                                int64_t w0, int64_t w_pre, float scale, const RopeFreqs& fr,
-                               int plain, int cont, int is_f32, int splits, int kps, int* tickets,
-                               float* part, int* base, int grid_wg, hipStream_t st) {
-  DecArgs a = decode_args(xq, kc, vc, o, lse, Hq, Hkv, w0, scale, fr, plain, cont, tickets, part);
+                               int plain, int cont, int is_f32, int splits, int kps, void* ws,
+                               int* base, int grid_wg, hipStream_t st) {
+  DecArgs a = decode_args(xq, kc, vc, o, lse, Hq, Hkv, w0, scale, fr, plain, cont, ws);
   a.bpos = positions;
   a.bstart = starts;
   a.max_keys = (int)max_keys;
@@ -1210,27 +967,7 @@ hipError_t launch_decode_batch(const void* xq, const void* kc, const void* vc, v
   a.w_pre = w_pre;
   a.S = splits;
   a.kps = kps;
-  if (is_f32) {
-    if (d == 64) launch_decode_f32<64, true>(Hq / Hkv, B, st, a);
-    else launch_decode_f32<128, true>(Hq / Hkv, B, st, a);
-  } else {
-    hipLaunchKernelGGL(decode_batch_plan_kernel, dim3(1), dim3(1024), 0, st, a, base, B);
-    if (d == 64)
-      hipLaunchKernelGGL((decode_bf16_batch_kernel<64>), dim3(grid_wg), dim3(256), 0, st, a,
-                         (const int*)base, B);
-    else
-      hipLaunchKernelGGL((decode_bf16_batch_kernel<128>), dim3(grid_wg), dim3(256), 0, st, a,
-                         (const int*)base, B);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st) {
-  const size_t n = bytes / 4;
-  if (n == 0) return hipSuccess;
-  const size_t want = (n + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
-  hipLaunchKernelGGL(dec_zero_kernel, dim3(blocks), dim3(256), 0, st, (uint32_t*)p, n);
+  launch_decode_any<true>(is_f32, d, Hq / Hkv, B, base, grid_wg, st, a);
   return hipGetLastError();
 }
 

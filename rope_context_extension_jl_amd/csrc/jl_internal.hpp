@@ -109,27 +109,22 @@ hipError_t launch_prefill_f32(int pass, const void* xq, const void* v, void* o, 
 hipError_t launch_ie_merge(void* o, float* lse, int out_f32, int64_t T, int Hq, int d, void* ws,
                            const PrefillLayout& lay, hipStream_t st);
 
-// tickets: one int per (sequence, KV head), zero before the call and left
-// zero by it (bf16); part: the partials (float32 [B, Hq, S, d + 2] or the
-// bf16 range records). kps: keys per split (bf16: a multiple of 32).
 hipError_t launch_decode(const void* xq, const void* kc, const void* vc, void* o, float* lse,
                          int64_t pos, int Hq, int Hkv, int d, int64_t w0, int64_t G, float scale,
                          const RopeFreqs& fr, int plain, int cont, int is_f32, int kps,
-                         int* tickets, float* part, hipStream_t st);
+                         void* ws, hipStream_t st);
 
 // Batched decode: sequence b's query is row b of xq [B, Hq, d], its keys
 // 0 .. positions[b] sit at cache rows starts[b] + k; `splits` splits of `kps`
-// keys each cover max_keys keys. bf16: base (int32 [B + 1], device) receives
-// the work list and grid_wg workgroups walk it.
+// keys each cover max_keys keys (the partials, at ws, are
+// [B, Hq, splits, d + 2]). bf16: base (int32 [B + 1], device) receives the
+// work list and grid_wg workgroups walk it.
 hipError_t launch_decode_batch(const void* xq, const void* kc, const void* vc, void* o, float* lse,
                                const int32_t* positions, const int32_t* starts, int B,
                                int64_t max_keys, int64_t cap_rows, int Hq, int Hkv, int d,
                                int64_t w0, int64_t w_pre, float scale, const RopeFreqs& fr,
-                               int plain, int cont, int is_f32, int splits, int kps, int* tickets,
-                               float* part, int* base, int grid_wg, hipStream_t st);
-
-// Zero fill of bytes / 4 words by a kernel (no memset, so it may be captured).
-hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
+                               int plain, int cont, int is_f32, int splits, int kps, void* ws,
+                               int* base, int grid_wg, hipStream_t st);
 
 hipError_t launch_tile_dump(int64_t L, int64_t w0, int8_t* out, hipStream_t st);
 

@@ -462,19 +462,16 @@ def test_prefill_range_flags(where):
 
 
 # ------------------------------------------------------------------ decode workspace, fp16 range
-def test_decode_workspace_counters_reset_and_reuse():
-    """The bf16 decode counts the ranges of each KV head in as they finish;
-    the last one merges and puts the counter back to zero. A workspace
-    prepared once (jl_decode_workspace_init) serves any number of calls, at
-    any position and split count, and each result is the same as with a
-    fresh workspace."""
+def test_decode_workspace_reuse():
+    """One workspace with stale contents serves any number of calls, at any
+    position and split count; each result equals a call with a fresh
+    workspace, bit for bit, and the oracle within the tolerance."""
     w0, w_pre, theta = 100, 512, 1e6
     xq, xk, v, kc, vc, tdt = _decode_setup("bf16")
     Hq = xq.shape[1]
     ws = torch.empty(jl.decode_workspace_size(kc.shape[0], Hq, 128), dtype=torch.uint8,
                      device="cuda")
-    ws.fill_(0x5a)  # stale contents: the init call must clear them
-    jl.decode_workspace_init(ws)
+    ws.fill_(0x5a)
     for pos, splits in ((2999, 0), (700, 3), (1500, 0), (2999, 40), (40, 0), (2999, 0)):
         note(f"decode workspace reuse pos={pos} splits={splits}")
         o1, l1 = jl.bifocal_decode(to_dev(xq[pos]), kc, vc, pos, w0, w_pre, theta,
@@ -483,7 +480,6 @@ def test_decode_workspace_counters_reset_and_reuse():
                                    num_splits=splits)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
-        assert int(ws[:4 * Hq].view(torch.int32).abs().sum()) == 0, "counters not reset"
         ro, _ = decode_row(xq[pos], xk, v, pos, w0, w_pre, theta)
         assert_bf16_close(to_host(o1), ro, f"reuse pos={pos}")
 

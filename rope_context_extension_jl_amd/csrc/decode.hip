@@ -692,13 +692,15 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   // ---- split partial: m (log2 domain), l, unnormalised O for each query head
   float lt = lsum + __shfl_xor(lsum, 16);
   lt += __shfl_xor(lt, 32);
-  // an operand out of the fp16 range: the sum l of every query head of this
-  // KV head becomes NaN, and with it their merged outputs and LSE
-  if (__any(!(chk - chk == 0.f))) lt = __builtin_nanf("");
+  // an operand out of the fp16 range: every query head of this KV head
+  // publishes m = +inf and l = NaN, so the merge's weights, and with them the
+  // outputs and the LSE, are NaN (a NaN m alone would be skipped by the max)
+  const bool bad = __any(!(chk - chk == 0.f));
+  if (bad) lt = __builtin_nanf("");
   float* part = sq.part;
   if (g16 == 0 && r16 < R) {
     float* pp = part + ((int64_t)(h0 + r16) * a.S + s) * (D + 2);
-    pp[0] = m;
+    pp[0] = bad ? INFINITY : m;
     pp[1] = lt;
   }
 #pragma unroll

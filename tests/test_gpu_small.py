@@ -193,6 +193,9 @@ def test_prefill_bf16_peaked_small():
     assert diff[ok].max() <= 2e-2 and diff[ok].mean() <= 2e-3
 
 
+@pytest.mark.xfail(strict=True, reason="Eq. 7 cancels catastrophically on rows whose "
+                   "cancellation ratio exceeds 1e3 (errors up to ~2.4 on this peaked case); "
+                   "the fused pass is the production path")
 def test_prefill_bf16_peaked_small_ie_cancelling_rows():
     """Eq. 7 on the rows whose cancellation ratio exceeds RATIO_OK, at the
     same tolerance."""

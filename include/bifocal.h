@@ -257,6 +257,26 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
                             jl_mode mode, int num_splits, void* workspace, size_t ws_bytes,
                             void* stream, void* ev_begin, void* ev_end);
 
+/* jl_bifocal_decode for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid it): the
+ * same arguments without a workspace, the same kernels and results. The split
+ * partials live in one file-scope device array of JL_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the library's load until the process ends; its device
+ * address is looked up on a device's first call. No entry point allocates.
+ * A call whose partials (Hq x splits x (d + 2) floats, after the alignment
+ * of jl_decode_workspace_size) would not fit returns JL_EWORKSPACE before
+ * any launch. With num_splits = 0 the bf16 split choice fits for Hq <= 32 at
+ * d = 128 and any position (it picks at most 512 splits when Hkv <= 4, 256
+ * when Hkv <= 8: at most 8.5 MB of partials).
+ * Every call on one GPU shares that GPU's array, and nothing in it needs to
+ * start at zero: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. */
+#define JL_NOALLOC_SCRATCH_BYTES (16u << 20)
+int jl_bifocal_decode_noalloc(const void* xq, const void* kcache, const void* vcache, void* o,
+                              float* lse, int64_t pos, int64_t capacity, int Hq, int Hkv, int d,
+                              int64_t w0, int64_t w_pre, double theta, float scale, jl_dtype dt,
+                              jl_mode mode, int num_splits, void* stream);
+
 /* Bytes of device workspace jl_bifocal_decode_batch needs for B sequences
  * whose positions are all below max_keys (any num_splits it would choose or
  * accept); 0 for arguments it would reject. */

@@ -69,6 +69,9 @@ _SIGS = {
     "jl_bifocal_decode_timed": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int,
                                          _c_int, _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int,
                                          _c_int, _c_int, _c_p, _c_sz, _c_p, _c_p, _c_p]),
+    "jl_bifocal_decode_noalloc": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int,
+                                           _c_int, _c_int, _c_i64, _c_i64, _c_dbl, _c_flt, _c_int,
+                                           _c_int, _c_int, _c_p]),
     "jl_decode_batch_workspace_size": (_c_sz, [_c_int, _c_i64, _c_int, _c_int]),
     "jl_bifocal_decode_batch": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_i64,
                                          _c_i64, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_dbl,

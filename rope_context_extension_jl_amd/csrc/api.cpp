@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "jl_internal.hpp"
 
 namespace jl {
@@ -478,6 +480,49 @@ int jl_bifocal_decode(const void* xq, const void* kcache, const void* vcache, vo
   return jl_bifocal_decode_timed(xq, kcache, vcache, o, lse, pos, capacity, Hq, Hkv, d, w0, w_pre,
                                  theta, scale, dt, mode, num_splits, workspace, ws_bytes, stream,
                                  nullptr, nullptr);
+}
+
+}  // extern "C"
+
+// ---- decode without allocation, for callers that cannot allocate
+// The partials live in a file-scope device array instead of a caller
+// workspace. Its name is a host-side stand-in in host code: the device
+// address is looked up once per device (hipGetSymbolAddress with that device
+// current) and only that address is passed to the kernels.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[JL_NOALLOC_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];  // per device ordinal
+
+static int scratch_pointer(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= 64) return JL_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return JL_OK;
+}
+
+extern "C" {
+
+int jl_bifocal_decode_noalloc(const void* xq, const void* kcache, const void* vcache, void* o,
+                              float* lse, int64_t pos, int64_t capacity, int Hq, int Hkv, int d,
+                              int64_t w0, int64_t w_pre, double theta, float scale, jl_dtype dt,
+                              jl_mode mode, int num_splits, void* stream) {
+  void* ws = nullptr;
+  const int st = scratch_pointer(&ws);
+  if (st != JL_OK) return st;
+  // the same checks, split plan and kernels as jl_bifocal_decode; a plan whose
+  // partials exceed the array comes back as JL_EWORKSPACE before any launch
+  return jl_bifocal_decode_timed(xq, kcache, vcache, o, lse, pos, capacity, Hq, Hkv, d, w0, w_pre,
+                                 theta, scale, dt, mode, num_splits, ws, JL_NOALLOC_SCRATCH_BYTES,
+                                 stream, nullptr, nullptr);
 }
 
 int jl_debug_tile_classes(int64_t L, int64_t w0, int8_t* out_dev, void* stream) {

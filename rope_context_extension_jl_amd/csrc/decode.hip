@@ -570,9 +570,41 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
 // One work unit of the bf16 decode for one wave: keys [s kps, (s + 1) kps)
 // of KV head kvh of sequence sq, leaving the partial of each query head of
 // the group. vA / vB: this wave's two V stages.
+// cos / sin tables a workgroup computes once for the rotations shared by all
+// of its lanes: [0][i] of pos * omega_i, [1][i] of f(pos) * omega_i (the
+// query at the absolute and the remapped position), [2][i] of c16 * omega_i
+// (the step between a chunk's two 16-key blocks). One angle per thread.
+template <int D>
+__device__ __forceinline__ void dec_tables(const DecArgs& a, const DecSeq& sq, bool step16,
+                                           const double* w2pi_s, float2 (*tab)[D / 2]) {
+  const int i = threadIdx.x;
+  if (i < D / 2) {
+    const double w = w2pi_s[i];
+    float c, s;
+    rope_cs_turns((double)sq.pos, w, c, s);
+    tab[0][i] = make_float2(c, s);
+    if (!a.plain) {
+      rope_cs_turns(remap_pos(sq.pos, sq.G, a.cont), w, c, s);
+      tab[1][i] = make_float2(c, s);
+    }
+    if (step16) {
+      rope_cs_turns(a.cont ? 16.0 * sq.fk_rel : (double)(16 / sq.G - 16), w, c, s);
+      tab[2][i] = make_float2(c, s);
+    }
+  }
+}
+
+// Whether the second 16-key block of a chunk takes its cos / sin from the
+// first by one rotation R_{c16}: with G dividing 16 (floor map) or the
+// continuous map, f(k) - k moves by the same c16 from key k to key k + 16.
+__device__ __forceinline__ bool dec_step16(const DecArgs& a, const DecSeq& sq) {
+  return !a.plain && sq.G > 1 && (a.cont || 16 % sq.G == 0);
+}
+
 template <int D, bool STEP16>
 __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int s, int kvh,
-                                         const double* w2pi_s, uint8_t* sA, uint8_t* sB) {
+                                         const double* w2pi_s, const float2 (*tab)[D / 2],
+                                         uint8_t* sA, uint8_t* sB) {
   using G = DecGeom<D>;
   constexpr int NDS = G::NDS, NDB = G::NDB;
   const int lane = threadIdx.x & 63;
@@ -620,7 +652,6 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
       raw0[ds] = *(const du32x4*)(qp + 32 * ds + 8 * g16);
       raw1[ds] = *(const du32x4*)(qp + 32 * ds + 8 * g16 + D / 2);
     }
-    const double fpos = remap_pos(sq.pos, sq.G, a.cont);
 #pragma unroll
     for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
@@ -628,35 +659,31 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
         const int i = 32 * ds + 8 * g16 + j;
         const float x0 = qv ? bf16_lane(raw0[ds], j) : 0.f;
         const float x1 = qv ? bf16_lane(raw1[ds], j) : 0.f;
-        float cs, sn;
-        rope_cs_turns((double)sq.pos, w2pi_s[i], cs, sn);
-        qa[ds][j] = (_Float16)((x0 * cs - x1 * sn) * a.scale_log2);
-        qa[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * cs) * a.scale_log2);
+        const float2 ta = tab[0][i];
+        qa[ds][j] = (_Float16)((x0 * ta.x - x1 * ta.y) * a.scale_log2);
+        qa[ds + NDS / 2][j] = (_Float16)((x0 * ta.y + x1 * ta.x) * a.scale_log2);
         if (!a.plain) {  // plain mode has no remapped route
-          rope_cs_turns(fpos, w2pi_s[i], cs, sn);
-          qr[ds][j] = (_Float16)((x0 * cs - x1 * sn) * a.scale_log2);
-          qr[ds + NDS / 2][j] = (_Float16)((x0 * sn + x1 * cs) * a.scale_log2);
+          const float2 tr = tab[1][i];
+          qr[ds][j] = (_Float16)((x0 * tr.x - x1 * tr.y) * a.scale_log2);
+          qr[ds + NDS / 2][j] = (_Float16)((x0 * tr.y + x1 * tr.x) * a.scale_log2);
         } else {
           qr[ds][j] = qr[ds + NDS / 2][j] = (_Float16)0.f;
         }
       }
   }
-  // With G dividing 16 (floor map) or the continuous map, f(k) - k moves by
-  // the same c16 from key k to key k + 16, so a chunk's second block takes
-  // its cos/sin from the first by one rotation R_{c16}.
-  const bool step16 = STEP16 && c.correct && (c.cont || 16 % c.G == 0);
+  // R_{c16} between a chunk's two 16-key blocks (see dec_step16), as fp16
+  // pairs of neighbouring frequencies
+  const bool step16 = STEP16 && dec_step16(a, sq);
   dh2v cst[NDS / 2][4], sst[NDS / 2][4];
   if (step16) {
-    const double c16 = c.cont ? 16.0 * c.fk_rel : (double)(16 / c.G - 16);
 #pragma unroll
     for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        float c0, s0, c1, s1;
-        rope_cs_turns(c16, w2pi_s[32 * ds + 8 * g16 + 2 * m], c0, s0);
-        rope_cs_turns(c16, w2pi_s[32 * ds + 8 * g16 + 2 * m + 1], c1, s1);
-        cst[ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
-        sst[ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
+        const float2 t0 = tab[2][32 * ds + 8 * g16 + 2 * m];
+        const float2 t1 = tab[2][32 * ds + 8 * g16 + 2 * m + 1];
+        cst[ds][m] = dh2v{(_Float16)t0.x, (_Float16)t1.x};
+        sst[ds][m] = dh2v{(_Float16)t0.y, (_Float16)t1.y};
       }
   }
 
@@ -725,18 +752,21 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
   __shared__ double w2pi_s[D / 2];
+  __shared__ float2 tab_s[3][D / 2];
   // the wave index is uniform per wave: say so, so that every split-derived
   // value (key range, route of a key block) lives in scalar registers and the
   // route branches are scalar jumps; matrix instructions then never run under
   // a partial or empty EXEC mask
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const DecSeq sq = dec_seq<false>(a, 0, D, 2);
   if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
+  __syncthreads();
+  dec_tables<D>(a, sq, dec_step16(a, sq), w2pi_s, tab_s);
   __syncthreads();
   const int hgroups = (a.Hkv + 3) >> 2;
   const int s = blockIdx.x / hgroups, kvh = (blockIdx.x % hgroups) * 4 + wave;
   if (kvh >= a.Hkv) return;
-  const DecSeq sq = dec_seq<false>(a, 0, D, 2);
-  dec_unit<D, true>(a, sq, s, kvh, w2pi_s, vstA[wave], vstB[wave]);
+  dec_unit<D, true>(a, sq, s, kvh, w2pi_s, tab_s, vstA[wave], vstB[wave]);
 }
 
 // Batch: a fixed grid of workgroups walks the work list the plan kernel
@@ -751,6 +781,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, co
   __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
   __shared__ double w2pi_s[D / 2];
+  __shared__ float2 tab_s[3][D / 2];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
   __syncthreads();
@@ -758,15 +789,20 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, co
   const int units = base[B] * hgroups;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int item = u / hgroups, kvh = (u % hgroups) * 4 + wave;
-    if (kvh >= a.Hkv) continue;
     int lo = 0, hi = B - 1;  // the sequence b with base[b] <= item < base[b + 1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (base[mid] <= item) lo = mid; else hi = mid - 1;
     }
     const DecSeq sq = dec_seq<true>(a, lo, D, 2);
+    // this unit's tables (every wave passes both barriers, also the waves
+    // past the last KV head)
+    __syncthreads();
+    dec_tables<D>(a, sq, false, w2pi_s, tab_s);
+    __syncthreads();
+    if (kvh >= a.Hkv) continue;
     // (the batch kernel has no registers to spare for the step table)
-    dec_unit<D, false>(a, sq, item - base[lo], kvh, w2pi_s, vstA[wave], vstB[wave]);
+    dec_unit<D, false>(a, sq, item - base[lo], kvh, w2pi_s, tab_s, vstA[wave], vstB[wave]);
   }
 }
 

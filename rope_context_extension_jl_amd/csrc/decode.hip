@@ -260,17 +260,25 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
 // ---------------------------------------------------------------------------
 // bf16 path: one wave per split, both products on the matrix cores.
 //
-// Per 64-key chunk a wave loads K (as the A operand of S^T = K Q^T, fp16,
-// 16x16x32 MFMAs: lane = one key, 8 consecutive dims) and V (row-major into a
-// wave-private LDS region). Remote keys are corrected in-lane: the pairs
-// (i, i + D/2) of a key sit in d-steps ds and ds + D/64 of the same lane. The
-// S^T tile gives each lane one query (lane % 16) and four keys per 16-key
-// block, which is exactly the A operand of O = P V for two consecutive
-// blocks; the V operand (8 keys at one dim per lane) comes from LDS with the
+// Keys stream in 16-key chunks. A chunk's K and V rows go from HBM straight
+// into one of two wave-private LDS stages (direct-to-LDS transfers, no
+// registers on the way), so the next chunk is in flight while this one is
+// computed. K comes back from LDS as the A operand of S^T = K Q^T (fp16,
+// 16x16x32 MFMAs: lane = one key, 8 consecutive dims per 32-dim step); remote
+// keys are corrected in-lane, the pairs (i, i + D/2) of a key sitting in
+// d-steps ds and ds + D/64 of the same lane. The S^T tile gives each lane one
+// query (lane % 16) and four keys, which is the A operand of O = P V in
+// 16x16x16 MFMAs; the V operand (4 keys at one dim per lane) comes from the
 // transpose read ds_read_b64_tr_b16: within 16 lanes, lane i receives element
 // i % 4 of the 8-byte rows addressed by lanes i / 4 + 4t, t = 0..3, so lanes
 // pointing at V[key_t][4c .. 4c + 3] deliver V[key_t][own dim] for 4 keys.
 // Query heads are padded to the 16 MFMA columns with zeros.
+//
+// The LDS reads of the stages are inline assembly that waits for its own
+// results. Before an LDS read that may touch a transfer's target the compiler
+// would wait for every transfer in flight, the next chunk's included; this
+// way the only wait on the transfers is the counted one at the top of each
+// chunk (transfers complete in issue order).
 //
 // Softmax: the query operand carries scale * log2(e) and the score
 // accumulator starts at -m, m a per-split reference that moves only when a
@@ -279,51 +287,47 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecArgs a) {
 // ---------------------------------------------------------------------------
 typedef _Float16 dh8v __attribute__((ext_vector_type(8)));
 typedef _Float16 dh2v __attribute__((ext_vector_type(2)));
-typedef __bf16 db8v __attribute__((ext_vector_type(8)));
+typedef __bf16 db4v __attribute__((ext_vector_type(4)));
 typedef __bf16 db2v __attribute__((ext_vector_type(2)));
 typedef short ds4v __attribute__((ext_vector_type(4)));
 typedef float df32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t du32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int DEC_CHUNK = 32;  // keys per chunk; two chunks are in flight per wave
+constexpr int DEC_CHUNK = 16;  // keys per chunk: one 16-key MFMA block
 constexpr float kDecSumMax = 256.f;
 
 template <int D>
 struct DecGeom {
-  static constexpr int NDS = D / 32;                    // 32-dim steps of the QK product
-  static constexpr int NDB = D / 16;                    // 16-dim output blocks of the PV product
-  static constexpr int NC = D / 8;                      // 16-byte chunks per key row
-  static constexpr int VROW = 2 * D;                    // LDS bytes per key row
-  static constexpr int VLD = DEC_CHUNK * 2 * D / 1024;  // 1 KiB V transfers per chunk
-  static constexpr int RPL = 64 / NC;                   // key rows per transfer
-  static constexpr int VBYTES = DEC_CHUNK * VROW;       // one LDS stage
+  static constexpr int NDS = D / 32;              // 32-dim steps of the QK product
+  static constexpr int NDB = D / 16;              // 16-dim output blocks of the PV product
+  static constexpr int NC = D / 8;                // 16-byte chunks per key row
+  static constexpr int ROW = 2 * D;               // bytes per key row
+  static constexpr int RPL = 64 / NC;             // rows per 1 KiB transfer
+  static constexpr int XFER = DEC_CHUNK / RPL;    // transfers per array per chunk
+  static constexpr int OPS = 2 * XFER;            // transfers per chunk (K and V)
+  static constexpr int KBYTES = DEC_CHUNK * ROW;  // K part of a stage, V follows
+  static constexpr int STAGE = 2 * KBYTES;        // bytes per LDS stage
 };
 
-// LDS position of 16-byte chunk ch of key row r in a V stage: rows are
-// packed (the direct-to-LDS transfers write 1 KiB contiguously) and the chunk
-// index is XOR-swizzled by the row so that the transpose reads of the PV
-// operand (4 rows x 32 bytes per 16 lanes) hit distinct banks.
+// LDS slot of 16-byte chunk ch of stage row r: ch ^ dec_swz(r). Rows are 256
+// bytes (D = 128), so unswizzled rows would fall on the same banks; with this
+// XOR the 16 rows of a K read (the same chunk of every row) hit 16 different
+// slots, and the four rows of a V transpose read (a 32-byte chunk pair per
+// row) four different pairs.
 template <int D>
-__device__ __forceinline__ int dec_vswz(int r) {
-  return (2 * r) & (DecGeom<D>::NC - 1);
+__device__ __forceinline__ int dec_swz(int r) {
+  return ((2 * r) & (DecGeom<D>::NC - 1)) ^ ((r >> 3) & 1);
 }
 
 // Per-wave constants of the key loop (all wave-uniform except the lane ids).
 struct DecCtx {
-  const uint16_t* kbase;  // this lane's K slice: head, dims 8 * g16 ..
+  const uint16_t* kbase;  // the head's K row 0
   const uint16_t* vbase;  // the head's V row 0
   int64_t rstride;        // elements between consecutive keys
   int pos, w0, G, plain, correct, k_hi;
   int cont;       // remote map x / G (real) instead of floor(x / G)
   double fk_rel;  // with cont: f(k) - k = k * fk_rel
   int lane, g16, r16;
-};
-
-// One chunk's K fragments (key k0 + 16 kb + r16, dims 32 ds + 8 g16 .. + 8);
-// its V rows go straight to an LDS stage.
-template <int D>
-struct DecBuf {
-  du32x4 k[2][D / 32];
 };
 
 template <int D>
@@ -343,7 +347,7 @@ __device__ __forceinline__ void dec_qk(const dh8v (&kf)[D / 32], const dh8v (&q)
 }
 
 // bf16 pairs of a 16-byte vector -> 8 fp16 (exact for normal bf16 values in
-// fp16 range), optionally rotated by the remote correction first.
+// fp16 range).
 __device__ __forceinline__ dh8v dec_to_f16(const du32x4& v) {
   dh8v r;
 #pragma unroll
@@ -351,175 +355,224 @@ __device__ __forceinline__ dh8v dec_to_f16(const du32x4& v) {
   return r;
 }
 
+// Chunk k0's K and V rows -> an LDS stage: transfer i of an array writes rows
+// RPL i .. RPL i + RPL - 1 (1 KiB; lane L fills byte 16 L, i.e. row
+// RPL i + L / NC, slot L % NC), so lane L fetches that row's chunk
+// (L % NC) ^ swz(row). Keys past the split end load the split's last key
+// (finite data, masked later), so the loads need no branch.
 template <int D>
-__device__ __forceinline__ void dec_issue_k(const DecCtx& c, int k0, DecBuf<D>& b) {
+__device__ __forceinline__ void dec_issue(const DecCtx& c, int k0, uint8_t* stage) {
   using G = DecGeom<D>;
+  const int rl = c.lane / G::NC, sl = c.lane % G::NC;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    // keys past the split end load the last key (finite data, masked later)
-    const int key = min(k0 + 16 * kb + c.r16, c.k_hi - 1);
-#pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds)
-      b.k[kb][ds] = __builtin_nontemporal_load((const du32x4*)(c.kbase + key * c.rstride + 32 * ds));
-  }
-}
-
-// V rows of the chunk, global -> LDS stage without registers: transfer i
-// writes rows RPL i .. RPL i + RPL - 1; lane L fills slot L, i.e. row
-// RPL i + L / NC, swizzled chunk L % NC, so it fetches the row's chunk
-// (L % NC) ^ swz(row).
-template <int D>
-__device__ __forceinline__ void dec_issue_v(const DecCtx& c, int k0, uint8_t* stage) {
-  using G = DecGeom<D>;
-#pragma unroll
-  for (int i = 0; i < G::VLD; ++i) {
-    const int row = G::RPL * i + c.lane / G::NC;
-    const int ch = (c.lane % G::NC) ^ dec_vswz<D>(row);
-    const int key = min(k0 + row, c.k_hi - 1);
+  for (int i = 0; i < G::XFER; ++i) {
+    const int row = G::RPL * i + rl;
+    const int64_t off =
+        (int64_t)min(k0 + row, c.k_hi - 1) * c.rstride + 8 * (sl ^ dec_swz<D>(row));
+    __builtin_amdgcn_global_load_lds((const void*)(c.kbase + off),
+                                     (__attribute__((address_space(3))) void*)(stage + 1024 * i),
+                                     16, 0, 2);  // 2: nontemporal
     __builtin_amdgcn_global_load_lds(
-        (const void*)(c.vbase + key * c.rstride + 8 * ch),
-        (__attribute__((address_space(3))) void*)(stage + 1024 * i), 16, 0, 2);  // 2: nontemporal
+        (const void*)(c.vbase + off),
+        (__attribute__((address_space(3))) void*)(stage + G::KBYTES + 1024 * i), 16, 0, 2);
   }
 }
 
-// p = exp2(s') of the chunk's two 16-key blocks, packed as the A operand of
-// O = P V; returns the lane's sum of the rounded p.
-__device__ __forceinline__ float dec_exp(const df32x4 (&st)[2], db8v& pb) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pb[4 * kb + r] = (__bf16)__builtin_amdgcn_exp2f(st[kb][r]);
-  const db2v one = {(__bf16)1.f, (__bf16)1.f};
-  float ps0 =
-      __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one, 0.f, false);
-  float ps1 =
-      __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one, 0.f, false);
-  ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one, ps0, false);
-  ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one, ps1, false);
-  return ps0 + ps1;
-}
-
+// The chunk issued before the last one has landed: only the OPS transfers
+// of the chunk issued after it may still be in flight.
 template <int D>
-__device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<D>& b,
+__device__ __forceinline__ void dec_wait_chunk() {
+  static_assert(DecGeom<D>::OPS == 8 || DecGeom<D>::OPS == 4, "transfer count");
+  if constexpr (DecGeom<D>::OPS == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+
+// The lane's K fragments of a stage (16 bytes at each of the NDS addresses,
+// plus the stage offset OFF); V operands (8 bytes transposed at each of the
+// NDB addresses). Each block waits for its own results before it ends, so its
+// outputs are complete when the compiler next sees them.
+template <int OFF>
+__device__ __forceinline__ void dec_read_k(const uint32_t (&a)[4], du32x4 (&k)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+      : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void dec_read_k(const uint32_t (&a)[2], du32x4 (&k)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%4\n\t"
+      "ds_read_b128 %1, %3 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1])
+      : "v"(a[0]), "v"(a[1]), "i"(OFF)
+      : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void dec_read_v(const uint32_t (&a)[8], ds4v (&v)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "i"(OFF)
+      : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void dec_read_v(const uint32_t (&a)[4], ds4v (&v)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+      : "memory");
+}
+
+// p = exp2(s') of the chunk's 16 keys, packed as the A operand of O = P V;
+// returns the lane's sum of the rounded p.
+__device__ __forceinline__ float dec_exp(const df32x4& s, ds4v& pb) {
+  const db4v p = {(__bf16)__builtin_amdgcn_exp2f(s[0]), (__bf16)__builtin_amdgcn_exp2f(s[1]),
+                  (__bf16)__builtin_amdgcn_exp2f(s[2]), (__bf16)__builtin_amdgcn_exp2f(s[3])};
+  pb = __builtin_bit_cast(ds4v, p);
+  const db2v one = {(__bf16)1.f, (__bf16)1.f};
+  const float ps =
+      __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, 0.f, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, ps, false);
+}
+
+// One 16-key chunk from LDS stage ST (the even chunks of a split use stage 0,
+// the odd ones stage 1). rc / rs carry the even chunk's correction cos / sin
+// to the odd one.
+template <int D, int ST>
+__device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0,
+                                          const uint32_t (&ka)[DecGeom<D>::NDS],
+                                          const uint32_t (&va)[DecGeom<D>::NDB],
                                           const dh8v (&qa)[D / 32], const dh8v (&qr)[D / 32],
-                                          const double* w2pi, const uint8_t* vb,
-                                          DecState<D>& st, bool step16,
-                                          const dh2v (&cst)[D / 64][4],
-                                          const dh2v (&sst)[D / 64][4], float& chk) {
+                                          const double (&w2)[D / 64][8], DecState<D>& st,
+                                          bool step16, const dh2v (&cst)[D / 64][4],
+                                          const dh2v (&sst)[D / 64][4], dh2v (&rc)[D / 64][4],
+                                          dh2v (&rs)[D / 64][4], float& chk) {
   using G = DecGeom<D>;
-  constexpr int NDS = G::NDS, NDB = G::NDB, VROW = G::VROW;
-  // ---- cos / sin of the correction R_{f(k) - k} of the lane's key in both
-  // blocks (pairs (ds, ds + NDS/2), frequencies 32 ds + 8 g16 + j), as fp16
-  // pairs of neighbouring frequencies (j, j + 1), the layout of the key
-  // fragments. They depend on the key index only, so they are computed
-  // before the chunk's data is first touched, i.e. while its loads (and the
-  // next chunk's) are still in flight.
-  dh2v rc[2][NDS / 2][4], rs[2][NDS / 2][4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key = k0 + 16 * kb + c.r16;
-    if (c.correct && c.pos - (k0 + 16 * kb) > c.w0) {  // the block has remote keys
-      if (kb == 1 && step16) {
-        // key + 16 (block 0 is remote too): the angle moves by a fixed step,
-        // R_{d + c16} = R_d R_{c16}
-#pragma unroll
-        for (int ds = 0; ds < NDS / 2; ++ds)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            rc[1][ds][m] = rc[0][ds][m] * cst[ds][m] - rs[0][ds][m] * sst[ds][m];
-            rs[1][ds][m] = rs[0][ds][m] * cst[ds][m] + rc[0][ds][m] * sst[ds][m];
-          }
-      } else {
-        const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
-#pragma unroll
-        for (int ds = 0; ds < NDS / 2; ++ds)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            float c0, s0, c1, s1;
-            rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m], c0, s0);
-            rope_cs_turns(delta, w2pi[32 * ds + 8 * c.g16 + 2 * m + 1], c1, s1);
-            rc[kb][ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
-            rs[kb][ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
-          }
-      }
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // ---- S^T = K Q^T per 16-key block, seeded with -m
-  df32x4 s2[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int kfirst = k0 + 16 * kb;
-    const int klast = min(kfirst + 15, c.k_hi - 1);
-    const bool any_rem = !c.plain && c.pos - kfirst > c.w0;
-    const bool any_loc = c.plain || c.pos - klast <= c.w0;
-    const int key = kfirst + c.r16;
-    dh8v kf[NDS];
-    if (c.correct && c.pos - key > c.w0) {
-      // R_{f(k) - k}: absolute -> remapped rotation, pairs (ds, ds + NDS/2),
-      // in packed fp16 arithmetic on two neighbouring frequencies at a time
-      // (the bf16 key values are exact in fp16)
+  constexpr int NDS = G::NDS, NDB = G::NDB;
+  constexpr int KOFF = ST * G::STAGE, VOFF = ST * G::STAGE + G::KBYTES;
+  const int key = k0 + c.r16;
+  const int klast = min(k0 + DEC_CHUNK - 1, c.k_hi - 1);
+  const bool any_rem = !c.plain && c.pos - k0 > c.w0;
+  const bool any_loc = c.plain || c.pos - klast <= c.w0;
+  const bool fix = c.correct && any_rem;  // the chunk has keys to correct
+  // ---- cos / sin of the correction R_{f(k) - k} of the lane's key (pairs
+  // (ds, ds + NDS/2), frequencies 32 ds + 8 g16 + j), as fp16 pairs of
+  // neighbouring frequencies (j, j + 1), the layout of the key fragments.
+  // They depend on the key index only: computed while the chunk's transfers
+  // may still be in flight.
+  if (fix) {
+    if (ST == 1 && step16) {
+      // the even chunk k0 - 16 is farther from pos, hence remote too: its
+      // rotation moves by a fixed step, R_{d + c16} = R_d R_{c16}
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const uint32_t w0 = b.k[kb][ds][m], w1 = b.k[kb][ds + NDS / 2][m];
-          const dh2v x0 = {(_Float16)__uint_as_float(w0 << 16),
-                           (_Float16)__uint_as_float(w0 & 0xffff0000u)};
-          const dh2v x1 = {(_Float16)__uint_as_float(w1 << 16),
-                           (_Float16)__uint_as_float(w1 & 0xffff0000u)};
-          const dh2v y0 = x0 * rc[kb][ds][m] - x1 * rs[kb][ds][m];
-          const dh2v y1 = x0 * rs[kb][ds][m] + x1 * rc[kb][ds][m];
-          kf[ds][2 * m] = y0[0];
-          kf[ds][2 * m + 1] = y0[1];
-          kf[ds + NDS / 2][2 * m] = y1[0];
-          kf[ds + NDS / 2][2 * m + 1] = y1[1];
+          const dh2v c0 = rc[ds][m], s0 = rs[ds][m];
+          rc[ds][m] = c0 * cst[ds][m] - s0 * sst[ds][m];
+          rs[ds][m] = s0 * cst[ds][m] + c0 * sst[ds][m];
         }
     } else {
+      const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) kf[ds] = dec_to_f16(b.k[kb][ds]);
-    }
-    if (!any_loc) {
-      dec_qk<D>(kf, qr, st.negm, s2[kb]);
-    } else if (!any_rem) {
-      dec_qk<D>(kf, qa, st.negm, s2[kb]);
-    } else {
-      // block across the window edge: each lane (one key) keeps its fragment
-      // for its own route and zeros it for the other, so one accumulation
-      // chain adds exactly one product per key
-      const bool rem = c.pos - key > c.w0;
-      dh8v kl[NDS], krm[NDS];
+      for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const dh8v z = {};
-        kl[ds] = rem ? z : kf[ds];
-        krm[ds] = rem ? kf[ds] : z;
-      }
-      df32x4 t;
-      dec_qk<D>(kl, qa, st.negm, t);
-      dec_qk<D>(krm, qr, t, s2[kb]);
-    }
-    // raw scores of an fp16 operand out of range are not finite: their sum
-    // carries that to the end of the split
-    chk += (s2[kb][0] + s2[kb][1]) + (s2[kb][2] + s2[kb][3]);
-    if (klast - kfirst < 15) {  // keys past the split end
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (kfirst + 4 * c.g16 + r >= c.k_hi) s2[kb][r] = -INFINITY;
+        for (int m = 0; m < 4; ++m) {
+          float c0, s0, c1, s1;
+          rope_cs_turns(delta, w2[ds][2 * m], c0, s0);
+          rope_cs_turns(delta, w2[ds][2 * m + 1], c1, s1);
+          rc[ds][m] = dh2v{(_Float16)c0, (_Float16)c1};
+          rs[ds][m] = dh2v{(_Float16)s0, (_Float16)s1};
+        }
     }
   }
+  dec_wait_chunk<D>();
+  // ---- S^T = K Q^T, seeded with -m
+  du32x4 kr[NDS];
+  dec_read_k<KOFF>(ka, kr);
+  dh8v kf[NDS];
+  if (fix && c.pos - key > c.w0) {
+    // R_{f(k) - k}: absolute -> remapped rotation in packed fp16 arithmetic
+    // on two neighbouring frequencies at a time (bf16 keys are exact in fp16)
+#pragma unroll
+    for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const du32x4 r0 = kr[ds], r1 = kr[ds + NDS / 2];
+        const uint32_t w0 = r0[m], w1 = r1[m];
+        const dh2v x0 = {(_Float16)__uint_as_float(w0 << 16),
+                         (_Float16)__uint_as_float(w0 & 0xffff0000u)};
+        const dh2v x1 = {(_Float16)__uint_as_float(w1 << 16),
+                         (_Float16)__uint_as_float(w1 & 0xffff0000u)};
+        const dh2v y0 = x0 * rc[ds][m] - x1 * rs[ds][m];
+        const dh2v y1 = x0 * rs[ds][m] + x1 * rc[ds][m];
+        kf[ds][2 * m] = y0[0];
+        kf[ds][2 * m + 1] = y0[1];
+        kf[ds + NDS / 2][2 * m] = y1[0];
+        kf[ds + NDS / 2][2 * m + 1] = y1[1];
+      }
+  } else {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) kf[ds] = dec_to_f16(kr[ds]);
+  }
+  df32x4 s;
+  if (!any_loc) {
+    dec_qk<D>(kf, qr, st.negm, s);
+  } else if (!any_rem) {
+    dec_qk<D>(kf, qa, st.negm, s);
+  } else {
+    // chunk across the window edge: each lane (one key) keeps its fragment
+    // for its own route and zeros it for the other, so one accumulation
+    // chain adds exactly one product per key
+    const bool rem = c.pos - key > c.w0;
+    dh8v kl[NDS], krm[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const dh8v z = {};
+      kl[ds] = rem ? z : kf[ds];
+      krm[ds] = rem ? kf[ds] : z;
+    }
+    df32x4 t;
+    dec_qk<D>(kl, qa, st.negm, t);
+    dec_qk<D>(krm, qr, t, s);
+  }
+  // raw scores of an fp16 operand out of range are not finite: their sum
+  // carries that to the end of the split
+  chk += (s[0] + s[1]) + (s[2] + s[3]);
+  if (klast - k0 < DEC_CHUNK - 1) {  // keys past the split end
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (k0 + 4 * c.g16 + r >= c.k_hi) s[r] = -INFINITY;
+  }
   // ---- softmax with the lazy reference
-  db8v pb;
-  float psum = dec_exp(s2, pb);
+  ds4v pb;
+  float psum = dec_exp(s, pb);
   const bool need = !(psum <= kDecSumMax) || st.m == -INFINITY;
   if (__any(need)) {
     // move the reference of the queries that need it to their chunk max; a
     // query's scores live in lanes r16 + 16 g, g = 0..3
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s2[kb][r]);
+    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     float nf = need ? 1.f : 0.f;
@@ -540,40 +593,22 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0, const DecBuf<
       for (int db = 0; db < NDB; ++db) st.acc[db][r] *= al;
     }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s2[kb][r] -= delta;
-    psum = dec_exp(s2, pb);
+    for (int r = 0; r < 4; ++r) s[r] -= delta;
+    psum = dec_exp(s, pb);
   }
   st.lsum += psum;
-  // ---- O += P V, the V operand through transpose reads of the LDS stage:
-  // lane (g16, r16) addresses row 4 g16 + r16 / 4 (and + 16), dims
-  // 16 db + 4 (r16 % 4) .. + 3, i.e. byte 8 (r16 & 1) of chunk
-  // 2 db + (r16 & 3) / 2 before the swizzle
-  const int row = 4 * c.g16 + (c.r16 >> 2);
-  const int sub = 8 * (c.r16 & 1);
+  // ---- O += P V
+  ds4v vr[NDB];
+  dec_read_v<VOFF>(va, vr);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int ch = 2 * db + ((c.r16 & 3) >> 1);
-    const ds4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) ds4v*)(vb + row * VROW +
-                                                  16 * (ch ^ dec_vswz<D>(row)) + sub));
-    const ds4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) ds4v*)(vb + (row + 16) * VROW +
-                                                  16 * (ch ^ dec_vswz<D>(row + 16)) + sub));
-    const db8v vop =
-        __builtin_bit_cast(db8v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vop, st.acc[db], 0, 0, 0);
-  }
+  for (int db = 0; db < NDB; ++db)
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vr[db], st.acc[db], 0, 0, 0);
 }
 
-// One work unit of the bf16 decode for one wave: keys [s kps, (s + 1) kps)
-// of KV head kvh of sequence sq, leaving the partial of each query head of
-// the group. vA / vB: this wave's two V stages.
 // cos / sin tables a workgroup computes once for the rotations shared by all
 // of its lanes: [0][i] of pos * omega_i, [1][i] of f(pos) * omega_i (the
 // query at the absolute and the remapped position), [2][i] of c16 * omega_i
-// (the step between a chunk's two 16-key blocks). One angle per thread.
+// (the step between the two chunks of a 32-key pair). One angle per thread.
 template <int D>
 __device__ __forceinline__ void dec_tables(const DecArgs& a, const DecSeq& sq, bool step16,
                                            const double* w2pi_s, float2 (*tab)[D / 2]) {
@@ -594,17 +629,20 @@ __device__ __forceinline__ void dec_tables(const DecArgs& a, const DecSeq& sq, b
   }
 }
 
-// Whether the second 16-key block of a chunk takes its cos / sin from the
-// first by one rotation R_{c16}: with G dividing 16 (floor map) or the
+// Whether the odd chunk of a 32-key pair takes its cos / sin from the even
+// one by one rotation R_{c16}: with G dividing 16 (floor map) or the
 // continuous map, f(k) - k moves by the same c16 from key k to key k + 16.
 __device__ __forceinline__ bool dec_step16(const DecArgs& a, const DecSeq& sq) {
   return !a.plain && sq.G > 1 && (a.cont || 16 % sq.G == 0);
 }
 
-template <int D, bool STEP16>
+// One work unit of the bf16 decode for one wave: keys [s kps, (s + 1) kps)
+// of KV head kvh of sequence sq, leaving the partial of each query head of
+// the group. stages: this wave's two LDS stages (2 * STAGE bytes).
+template <int D>
 __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int s, int kvh,
                                          const double* w2pi_s, const float2 (*tab)[D / 2],
-                                         uint8_t* sA, uint8_t* sB) {
+                                         uint8_t* stages) {
   using G = DecGeom<D>;
   constexpr int NDS = G::NDS, NDB = G::NDB;
   const int lane = threadIdx.x & 63;
@@ -618,7 +656,7 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   DecCtx c;
   c.k_hi = min(k_lo + a.kps, sq.pos + 1);
   c.rstride = (int64_t)a.Hkv * D;
-  c.kbase = kc + (int64_t)kvh * D + 8 * g16;
+  c.kbase = kc + (int64_t)kvh * D;
   c.vbase = vc + (int64_t)kvh * D;
   c.pos = sq.pos;
   c.w0 = a.w0;
@@ -631,12 +669,27 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   c.g16 = g16;
   c.r16 = r16;
 
-  // the first chunk is in flight while the query operands and tables are
-  // computed
-  DecBuf<D> bA, bB;
-  int k0 = k_lo;
-  dec_issue_k<D>(c, k0, bA);
-  dec_issue_v<D>(c, k0, sA);
+  // the first chunk is in flight while the query operands are computed
+  dec_issue<D>(c, k_lo, stages);
+
+  // LDS addresses of the lane's reads, relative to a stage's K or V part
+  // (the stage and part offsets are immediates of the reads): K row r16,
+  // chunks 4 ds + g16 (dims 32 ds + 8 g16 .. + 8); for the V transpose reads
+  // row 4 g16 + r16 / 4, dims 16 db + 4 (r16 % 4) .. + 3, i.e. byte
+  // 8 (r16 & 1) of chunk 2 db + (r16 & 3) / 2
+  uint32_t ka[NDS], va[NDB];
+  {
+    const uint32_t sb =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)stages;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+      ka[ds] = sb + r16 * G::ROW + 16 * ((4 * ds + g16) ^ dec_swz<D>(r16));
+    const int vrow = 4 * g16 + (r16 >> 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      va[db] = sb + vrow * G::ROW +
+               16 * ((2 * db + ((r16 & 3) >> 1)) ^ dec_swz<D>(vrow)) + 8 * (r16 & 1);
+  }
 
   // query operands (B of S^T = K Q^T): lane holds dims 32 ds + 8 g16 + j of
   // query head r16, rotated at pos (qa) and at f(pos) (qr), times scale*log2 e
@@ -671,9 +724,16 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
         }
       }
   }
-  // R_{c16} between a chunk's two 16-key blocks (see dec_step16), as fp16
+  // the lane's correction frequencies (in turns), held in registers: the key
+  // loop reads no LDS outside its stages
+  double w2[NDS / 2][8];
+#pragma unroll
+  for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w2[ds][j] = w2pi_s[32 * ds + 8 * g16 + j];
+  // R_{c16} between the two chunks of a pair (see dec_step16), as fp16
   // pairs of neighbouring frequencies
-  const bool step16 = STEP16 && dec_step16(a, sq);
+  const bool step16 = dec_step16(a, sq);
   dh2v cst[NDS / 2][4], sst[NDS / 2][4];
   if (step16) {
 #pragma unroll
@@ -694,23 +754,21 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   st.m = -INFINITY;
   st.lsum = 0.f;
   float chk = 0.f;
+  dh2v rc[NDS / 2][4], rs[NDS / 2][4];
 
-  // chunk i + 1 (K in registers, V in the other LDS stage) is in flight
-  // while chunk i is computed. The next chunk is always issued: its keys are
-  // clamped to the split, so past the end it re-reads the last key (from L2)
-  // and the loads need no branch.
-  for (;;) {
-    dec_issue_k<D>(c, k0 + DEC_CHUNK, bB);
-    dec_issue_v<D>(c, k0 + DEC_CHUNK, sB);
-    __builtin_amdgcn_sched_barrier(0);  // all of the next chunk's loads go out first
-    dec_chunk<D>(c, k0, bA, qa, qr, w2pi_s, sA, st, step16, cst, sst, chk);
+  // chunk i + 1 is in flight while chunk i is computed; the next chunk is
+  // always issued (past the split end it re-reads the last key, from L2).
+  // Chunks alternate between the two stages; a stage is refilled only after
+  // the chunk that read it, whose reads have completed.
+  for (int k0 = k_lo;; k0 += 2 * DEC_CHUNK) {
+    dec_issue<D>(c, k0 + DEC_CHUNK, stages + G::STAGE);
+    __builtin_amdgcn_sched_barrier(0);  // the transfers go out first
+    dec_chunk<D, 0>(c, k0, ka, va, qa, qr, w2, st, step16, cst, sst, rc, rs, chk);
     if (k0 + DEC_CHUNK >= c.k_hi) break;
-    dec_issue_k<D>(c, k0 + 2 * DEC_CHUNK, bA);
-    dec_issue_v<D>(c, k0 + 2 * DEC_CHUNK, sA);
+    dec_issue<D>(c, k0 + 2 * DEC_CHUNK, stages);
     __builtin_amdgcn_sched_barrier(0);
-    dec_chunk<D>(c, k0 + DEC_CHUNK, bB, qa, qr, w2pi_s, sB, st, step16, cst, sst, chk);
+    dec_chunk<D, 1>(c, k0 + DEC_CHUNK, ka, va, qa, qr, w2, st, step16, cst, sst, rc, rs, chk);
     if (k0 + 2 * DEC_CHUNK >= c.k_hi) break;
-    k0 += 2 * DEC_CHUNK;
   }
   // no transfer into these LDS stages may outlive the unit
   __builtin_amdgcn_s_waitcnt(0);
@@ -747,10 +805,7 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
 template <int D>
 __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   using G = DecGeom<D>;
-  // two V stages per wave, as separate arrays so that reads of one are known
-  // not to alias the transfers in flight into the other
-  __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[4][2 * G::STAGE];  // two stages per wave
   __shared__ double w2pi_s[D / 2];
   __shared__ float2 tab_s[3][D / 2];
   // the wave index is uniform per wave: say so, so that every split-derived
@@ -766,7 +821,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   const int hgroups = (a.Hkv + 3) >> 2;
   const int s = blockIdx.x / hgroups, kvh = (blockIdx.x % hgroups) * 4 + wave;
   if (kvh >= a.Hkv) return;
-  dec_unit<D, true>(a, sq, s, kvh, w2pi_s, tab_s, vstA[wave], vstB[wave]);
+  dec_unit<D>(a, sq, s, kvh, w2pi_s, tab_s, stg[wave]);
 }
 
 // Batch: a fixed grid of workgroups walks the work list the plan kernel
@@ -778,8 +833,7 @@ template <int D>
 __global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, const int* base,
                                                                    int B) {
   using G = DecGeom<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t vstA[4][G::VBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t vstB[4][G::VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[4][2 * G::STAGE];  // two stages per wave
   __shared__ double w2pi_s[D / 2];
   __shared__ float2 tab_s[3][D / 2];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -798,11 +852,10 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, co
     // this unit's tables (every wave passes both barriers, also the waves
     // past the last KV head)
     __syncthreads();
-    dec_tables<D>(a, sq, false, w2pi_s, tab_s);
+    dec_tables<D>(a, sq, dec_step16(a, sq), w2pi_s, tab_s);
     __syncthreads();
     if (kvh >= a.Hkv) continue;
-    // (the batch kernel has no registers to spare for the step table)
-    dec_unit<D, false>(a, sq, item - base[lo], kvh, w2pi_s, tab_s, vstA[wave], vstB[wave]);
+    dec_unit<D>(a, sq, item - base[lo], kvh, w2pi_s, tab_s, stg[wave]);
   }
 }
 

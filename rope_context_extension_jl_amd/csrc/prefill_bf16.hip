@@ -355,6 +355,13 @@ struct Tctx {
   int R;                 // padded row stride of vt
   int q0, q1, len, nkt, w0;
   int tid, hh, l32, myq;
+  // this lane's first source byte of its tile transfers (tile 0), fixed for
+  // the whole walk, and the byte step between a lane's value transfers: the
+  // per-tile address is then one uniform offset away
+  const char* kabs_l;
+  const char* krem_l;
+  const char* vt_l;
+  int64_t vstep;
 };
 
 // Running softmax state of one lane's query row. Scores come out of the
@@ -385,27 +392,33 @@ __device__ __forceinline__ int tile_cls_of(const Tctx& c, int j) {
 // so its source address advances by a constant per transfer.
 __device__ __forceinline__ void tile_dma(const Tctx& c, int j, bool rem, uint16_t* ks,
                                          uint16_t* vs) {
+  const int w = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  const char* kg = (rem ? c.krem_l : c.kabs_l) + (int64_t)j * (PF_BN * PF_D * 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(kg + 16 * PF_D * 2 * i),
+        (__attribute__((address_space(3))) void*)(ks + 512 * (w + 4 * i)), 16, 0, 0);
+  const char* vg = c.vt_l + (int64_t)j * (PF_BN * 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(vg + c.vstep * i),
+        (__attribute__((address_space(3))) void*)(vs + 512 * (w + 4 * i)), 16, 0, 0);
+}
+// The lane's tile-0 sources of tile_dma (NW = 4) or tile_dma8 (NW = 8): key
+// row 4 w + L / 16 of the tile at swizzled chunk (L % 16) ^ kswz(row);
+// value^T row 8 w + L / 8 at chunk (L % 8) ^ vswz(row); a value transfer
+// moves on by 8 NW rows.
+template <int NW>
+__device__ __forceinline__ void tile_dma_lanes(Tctx& c) {
   const int w = __builtin_amdgcn_readfirstlane(c.tid >> 6), lane = c.tid & 63;
-  const uint16_t* kg = (rem ? c.krem : c.kabs) + (int64_t)j * PF_BN * PF_D;
-  {
-    const int r0 = 4 * w + (lane >> 4), lc = (lane & 15) ^ kswz(r0);
-    const uint16_t* src = kg + r0 * PF_D + 8 * lc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src + 16 * PF_D * i),
-          (__attribute__((address_space(3))) void*)(ks + 512 * (w + 4 * i)), 16, 0, 0);
-  }
-  const uint16_t* vg = c.vt + j * PF_BN;
-  {
-    const int r0 = 8 * w + (lane >> 3), lc = (lane & 7) ^ vswz(r0);
-    const uint16_t* src = vg + (int64_t)r0 * c.R + 8 * lc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src + (int64_t)32 * c.R * i),
-          (__attribute__((address_space(3))) void*)(vs + 512 * (w + 4 * i)), 16, 0, 0);
-  }
+  const int rk = 4 * w + (lane >> 4), lk = (lane & 15) ^ kswz(rk);
+  const int rv = 8 * w + (lane >> 3), lv = (lane & 7) ^ vswz(rv);
+  c.kabs_l = (const char*)(c.kabs + rk * PF_D + 8 * lk);
+  c.krem_l = (const char*)(c.krem + rk * PF_D + 8 * lk);
+  c.vt_l = (const char*)(c.vt + (int64_t)rv * c.R + 8 * lv);
+  c.vstep = (int64_t)(8 * NW) * c.R * 2;
 }
 // End of a tile: this wave's transfers into the other stage have landed,
 // then every wave is past its reads of this stage.
@@ -589,24 +602,44 @@ __device__ __forceinline__ void reference_pv(const Tctx& c, const uint16_t* vs, 
 }
 
 // A tile no mask can touch (all-remote, or wholly below the causal diagonal
-// in a local or plain walk): the two 32-key blocks are scored one after the
-// other, and the exp of the first block is interleaved with the second
-// block's MFMAs, so the wave's VALU work overlaps its own matrix work. Same
+// in a local or plain walk), scheduled by hand: the key operands of the first
+// 32-key block are read together and block 1's are read while block 0's
+// MFMAs run; block 1's MFMAs run under block 0's exponentials and the first
+// value operands are read then; the PV product reads the operands of its
+// next k-step while the current one runs. So no MFMA waits for a read issued
+// just before it. The wave raises its issue priority over its MFMA phases and
+// drops it for the second block's exponentials, so the other wave on the
+// SIMD gets the issue slots while this one has only vector work. Same
 // operations, in the same order per value, as qk_lds followed by
 // softmax_pv_any.
 __device__ __forceinline__ void tile_nomask(const Tctx& c, const uint16_t* ks, const uint16_t* vs,
                                             const h8v (&q)[8], RowState& st) {
-  const int x = kswz(c.l32);
-  f32x16 s[2];
-  auto chain = [&](int bk) __attribute__((always_inline)) {
-    const uint16_t* krow = ks + (32 * bk + c.l32) * PF_D;
-    s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8v*)(krow + 8 * (c.hh ^ x)), q[0],
-                                                   st.negm, 0, 0, 0);
-#pragma unroll
-    for (int cc = 1; cc < 8; ++cc)
-      s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-          *(const h8v*)(krow + 8 * ((2 * cc + c.hh) ^ x)), q[cc], s[bk], 0, 0, 0);
+  const int x = kswz(c.l32), y = vswz(c.l32);
+  const uint16_t* kr0 = ks + c.l32 * PF_D;
+  const uint16_t* kr1 = ks + (32 + c.l32) * PF_D;
+  auto vop = [&](int db, int kk) __attribute__((always_inline)) -> b8v {
+    return *(const b8v*)(vs + (32 * db + c.l32) * PF_BN + 8 * ((2 * kk + c.hh) ^ y));
   };
+  h8v ka[8], kb[8];
+  f32x16 s[2];
+  __builtin_amdgcn_s_setprio(1);
+  // ---- block 0
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) ka[cc] = *(const h8v*)(kr0 + 8 * ((2 * cc + c.hh) ^ x));
+  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], q[0], st.negm, 0, 0, 0);
+#pragma unroll
+  for (int cc = 1; cc < 8; ++cc)
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[cc], q[cc], s[0], 0, 0, 0);
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) kb[cc] = *(const h8v*)(kr1 + 8 * ((2 * cc + c.hh) ^ x));
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // block 0's reads
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an MFMA of block 0
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a read for block 1
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- block 1, block 0's exponentials, the first value operands
   const b2v one = {(__bf16)1.f, (__bf16)1.f};
   b8v pb[4];
   float ps0 = 0.f, ps1 = 0.f;
@@ -626,20 +659,69 @@ __device__ __forceinline__ void tile_nomask(const Tctx& c, const uint16_t* ks, c
                                             ps1, false);
     }
   };
-  chain(0);
-  __builtin_amdgcn_sched_barrier(0);
-  // block 1's reads and MFMAs, each MFMA followed by a share of block 0's exp
-  chain(1);
+  b8v vc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vc[db] = vop(db, 0);
+  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kb[0], q[0], st.negm, 0, 0, 0);
+#pragma unroll
+  for (int cc = 1; cc < 8; ++cc)
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kb[cc], q[cc], s[1], 0, 0, 0);
   expb(0);
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // value operands of k-step 0
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   expb(1);
-  reference_pv(c, vs, s, pb, ps0 + ps1, st);
+  float psum = ps0 + ps1;
+  // ---- reference (rare), row sum, O^T += V^T P^T
+  const bool need = !(psum <= kSumMax) || st.m == -INFINITY;
+  if (__any(need)) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[bk][r]);
+    mt = max_with_partner(mt);
+    const bool grow = max_with_partner(need ? 1.f : 0.f) > 0.f && mt > -INFINITY;
+    const float delta = grow ? mt : 0.f;
+    const float alpha = grow ? (st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-mt)) : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[i][r] *= alpha;
+    if (grow) st.m = (st.m == -INFINITY ? 0.f : st.m) + mt;
+    const float nm = st.m == -INFINITY ? 0.f : -st.m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.negm[r] = nm;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[bk][r] -= delta;
+    psum = exp_pack(s, pb);
+  }
+  st.l += psum;
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    b8v vn[4];
+    if (kk < 3) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vn[db] = vop(db, kk + 1);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[db], pb[kk], st.acc[db], 0, 0, 0);
+    if (kk < 3) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vc[db] = vn[db];
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // One key tile from stage (kc, vc) while the next one (if any) streams into
@@ -771,6 +853,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
   c.kabs = a.kabs + ((int64_t)g * R + sq.pad_off) * PF_D;
   c.krem = a.krem + ((int64_t)g * R + sq.pad_off) * PF_D;
   c.vt = a.vt + (int64_t)g * PF_D * R + sq.pad_off;
+  tile_dma_lanes<4>(c);
   const bool qvalid = c.myq < sq.len;
 
   // raw query row slice of this lane (zeros past the sequence end); re-read
@@ -897,29 +980,23 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
 constexpr int PAIR_STAGES = 3;
 
 // Tile j into a stage by 8 waves: transfer o = w + 8 i (i < 2) of each array.
+// (kswz(r0 + 32 i) = kswz(r0), vswz(r0 + 64 i) = vswz(r0): a lane's swizzle
+// is the same in both of its transfers of an array)
 __device__ __forceinline__ void tile_dma8(const Tctx& c, int j, bool rem, uint16_t* ks,
                                           uint16_t* vs) {
-  const int w = __builtin_amdgcn_readfirstlane(c.tid >> 6), lane = c.tid & 63;
-  const uint16_t* kg = (rem ? c.krem : c.kabs) + (int64_t)j * PF_BN * PF_D;
-  {
-    const int r0 = 4 * w + (lane >> 4), lc = (lane & 15) ^ kswz(r0);  // kswz(r0 + 32 i) = kswz(r0)
-    const uint16_t* src = kg + r0 * PF_D + 8 * lc;
+  const int w = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  const char* kg = (rem ? c.krem_l : c.kabs_l) + (int64_t)j * (PF_BN * PF_D * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src + 32 * PF_D * i),
-          (__attribute__((address_space(3))) void*)(ks + 512 * (w + 8 * i)), 16, 0, 0);
-  }
-  const uint16_t* vg = c.vt + j * PF_BN;
-  {
-    const int r0 = 8 * w + (lane >> 3), lc = (lane & 7) ^ vswz(r0);  // vswz(r0 + 64 i) = vswz(r0)
-    const uint16_t* src = vg + (int64_t)r0 * c.R + 8 * lc;
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(kg + 32 * PF_D * 2 * i),
+        (__attribute__((address_space(3))) void*)(ks + 512 * (w + 8 * i)), 16, 0, 0);
+  const char* vg = c.vt_l + (int64_t)j * (PF_BN * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src + (int64_t)64 * c.R * i),
-          (__attribute__((address_space(3))) void*)(vs + 512 * (w + 8 * i)), 16, 0, 0);
-  }
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(vg + c.vstep * i),
+        (__attribute__((address_space(3))) void*)(vs + 512 * (w + 8 * i)), 16, 0, 0);
 }
 
 // End of a tile of the 3-stage walk: the tile after this one has landed
@@ -988,6 +1065,7 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
   c.kabs = a.kabs + ((int64_t)g * R + sq.pad_off) * PF_D;
   c.krem = a.krem + ((int64_t)g * R + sq.pad_off) * PF_D;
   c.vt = a.vt + (int64_t)g * PF_D * R + sq.pad_off;
+  tile_dma_lanes<8>(c);
   const bool qvalid = c.myq < sq.len;
 
   const uint16_t* qp =

@@ -50,7 +50,17 @@ extern "C" {
 #define JL_EHIP (-3)         /* HIP launch or runtime error                      */
 #define JL_EWORKSPACE (-4)   /* workspace NULL or smaller than the size query    */
 
-typedef enum { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
+/* The enums are int-sized in both languages; in C++ they get int as their
+ * fixed underlying type, so any int a C caller passes (an unsupported dtype,
+ * a mode with flags OR-ed in) is a valid value there too and is rejected or
+ * decoded by the callee, never undefined. */
+#ifdef __cplusplus
+#define JL_ENUM_BASE : int
+#else
+#define JL_ENUM_BASE
+#endif
+
+typedef enum JL_ENUM_BASE { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
 
 /* FUSED: one pass, each (query tile, key tile) classified local / remote /
  *        boundary, per-element select on boundary tiles.
@@ -58,7 +68,7 @@ typedef enum { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
  *        window+remapped) merged by Eq. 7. A checked alternative.
  * PLAIN: ordinary causal RoPE attention (every pair local) -- the baseline
  *        the bifocal overhead is measured against. */
-typedef enum { JL_MODE_FUSED = 0, JL_MODE_IE = 1, JL_MODE_PLAIN = 2 } jl_mode;
+typedef enum JL_ENUM_BASE { JL_MODE_FUSED = 0, JL_MODE_IE = 1, JL_MODE_PLAIN = 2 } jl_mode;
 
 /* Remote-map flag, OR-ed into the mode argument of every call that takes one
  * (e.g. (jl_mode)(JL_MODE_FUSED | JL_REMAP_CONTINUOUS)). Without it the

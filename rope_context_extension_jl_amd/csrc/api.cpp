@@ -111,12 +111,20 @@ static jl_mode strip_remap(jl_mode mode, int* cont) {
   return (jl_mode)(m & ~JL_REMAP_CONTINUOUS);
 }
 
+// Head counts and head dims any entry point or size query accepts. With
+// T, capacity <= 2^31, heads <= 2^16 and d <= 256 every byte count below
+// stays far inside size_t.
+constexpr int kMaxHeads = 1 << 16;
+static bool heads_ok(int Hq, int Hkv) {
+  return Hkv >= 1 && Hq >= Hkv && Hq <= kMaxHeads && Hq % Hkv == 0;
+}
+static bool dim_ok(int d) { return d >= 2 && d <= 256 && d % 2 == 0; }
+
 static bool prefill_shape_ok(int64_t T, int B, int Hq, int Hkv, int d, jl_dtype dt, jl_mode mode) {
-  if (T < 0 || B < 1 || B > 4096 || Hq < 1 || Hkv < 1 || Hq % Hkv) return false;
+  if (T < 0 || B < 1 || B > 4096 || !heads_ok(Hq, Hkv) || !dim_ok(d)) return false;
   if (T > (int64_t)INT32_MAX / 2) return false;
   if (dt != JL_BF16 && dt != JL_FP32) return false;
   if (mode != JL_MODE_FUSED && mode != JL_MODE_IE && mode != JL_MODE_PLAIN) return false;
-  (void)d;
   return true;
 }
 
@@ -229,8 +237,9 @@ int jl_prefill_flags(const void* workspace, uint32_t* flags, void* stream) {
 
 // ---- prefill continued on an existing absolute cache
 static bool cached_shape_ok(int64_t q_off, int64_t Tq, int Hq, int Hkv) {
-  if (q_off < 0 || Tq < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv) return false;
-  return q_off + Tq <= (int64_t)INT32_MAX / 2;
+  if (q_off < 0 || Tq < 0 || !heads_ok(Hq, Hkv)) return false;
+  const int64_t lim = (int64_t)INT32_MAX / 2;
+  return q_off <= lim && Tq <= lim - q_off;
 }
 
 size_t jl_prefill_cached_workspace_size(int64_t q_off, int64_t Tq, int Hq, int Hkv, int d,
@@ -319,7 +328,8 @@ static int decode_max_splits(int64_t capacity) {
 }
 
 size_t jl_decode_workspace_size(int64_t capacity, int Hq, int d) {
-  if (capacity < 1 || Hq < 1 || d < 2) return 0;
+  if (capacity < 1 || capacity > (int64_t)INT32_MAX || Hq < 1 || Hq > kMaxHeads || !dim_ok(d))
+    return 0;
   return align256((size_t)Hq * decode_max_splits(capacity) * (d + 2) * sizeof(float));
 }
 
@@ -331,7 +341,7 @@ int jl_bifocal_decode_timed(const void* xq, const void* kcache, const void* vcac
   int cont;
   mode = strip_remap(mode, &cont);
   if (pos < 0 || capacity < 1 || pos >= capacity || capacity > (int64_t)INT32_MAX) return JL_EINVAL;
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 0 || w_pre < 1 || !(theta > 1.0)) return JL_EINVAL;
+  if (!heads_ok(Hq, Hkv) || w0 < 0 || w_pre < 1 || !(theta > 1.0)) return JL_EINVAL;
   if (num_splits < 0 || !(scale == scale)) return JL_EINVAL;
   if (dt != JL_BF16 && dt != JL_FP32) return JL_EINVAL;
   if (mode == JL_MODE_IE) return JL_EUNSUPPORTED;
@@ -394,7 +404,9 @@ static size_t decode_batch_list_offset(int B, int Hq, int S, int d) {
 }
 
 size_t jl_decode_batch_workspace_size(int B, int64_t max_keys, int Hq, int d) {
-  if (B < 1 || max_keys < 1 || max_keys > (int64_t)INT32_MAX || Hq < 1 || d < 2) return 0;
+  if (B < 1 || B > 65535 || max_keys < 1 || max_keys > (int64_t)INT32_MAX || Hq < 1 ||
+      Hq > kMaxHeads || !dim_ok(d))
+    return 0;
   return decode_batch_list_offset(B, Hq, decode_max_splits(max_keys), d) +
          align256((size_t)(B + 1) * sizeof(int));
 }
@@ -410,7 +422,7 @@ int jl_bifocal_decode_batch_timed(const void* xq, const void* kcache, const void
   mode = strip_remap(mode, &cont);
   if (B < 0 || B > 65535 || max_keys < 1 || max_keys > (int64_t)INT32_MAX || cache_rows < 1)
     return JL_EINVAL;
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 0 || w_pre < 1 || !(theta > 1.0)) return JL_EINVAL;
+  if (!heads_ok(Hq, Hkv) || w0 < 0 || w_pre < 1 || !(theta > 1.0)) return JL_EINVAL;
   if (num_splits < 0 || !(scale == scale)) return JL_EINVAL;
   if (dt != JL_BF16 && dt != JL_FP32) return JL_EINVAL;
   if (mode == JL_MODE_IE) return JL_EUNSUPPORTED;

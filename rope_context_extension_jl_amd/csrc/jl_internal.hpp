@@ -26,9 +26,10 @@ __host__ __device__ inline int tile_class(int64_t q0, int64_t q1, int64_t k0, in
   return c;
 }
 
-// Eq. 2 in integer arithmetic.
+// Eq. 2 in integer arithmetic: ceil(L / w_pre), at least 1, written so that
+// no intermediate overflows for any L, w_pre >= 1.
 __host__ __device__ inline int64_t group_size(int64_t L, int64_t w_pre) {
-  int64_t g = (L + w_pre - 1) / w_pre;
+  const int64_t g = L / w_pre + (L % w_pre != 0);
   return g < 1 ? 1 : g;
 }
 

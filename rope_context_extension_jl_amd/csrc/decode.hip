@@ -337,6 +337,21 @@ struct DecState {
   float m, lsum;       // reference (log2 domain) of query r16, partial row sum
 };
 
+// The step from an even chunk's correction cos / sin to the odd chunk's (the
+// keys 16 later): f(k + 16) - (k + 16) = f(k) - k + c16 with c16 =
+// floor(16 / G) - 16, plus one when (k mod G) + (16 mod G) >= G (floor map;
+// never when G divides 16), or exactly 16 / G - 16 (continuous map). c / s
+// hold R_{c16}, c1 / s1 R_{c16 + 1}, as fp16 pairs of neighbouring
+// frequencies in the key fragments' layout.
+template <int D>
+struct DecStep {
+  dh2v c[D / 64][4], s[D / 64][4];
+  dh2v c1[D / 64][4], s1[D / 64][4];
+  bool on;       // odd chunks derive their cos / sin from the even ones
+  bool carry;    // some keys step by c16 + 1
+  int G, r16m;   // G and 16 mod G
+};
+
 template <int D>
 __device__ __forceinline__ void dec_qk(const dh8v (&kf)[D / 32], const dh8v (&q)[D / 32],
                                        const df32x4& c, df32x4& out) {
@@ -465,9 +480,9 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0,
                                           const uint32_t (&va)[DecGeom<D>::NDB],
                                           const dh8v (&qa)[D / 32], const dh8v (&qr)[D / 32],
                                           const double (&w2)[D / 64][8], DecState<D>& st,
-                                          bool step16, const dh2v (&cst)[D / 64][4],
-                                          const dh2v (&sst)[D / 64][4], dh2v (&rc)[D / 64][4],
-                                          dh2v (&rs)[D / 64][4], float& chk) {
+                                          const DecStep<D>& stp, int kres,
+                                          dh2v (&rc)[D / 64][4], dh2v (&rs)[D / 64][4],
+                                          float& chk) {
   using G = DecGeom<D>;
   constexpr int NDS = G::NDS, NDB = G::NDB;
   constexpr int KOFF = ST * G::STAGE, VOFF = ST * G::STAGE + G::KBYTES;
@@ -482,16 +497,20 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0,
   // They depend on the key index only: computed while the chunk's transfers
   // may still be in flight.
   if (fix) {
-    if (ST == 1 && step16) {
-      // the even chunk k0 - 16 is farther from pos, hence remote too: its
-      // rotation moves by a fixed step, R_{d + c16} = R_d R_{c16}
+    if (ST == 1 && stp.on) {
+      // the even chunk k0 - 16 is farther from pos, hence remote too: the
+      // rotation moves by the step of the lane's key (kres: the even key's
+      // residue mod G), R_{d + c16} = R_d R_{c16}
+      const bool cy = stp.carry && kres + stp.r16m >= stp.G;
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const dh2v c0 = rc[ds][m], s0 = rs[ds][m];
-          rc[ds][m] = c0 * cst[ds][m] - s0 * sst[ds][m];
-          rs[ds][m] = s0 * cst[ds][m] + c0 * sst[ds][m];
+          const dh2v cs = cy ? stp.c1[ds][m] : stp.c[ds][m];
+          const dh2v sn = cy ? stp.s1[ds][m] : stp.s[ds][m];
+          rc[ds][m] = c0 * cs - s0 * sn;
+          rs[ds][m] = s0 * cs + c0 * sn;
         }
     } else {
       const double delta = c.cont ? (double)key * c.fk_rel : (double)(key / c.G - key);
@@ -607,8 +626,9 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0,
 
 // cos / sin tables a workgroup computes once for the rotations shared by all
 // of its lanes: [0][i] of pos * omega_i, [1][i] of f(pos) * omega_i (the
-// query at the absolute and the remapped position), [2][i] of c16 * omega_i
-// (the step between the two chunks of a 32-key pair). One angle per thread.
+// query at the absolute and the remapped position), [2][i] and [3][i] of
+// c16 * omega_i and (c16 + 1) * omega_i (the steps between the two chunks of
+// a 32-key pair, see DecStep). One angle per thread.
 template <int D>
 __device__ __forceinline__ void dec_tables(const DecArgs& a, const DecSeq& sq, bool step16,
                                            const double* w2pi_s, float2 (*tab)[D / 2]) {
@@ -623,17 +643,19 @@ __device__ __forceinline__ void dec_tables(const DecArgs& a, const DecSeq& sq, b
       tab[1][i] = make_float2(c, s);
     }
     if (step16) {
-      rope_cs_turns(a.cont ? 16.0 * sq.fk_rel : (double)(16 / sq.G - 16), w, c, s);
+      const double c16 = a.cont ? 16.0 * sq.fk_rel : (double)(16 / sq.G - 16);
+      rope_cs_turns(c16, w, c, s);
       tab[2][i] = make_float2(c, s);
+      rope_cs_turns(c16 + 1.0, w, c, s);
+      tab[3][i] = make_float2(c, s);
     }
   }
 }
 
 // Whether the odd chunk of a 32-key pair takes its cos / sin from the even
-// one by one rotation R_{c16}: with G dividing 16 (floor map) or the
-// continuous map, f(k) - k moves by the same c16 from key k to key k + 16.
+// one by one rotation (see DecStep): whenever keys are corrected.
 __device__ __forceinline__ bool dec_step16(const DecArgs& a, const DecSeq& sq) {
-  return !a.plain && sq.G > 1 && (a.cont || 16 % sq.G == 0);
+  return !a.plain && sq.G > 1;
 }
 
 // One work unit of the bf16 decode for one wave: keys [s kps, (s + 1) kps)
@@ -731,21 +753,31 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
     for (int j = 0; j < 8; ++j) w2[ds][j] = w2pi_s[32 * ds + 8 * g16 + j];
-  // R_{c16} between the two chunks of a pair (see dec_step16), as fp16
-  // pairs of neighbouring frequencies
-  const bool step16 = dec_step16(a, sq);
-  dh2v cst[NDS / 2][4], sst[NDS / 2][4];
-  if (step16) {
+  // the steps between the two chunks of a pair (see DecStep)
+  DecStep<D> stp;
+  stp.on = dec_step16(a, sq);
+  stp.carry = stp.on && !a.cont && 16 % sq.G != 0;
+  stp.G = sq.G;
+  stp.r16m = 16 % sq.G;
+  if (stp.on) {
 #pragma unroll
     for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const float2 t0 = tab[2][32 * ds + 8 * g16 + 2 * m];
-        const float2 t1 = tab[2][32 * ds + 8 * g16 + 2 * m + 1];
-        cst[ds][m] = dh2v{(_Float16)t0.x, (_Float16)t1.x};
-        sst[ds][m] = dh2v{(_Float16)t0.y, (_Float16)t1.y};
+        const int i = 32 * ds + 8 * g16 + 2 * m;
+        float2 t0 = tab[2][i], t1 = tab[2][i + 1];
+        stp.c[ds][m] = dh2v{(_Float16)t0.x, (_Float16)t1.x};
+        stp.s[ds][m] = dh2v{(_Float16)t0.y, (_Float16)t1.y};
+        t0 = tab[3][i];
+        t1 = tab[3][i + 1];
+        stp.c1[ds][m] = dh2v{(_Float16)t0.x, (_Float16)t1.x};
+        stp.s1[ds][m] = dh2v{(_Float16)t0.y, (_Float16)t1.y};
       }
   }
+  // residue mod G of the lane's key in the even chunk of the current pair;
+  // pairs advance by 32 keys
+  int kres = (k_lo + r16) % sq.G;
+  const int r32m = 32 % sq.G;
 
   DecState<D> st;
 #pragma unroll
@@ -763,12 +795,14 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   for (int k0 = k_lo;; k0 += 2 * DEC_CHUNK) {
     dec_issue<D>(c, k0 + DEC_CHUNK, stages + G::STAGE);
     __builtin_amdgcn_sched_barrier(0);  // the transfers go out first
-    dec_chunk<D, 0>(c, k0, ka, va, qa, qr, w2, st, step16, cst, sst, rc, rs, chk);
+    dec_chunk<D, 0>(c, k0, ka, va, qa, qr, w2, st, stp, kres, rc, rs, chk);
     if (k0 + DEC_CHUNK >= c.k_hi) break;
     dec_issue<D>(c, k0 + 2 * DEC_CHUNK, stages);
     __builtin_amdgcn_sched_barrier(0);
-    dec_chunk<D, 1>(c, k0 + DEC_CHUNK, ka, va, qa, qr, w2, st, step16, cst, sst, rc, rs, chk);
+    dec_chunk<D, 1>(c, k0 + DEC_CHUNK, ka, va, qa, qr, w2, st, stp, kres, rc, rs, chk);
     if (k0 + 2 * DEC_CHUNK >= c.k_hi) break;
+    kres += r32m;
+    if (kres >= sq.G) kres -= sq.G;
   }
   // no transfer into these LDS stages may outlive the unit
   __builtin_amdgcn_s_waitcnt(0);
@@ -807,7 +841,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   using G = DecGeom<D>;
   __shared__ __attribute__((aligned(16))) uint8_t stg[4][2 * G::STAGE];  // two stages per wave
   __shared__ double w2pi_s[D / 2];
-  __shared__ float2 tab_s[3][D / 2];
+  __shared__ float2 tab_s[4][D / 2];
   // the wave index is uniform per wave: say so, so that every split-derived
   // value (key range, route of a key block) lives in scalar registers and the
   // route branches are scalar jumps; matrix instructions then never run under
@@ -835,7 +869,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, co
   using G = DecGeom<D>;
   __shared__ __attribute__((aligned(16))) uint8_t stg[4][2 * G::STAGE];  // two stages per wave
   __shared__ double w2pi_s[D / 2];
-  __shared__ float2 tab_s[3][D / 2];
+  __shared__ float2 tab_s[4][D / 2];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
   __syncthreads();

@@ -65,6 +65,22 @@ def test_decode_batch_bf16(mode, remap):
     assert errs(to_host(lse), rl)[0] <= BF16_LSE_ABS
 
 
+def test_decode_batch_bf16_group_sizes_past_16():
+    """w_pretrained = 64: entries with G = 1 .. 47 in one launch (for G above 16
+    every 16-key step of f(k) - k is -16 or -15), most keys remote (w0 = 50)."""
+    w0, w_pre, theta, Hq, Hkv, d = 50, 64, 1e6, 8, 2, 128
+    positions = [30, 959, 1023, 1024, 1100, 2047, 2999, 600]
+    xq, k_rows, v_rows, starts, kc, vc, pos_t, st_t, tdt = _batch(8150, positions, Hq, Hkv, d,
+                                                                 theta, gaps=[2] * 8)
+    note(f"decode_batch bf16 G={[group_size(p + 1, w_pre) for p in positions]}")
+    o, lse = jl.bifocal_decode_batch(to_dev(xq), kc, vc, pos_t, st_t, max(positions) + 1, w0,
+                                     w_pre, theta)
+    torch.cuda.synchronize()
+    ro, rl = decode_batch(xq, k_rows, v_rows, positions, starts, w0, w_pre, theta)
+    assert_bf16_close(to_host(o), ro, "decode_batch G past 16")
+    assert errs(to_host(lse), rl)[0] <= BF16_LSE_ABS
+
+
 @pytest.mark.parametrize("Hq,Hkv,d", [(2, 2, 128), (4, 2, 128), (16, 2, 128), (8, 2, 64),
                                        (8, 8, 64), (12, 6, 128)])
 def test_decode_batch_heads_and_dims(Hq, Hkv, d):

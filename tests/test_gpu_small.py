@@ -321,6 +321,27 @@ def test_decode_small_positions(dtype):
     assert torch.equal(kc, k_before), "decode wrote the cache"
 
 
+@pytest.mark.parametrize("cont", [False, True])
+def test_decode_bf16_group_sizes_past_16(cont):
+    """G from 15 to 47 (w_pretrained = 64): for G above 16 every 16-key step of
+    f(k) - k is -16 or -15 (floor(16 / G) = 0, a carry whenever (k mod G) + 16
+    >= G), for G = 16 it is exactly -15, for G = 15 -15 or -14; most keys are
+    remote (w0 = 50). Split counts 1 and 7 change which chunk starts a split."""
+    w0, w_pre, theta = 50, 64, 1e6
+    xq, xk, v, kc, vc, tdt = _decode_setup("bf16")
+    for pos in (959, 1023, 1024, 1087, 1100, 2047, 2999):
+        G = group_size(pos + 1, w_pre)
+        for splits in (0, 1, 7):
+            note(f"decode bf16 pos={pos} G={G} splits={splits} continuous={cont}")
+            o, lse = jl.bifocal_decode(to_dev(xq[pos], tdt), kc, vc, pos, w0, w_pre, theta,
+                                       mode="fused", num_splits=splits,
+                                       remap="continuous" if cont else "floor")
+            torch.cuda.synchronize()
+            ro, rl = decode_row(xq[pos], xk, v, pos, w0, w_pre, theta, continuous=cont)
+            assert_bf16_close(to_host(o), ro, f"decode pos={pos} G={G} splits={splits}")
+            assert errs(to_host(lse), rl)[0] <= BF16_LSE_ABS
+
+
 @pytest.mark.parametrize("Hq,Hkv,d", [(2, 2, 128), (4, 2, 128), (16, 2, 128), (8, 2, 64),
                                        (8, 8, 64), (12, 6, 128)])
 def test_decode_bf16_head_ratios_and_dims(Hq, Hkv, d):

@@ -1184,8 +1184,17 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
       step_ie(n, j_nr + n, std::integral_constant<int, MASK_WINDOW>{});
     for (int n = n1; n < n1 + n2; ++n)
       step_ie(n, j_nr + (n - n1), std::integral_constant<int, MASK_REMOTE>{});
-    for (int n = n1 + n2; n < nwalk; ++n)
-      step_ie(n, n - n1 - n2, std::integral_constant<int, MASK_NONE>{});
+    // the all-remote tiles (no mask can apply: see the fused pass) take the
+    // hand-scheduled step, which performs the same operations per value
+    for (int n = n1 + n2; n < nwalk; ++n) {
+      const bool ahead = n + 2 < nwalk;
+      if (ahead) {
+        const int tn = tile_of(n + 2);
+        tile_dma8(c, tn, rem_of(tn), kst(n + 2), vst(n + 2));
+      }
+      tile_nomask(c, kst(n), vst(n), q, st);
+      pair_sync(ahead);
+    }
   } else {
     // plain causal RoPE attention (the baseline): the same mask-free step as
     // the fused pass on every tile below the diagonal

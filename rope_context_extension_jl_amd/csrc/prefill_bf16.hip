@@ -725,29 +725,37 @@ __device__ __forceinline__ void tile_nomask(const Tctx& c, const uint16_t* ks, c
 }
 
 // One key tile from stage (kc, vc) while the next one (if any) streams into
-// (kn, vn).
+// (kn, vn). NOMASK: a tile no mask can touch, on the hand-scheduled step
+// (the same operations per value as the generic one).
+template <bool NOMASK>
 __device__ __forceinline__ void tile_step(const Tctx& c, int j, int nxt, bool nrem, int mask_mode,
                                           const h8v (&q)[8], const uint16_t* kc,
                                           const uint16_t* vc, uint16_t* kn, uint16_t* vn,
                                           RowState& st) {
   if (nxt >= 0) tile_dma(c, nxt, nrem, kn, vn);
-  f32x16 s[2];
-  qk_lds(c, kc, q, st.negm, s);
-  softmax_pv_any(c, j, mask_mode, vc, s, st);
+  if constexpr (NOMASK) {
+    tile_nomask(c, kc, vc, q, st);
+  } else {
+    f32x16 s[2];
+    qk_lds(c, kc, q, st.negm, s);
+    softmax_pv_any(c, j, mask_mode, vc, s, st);
+  }
   tile_sync();
 }
 // Double-buffered walk over key tiles [j0, j1) whose LDS key tiles hold the
 // rotation `rem_src` (remote tiles: remapped keys). `next_after` is the tile
 // to prefetch after the last one (-1: none) and `next_rem` its rotation, so
 // segments chain in any order. `stg` is the LDS stage holding tile j0.
+// NOMASK: every tile of the segment is mask-free (see tile_step).
+template <bool NOMASK = false>
 __device__ __forceinline__ void walk(const Tctx& c, int j0, int j1, bool rem_src, int next_after,
                                      bool next_rem, int mask_mode, const h8v (&q)[8],
                                      const Stages& S, int& stg, RowState& st) {
   for (int j = j0; j < j1; ++j) {
     const int nxt = j + 1 < j1 ? j + 1 : next_after;
     const bool nrem = j + 1 < j1 ? rem_src : next_rem;
-    tile_step(c, j, nxt, nrem, mask_mode, q, stg ? S.k1 : S.k0, stg ? S.v1 : S.v0,
-              stg ? S.k0 : S.k1, stg ? S.v0 : S.v1, st);
+    tile_step<NOMASK>(c, j, nxt, nrem, mask_mode, q, stg ? S.k1 : S.k0, stg ? S.v1 : S.v0,
+                      stg ? S.k0 : S.k1, stg ? S.v0 : S.v1, st);
     stg ^= 1;
   }
 }
@@ -898,8 +906,9 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     {
       h8v qr[8];
       rotq(remap_pos(c.myq, sq.G, a.cont), qr);
-      // remote phase: remapped query against remapped key tiles
-      walk(c, 0, j_nr, true, j_nr < c.nkt ? j_nr : -1, false, MASK_NONE, qr, S, stg, st);
+      // remote phase: remapped query against remapped key tiles (no mask
+      // can apply: every key is more than w0 below every row)
+      walk<true>(c, 0, j_nr, true, j_nr < c.nkt ? j_nr : -1, false, MASK_NONE, qr, S, stg, st);
       if (j_nr < j_loc) {  // boundary phase: both routes, element-wise select
         h8v qa[8];
         rotq(c.myq, qa);
@@ -908,12 +917,18 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     }
     h8v qa[8];
     rotq(c.myq, qa);
-    // local phase: absolute query against absolute key tiles
-    walk(c, jl0, c.nkt, false, -1, false, MASK_NONE, qa, S, stg, st);
+    // local phase: absolute query against absolute key tiles; the tiles
+    // wholly below the causal diagonal (every key <= q0 <= every row, inside
+    // the sequence) need no mask
+    const int jf = max(jl0, min(c.nkt, (c.q0 + 1) / PF_BN));
+    walk<true>(c, jl0, jf, false, jf < c.nkt ? jf : -1, false, MASK_NONE, qa, S, stg, st);
+    walk(c, jf, c.nkt, false, -1, false, MASK_NONE, qa, S, stg, st);
   } else if (PASS == PASS_PLAIN) {
     h8v qa[8];
     rotq(c.myq, qa);
-    walk(c, 0, c.nkt, false, -1, false, MASK_NONE, qa, S, stg, st);
+    const int jf = min(c.nkt, (c.q0 + 1) / PF_BN);
+    walk<true>(c, 0, jf, false, jf < c.nkt ? jf : -1, false, MASK_NONE, qa, S, stg, st);
+    walk(c, jf, c.nkt, false, -1, false, MASK_NONE, qa, S, stg, st);
   } else if (PASS == PASS_IE_A) {
     h8v qa[8];
     rotq(c.myq, qa);
@@ -930,7 +945,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PfArgs a) {
     walk(c, j_nr, c.nkt, true, a.ie_remote ? seg2 : -1, true, MASK_WINDOW, qr, S, stg, st);
     if (a.ie_remote) {
       walk(c, j_nr, j_loc, true, j_nr > 0 ? 0 : -1, true, MASK_REMOTE, qr, S, stg, st);
-      walk(c, 0, j_nr, true, -1, true, MASK_NONE, qr, S, stg, st);
+      walk<true>(c, 0, j_nr, true, -1, true, MASK_NONE, qr, S, stg, st);
     }
   }
 

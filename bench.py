@@ -395,31 +395,35 @@ def main():
             for pos in cdec["decode_positions"]:
                 qd = q[pos].contiguous()
                 row = {}
-                for mode in ("fused", "plain", "continuous"):
-                    for evict in (("read",) if mode == "continuous" else ("read", "write")):
-                        ts = []
-                        for it in range(args.decode_iters + 3):
-                            if evict == "read":
-                                flush.sum()
-                            else:
-                                flush.zero_()
-                            jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta,
-                                              mode="fused" if mode == "continuous" else mode,
-                                              remap="continuous" if mode == "continuous" else "floor",
-                                              out=od, lse=ld, workspace=wsd, events=de)
-                            torch.cuda.synchronize()
-                            if it >= 3:
-                                ts.append(de[0].elapsed_time(de[1]) * 1e3)  # us
-                        nbytes = 4.0 * (pos + 1) * Hkv * d
-                        med = float(np.median(ts))
-                        key = mode if evict == "read" else mode + "_after_zero_fill"
-                        row[key] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
-                                    "us_p90": round(pct(ts, 90), 2),
-                                    "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
-                                    "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 /
-                                                          PEAK_HBM_GBS, 2),
-                                    "pct_calibrated_read": round(100 * nbytes / (med * 1e-6) / 1e9 /
-                                                                 read_gbs, 2)}
+                # the five (mode, cache state) variants take turns step by step,
+                # so a drift of the clock during the run affects them alike
+                variants = [(m, e) for m in ("fused", "plain", "continuous")
+                            for e in (("read",) if m == "continuous" else ("read", "write"))]
+                times = {v: [] for v in variants}
+                for it in range(args.decode_iters + 3):
+                    for mode, evict in variants:
+                        if evict == "read":
+                            flush.sum()
+                        else:
+                            flush.zero_()
+                        jl.bifocal_decode(qd, kcache, vv, pos, w0, w_pre, theta,
+                                          mode="fused" if mode == "continuous" else mode,
+                                          remap="continuous" if mode == "continuous" else "floor",
+                                          out=od, lse=ld, workspace=wsd, events=de)
+                        torch.cuda.synchronize()
+                        if it >= 3:
+                            times[(mode, evict)].append(de[0].elapsed_time(de[1]) * 1e3)  # us
+                for (mode, evict), ts in times.items():
+                    nbytes = 4.0 * (pos + 1) * Hkv * d
+                    med = float(np.median(ts))
+                    key = mode if evict == "read" else mode + "_after_zero_fill"
+                    row[key] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
+                                "us_p90": round(pct(ts, 90), 2),
+                                "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                "pct_hbm_peak": round(100 * nbytes / (med * 1e-6) / 1e9 /
+                                                      PEAK_HBM_GBS, 2),
+                                "pct_calibrated_read": round(100 * nbytes / (med * 1e-6) / 1e9 /
+                                                             read_gbs, 2)}
                 row["G"] = jl.group_size(pos + 1, w_pre)
                 row["overhead_ratio"] = round(row["fused"]["us_median"] / row["plain"]["us_median"],
                                               4)
@@ -454,16 +458,17 @@ def main():
             lb = torch.empty((len(bpos), Hq), dtype=torch.float32, device=dev)
             bbytes = sum(4.0 * (p + 1) * Hkv * d for p in bpos)
             brow = {"B": len(bpos), "keys": int(sum(p + 1 for p in bpos)), "max_keys": mk}
-            for mode in ("fused", "plain"):
-                ts = []
-                for it in range(args.decode_iters + 3):
+            btimes = {"fused": [], "plain": []}
+            for it in range(args.decode_iters + 3):  # the two modes take turns
+                for mode in ("fused", "plain"):
                     flush.sum()
                     jl.bifocal_decode_batch(xb, kb, vb, pos_t, st_t, mk, cb["w0"], cb["w_pre"],
                                             cb["theta"], mode=mode, out=ob, lse=lb, workspace=wsb,
                                             events=de)
                     torch.cuda.synchronize()
                     if it >= 3:
-                        ts.append(de[0].elapsed_time(de[1]) * 1e3)
+                        btimes[mode].append(de[0].elapsed_time(de[1]) * 1e3)
+            for mode, ts in btimes.items():
                 med = float(np.median(ts))
                 brow[mode] = {"us_median": round(med, 2), "us_p10": round(pct(ts, 10), 2),
                               "us_p90": round(pct(ts, 90), 2),

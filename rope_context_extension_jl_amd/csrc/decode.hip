@@ -294,6 +294,9 @@ typedef float df32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t du32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int DEC_CHUNK = 16;  // keys per chunk: one 16-key MFMA block
+// chunks per exact (float64) anchor of the correction cos / sin; the others
+// take them from the chunk before by one packed fp16 rotation
+constexpr int DEC_ANCHOR_CHUNKS = 4;
 constexpr float kDecSumMax = 256.f;
 
 template <int D>
@@ -324,7 +327,7 @@ struct DecCtx {
   const uint16_t* kbase;  // the head's K row 0
   const uint16_t* vbase;  // the head's V row 0
   int64_t rstride;        // elements between consecutive keys
-  int pos, w0, G, plain, correct, k_hi;
+  int pos, w0, G, plain, correct, k_lo, k_hi;
   int cont;       // remote map x / G (real) instead of floor(x / G)
   double fk_rel;  // with cont: f(k) - k = k * fk_rel
   int lane, g16, r16;
@@ -497,10 +500,10 @@ __device__ __forceinline__ void dec_chunk(const DecCtx& c, int k0,
   // They depend on the key index only: computed while the chunk's transfers
   // may still be in flight.
   if (fix) {
-    if (ST == 1 && stp.on) {
-      // the even chunk k0 - 16 is farther from pos, hence remote too: the
-      // rotation moves by the step of the lane's key (kres: the even key's
-      // residue mod G), R_{d + c16} = R_d R_{c16}
+    if (stp.on && ((k0 - c.k_lo) & (DEC_CHUNK * DEC_ANCHOR_CHUNKS - 1)) != 0) {
+      // the chunk k0 - 16 is farther from pos, hence remote too: the
+      // rotation moves by the step of the lane's key (kres: the previous
+      // key's residue mod G), R_{d + c16} = R_d R_{c16}
       const bool cy = stp.carry && kres + stp.r16m >= stp.G;
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds)
@@ -676,6 +679,7 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
 
   const int k_lo = s * a.kps;
   DecCtx c;
+  c.k_lo = k_lo;
   c.k_hi = min(k_lo + a.kps, sq.pos + 1);
   c.rstride = (int64_t)a.Hkv * D;
   c.kbase = kc + (int64_t)kvh * D;
@@ -776,8 +780,9 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   }
   // residue mod G of the lane's key in the even chunk of the current pair;
   // pairs advance by 32 keys
-  int kres = (k_lo + r16) % sq.G;
-  const int r32m = 32 % sq.G;
+  // residue mod G of the lane's key in the chunk before the one computed
+  int kres = ((k_lo + r16) % sq.G + sq.G - stp.r16m) % sq.G;
+  auto advance = [&]() { kres = kres + stp.r16m >= sq.G ? kres + stp.r16m - sq.G : kres + stp.r16m; };
 
   DecState<D> st;
 #pragma unroll
@@ -796,13 +801,13 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
     dec_issue<D>(c, k0 + DEC_CHUNK, stages + G::STAGE);
     __builtin_amdgcn_sched_barrier(0);  // the transfers go out first
     dec_chunk<D, 0>(c, k0, ka, va, qa, qr, w2, st, stp, kres, rc, rs, chk);
+    advance();
     if (k0 + DEC_CHUNK >= c.k_hi) break;
     dec_issue<D>(c, k0 + 2 * DEC_CHUNK, stages);
     __builtin_amdgcn_sched_barrier(0);
     dec_chunk<D, 1>(c, k0 + DEC_CHUNK, ka, va, qa, qr, w2, st, stp, kres, rc, rs, chk);
+    advance();
     if (k0 + 2 * DEC_CHUNK >= c.k_hi) break;
-    kres += r32m;
-    if (kres >= sq.G) kres -= sq.G;
   }
   // no transfer into these LDS stages may outlive the unit
   __builtin_amdgcn_s_waitcnt(0);

@@ -661,29 +661,26 @@ __device__ __forceinline__ bool dec_step16(const DecArgs& a, const DecSeq& sq) {
   return !a.plain && sq.G > 1;
 }
 
-// One work unit of the bf16 decode for one wave: keys [s kps, (s + 1) kps)
-// of KV head kvh of sequence sq, leaving the partial of each query head of
-// the group. stages: this wave's two LDS stages (2 * STAGE bytes).
-template <int D>
-__device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int s, int kvh,
-                                         const double* w2pi_s, const float2 (*tab)[D / 2],
-                                         uint8_t* stages) {
-  using G = DecGeom<D>;
-  constexpr int NDS = G::NDS, NDB = G::NDB;
-  const int lane = threadIdx.x & 63;
-  const int g16 = lane >> 4, r16 = lane & 15;
-  const int R = a.Hq / a.Hkv, h0 = kvh * R;
-  const uint16_t* xq = (const uint16_t*)sq.xq;
-  const uint16_t* kc = (const uint16_t*)sq.kc;
-  const uint16_t* vc = (const uint16_t*)sq.vc;
+// Workgroup barrier for the LDS tables: every ds_read / ds_write issued
+// before it has completed, and the compiler moves no memory access across
+// it. Global loads and the transfers into the waves' private stages stay in
+// flight (__syncthreads, and any LDS fence, would wait for all of them: a
+// transfer's LDS write is counted with the vector memory operations).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-  const int k_lo = s * a.kps;
+// Per-wave constants of one work unit: keys [s kps, (s + 1) kps) of KV head
+// kvh of sequence sq.
+template <int D>
+__device__ __forceinline__ DecCtx dec_ctx(const DecArgs& a, const DecSeq& sq, int s, int kvh) {
+  const int lane = threadIdx.x & 63;
   DecCtx c;
-  c.k_lo = k_lo;
-  c.k_hi = min(k_lo + a.kps, sq.pos + 1);
+  c.k_lo = s * a.kps;
+  c.k_hi = min(c.k_lo + a.kps, sq.pos + 1);
   c.rstride = (int64_t)a.Hkv * D;
-  c.kbase = kc + (int64_t)kvh * D;
-  c.vbase = vc + (int64_t)kvh * D;
+  c.kbase = (const uint16_t*)sq.kc + (int64_t)kvh * D;
+  c.vbase = (const uint16_t*)sq.vc + (int64_t)kvh * D;
   c.pos = sq.pos;
   c.w0 = a.w0;
   c.G = sq.G;
@@ -692,11 +689,51 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   c.plain = a.plain;
   c.correct = !a.plain && sq.G > 1;
   c.lane = lane;
-  c.g16 = g16;
-  c.r16 = r16;
+  c.g16 = lane >> 4;
+  c.r16 = lane & 15;
+  return c;
+}
 
-  // the first chunk is in flight while the query operands are computed
-  dec_issue<D>(c, k_lo, stages);
+// The lane's raw query elements: dims 32 ds + 8 g16 .. + 8 (lo) and their
+// partners + D/2 (hi) of query head r16 of the group, as 16-byte loads of a
+// valid row (head r16 clamped; the rotation zeroes heads past the group).
+template <int D>
+struct DecQRaw {
+  du32x4 lo[D / 64], hi[D / 64];
+};
+
+// Start of a work unit, before the rotation tables exist: the raw query
+// loads and the transfers of the first chunk (stage 0) go out, so the first
+// round trip to memory overlaps the table set-up.
+template <int D>
+__device__ __forceinline__ void dec_begin(const DecArgs& a, const DecSeq& sq, int kvh,
+                                          const DecCtx& c, DecQRaw<D>& raw, uint8_t* stages) {
+  const int R = a.Hq / a.Hkv;
+  const uint16_t* qp = (const uint16_t*)sq.xq + (int64_t)(kvh * R + (c.r16 < R ? c.r16 : 0)) * D;
+#pragma unroll
+  for (int ds = 0; ds < D / 64; ++ds) {
+    raw.lo[ds] = *(const du32x4*)(qp + 32 * ds + 8 * c.g16);
+    raw.hi[ds] = *(const du32x4*)(qp + 32 * ds + 8 * c.g16 + D / 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  dec_issue<D>(c, c.k_lo, stages);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One work unit of the bf16 decode for one wave, after dec_begin: keys
+// [c.k_lo, c.k_hi) of KV head kvh of sequence sq, leaving the partial of each
+// query head of the group. stages: this wave's two LDS stages (2 * STAGE
+// bytes), the first holding (in flight) the unit's first chunk.
+template <int D>
+__device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int s, int kvh,
+                                         const DecCtx& c, const DecQRaw<D>& raw,
+                                         const double* w2pi_s, const float2 (*tab)[D / 2],
+                                         uint8_t* stages) {
+  using G = DecGeom<D>;
+  constexpr int NDS = G::NDS, NDB = G::NDB;
+  const int g16 = c.g16, r16 = c.r16;
+  const int R = a.Hq / a.Hkv, h0 = kvh * R;
+  const int k_lo = c.k_lo;
 
   // LDS addresses of the lane's reads, relative to a stage's K or V part
   // (the stage and part offsets are immediates of the reads): K row r16,
@@ -721,23 +758,14 @@ __device__ __forceinline__ void dec_unit(const DecArgs& a, const DecSeq& sq, int
   // query head r16, rotated at pos (qa) and at f(pos) (qr), times scale*log2 e
   dh8v qa[NDS], qr[NDS];
   {
-    // the lane's dims 32 ds + 8 g16 .. + 8 and their partners + D/2, as
-    // 16-byte loads of a valid row (head r16 clamped), zeroed past R heads
     const bool qv = r16 < R;
-    const uint16_t* qp = xq + (int64_t)(h0 + (qv ? r16 : 0)) * D;
-    du32x4 raw0[NDS / 2], raw1[NDS / 2];
-#pragma unroll
-    for (int ds = 0; ds < NDS / 2; ++ds) {
-      raw0[ds] = *(const du32x4*)(qp + 32 * ds + 8 * g16);
-      raw1[ds] = *(const du32x4*)(qp + 32 * ds + 8 * g16 + D / 2);
-    }
 #pragma unroll
     for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 32 * ds + 8 * g16 + j;
-        const float x0 = qv ? bf16_lane(raw0[ds], j) : 0.f;
-        const float x1 = qv ? bf16_lane(raw1[ds], j) : 0.f;
+        const float x0 = qv ? bf16_lane(raw.lo[ds], j) : 0.f;
+        const float x1 = qv ? bf16_lane(raw.hi[ds], j) : 0.f;
         const float2 ta = tab[0][i];
         qa[ds][j] = (_Float16)((x0 * ta.x - x1 * ta.y) * a.scale_log2);
         qa[ds + NDS / 2][j] = (_Float16)((x0 * ta.y + x1 * ta.x) * a.scale_log2);
@@ -853,14 +881,24 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecArgs a) {
   // a partial or empty EXEC mask
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const DecSeq sq = dec_seq<false>(a, 0, D, 2);
-  if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
-  __syncthreads();
-  dec_tables<D>(a, sq, dec_step16(a, sq), w2pi_s, tab_s);
-  __syncthreads();
   const int hgroups = (a.Hkv + 3) >> 2;
   const int s = blockIdx.x / hgroups, kvh = (blockIdx.x % hgroups) * 4 + wave;
-  if (kvh >= a.Hkv) return;
-  dec_unit<D>(a, sq, s, kvh, w2pi_s, tab_s, stg[wave]);
+  // a wave past the last KV head starts the last head's unit too (in-bounds
+  // reads, no branch around the transfers) and drops it after the tables
+  const bool live = kvh < a.Hkv;
+  const int kvu = live ? kvh : a.Hkv - 1;
+  const DecCtx c = dec_ctx<D>(a, sq, s, kvu);
+  DecQRaw<D> raw;
+  dec_begin<D>(a, sq, kvu, c, raw, stg[wave]);
+  if (tid < D / 2) w2pi_s[tid] = a.fr.w(tid) * kInvTwoPi;
+  lds_barrier();
+  dec_tables<D>(a, sq, dec_step16(a, sq), w2pi_s, tab_s);
+  lds_barrier();
+  if (!live) {
+    __builtin_amdgcn_s_waitcnt(0);  // no transfer outlives the wave
+    return;
+  }
+  dec_unit<D>(a, sq, s, kvh, c, raw, w2pi_s, tab_s, stg[wave]);
 }
 
 // Batch: a fixed grid of workgroups walks the work list the plan kernel
@@ -888,13 +926,24 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_batch_kernel(DecArgs a, co
       if (base[mid] <= item) lo = mid; else hi = mid - 1;
     }
     const DecSeq sq = dec_seq<true>(a, lo, D, 2);
+    // this wave's stages are free: its previous unit waited for them; a wave
+    // past the last KV head starts the last head's unit and drops it
+    const bool live = kvh < a.Hkv;
+    const int kvu = live ? kvh : a.Hkv - 1;
+    const int s = item - base[lo];
+    const DecCtx c = dec_ctx<D>(a, sq, s, kvu);
+    DecQRaw<D> raw;
+    dec_begin<D>(a, sq, kvu, c, raw, stg[wave]);
     // this unit's tables (every wave passes both barriers, also the waves
     // past the last KV head)
-    __syncthreads();
+    lds_barrier();
     dec_tables<D>(a, sq, dec_step16(a, sq), w2pi_s, tab_s);
-    __syncthreads();
-    if (kvh >= a.Hkv) continue;
-    dec_unit<D>(a, sq, item - base[lo], kvh, w2pi_s, tab_s, stg[wave]);
+    lds_barrier();
+    if (!live) {
+      __builtin_amdgcn_s_waitcnt(0);  // the stages are free for the next unit
+      continue;
+    }
+    dec_unit<D>(a, sq, s, kvh, c, raw, w2pi_s, tab_s, stg[wave]);
   }
 }
 

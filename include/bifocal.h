@@ -162,7 +162,9 @@ int jl_prefill_flags(const void* workspace, uint32_t* flags, void* stream);
  * keys below 65504 / (scale log2 e) (about 5.1e5 at d = 128); beyond that the
  * scores overflow, the outputs of the affected rows are undefined (NaN or
  * wrong) and the call sets JL_FLAG_Q_RANGE / JL_FLAG_K_RANGE in the workspace
- * (jl_prefill_flags); the status returned is still JL_OK.
+ * (jl_prefill_flags); the status returned is still JL_OK. Values: the fp32
+ * softmax sums stay finite while max |v| * 2^65 * (key tiles of 64) < 2^128,
+ * i.e. |v| < 2^50 at 128K keys.
  * Workspace: jl_prefill_workspace_size(...) bytes of device memory, any
  * contents, 256-byte aligned; it holds the rotated key tiles, the transposed
  * values and the tile schedule. Errors: JL_EINVAL, JL_EUNSUPPORTED,

@@ -477,14 +477,22 @@ __device__ __forceinline__ void boundary_select(const Tctx& c, int j, const h8v 
 // Masks, online softmax and O^T += V^T P^T for one tile whose shifted
 // scores s' = c (q . k) - m are in s. The reference m does not follow every new
 // row maximum: it moves only when the tile's probabilities p = exp2(s') summed
-// over a lane's 32 keys exceed 2^8 (or the row has no reference yet), so
-// every p stays below 2^8 and the sum check replaces the per-tile row max.
+// over a lane's 32 keys exceed 2^64 (or the row has no reference yet), so
+// every p stays below 2^64 and the sum check replaces the per-tile row max.
 // Since the final division uses the same reference, the result does not
-// depend on where the reference sits; the rescale of the 64 accumulator
+// depend on where the reference sits (p is rounded to bf16 with the same
+// relative error at any magnitude); the rescale of the 64 accumulator
 // registers, the row max and the cross-lane exchange are skipped on almost
 // every tile. The tile sum is taken over the bf16-rounded p, the same values
 // the PV product weights, so numerator and denominator see identical p.
-constexpr float kSumMax = 256.f;
+// Bound: a row's l and |acc| stay below 2^65 per key tile times max |v| (at
+// 2048 key tiles, finite for |v| < 2^50). A small bound moves the reference
+// whenever some row's maximum grows by its log2; rows scored against a few
+// large keys then move it tens of times per walk (2^8: 53-58 moves per wave
+// over a 2048-tile walk at 128K, 2^64: the first tile only, simulated), each
+// on the rarely taken branch that every other wave waits for at the tile
+// barrier.
+constexpr float kSumMax = 0x1p64f;
 
 // Causal / window masks on the raw scores of a tile that needs them.
 __device__ __forceinline__ void mask_scores(const Tctx& c, int j, int cls, int mask_mode,

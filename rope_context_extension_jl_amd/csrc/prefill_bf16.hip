@@ -732,6 +732,154 @@ __device__ __forceinline__ void tile_nomask(const Tctx& c, const uint16_t* ks, c
   __builtin_amdgcn_s_setprio(0);
 }
 
+// The same mask-free tile with one reference check per 32-key block: block
+// 0's half of the PV product is issued right after its check, under block
+// 1's exponentials. Equal to tile_nomask whenever the reference does not
+// move in the tile; when it moves at block 1, block 0's products already in
+// the accumulator are rescaled with it (the online-softmax update), equal up
+// to rounding. The plain pass takes this step: compiled into that kernel it
+// ran faster than tile_nomask (121.5 -> 119.3 ms at 128K, A/B), compiled into
+// the fused kernel slower (120.3 -> 121.2 ms), with the same instructions per
+// tile in both kernels.
+__device__ __forceinline__ void tile_nomask_split(const Tctx& c, const uint16_t* ks,
+                                                  const uint16_t* vs, const h8v (&q)[8],
+                                                  RowState& st) {
+  const int x = kswz(c.l32), y = vswz(c.l32);
+  const uint16_t* kr0 = ks + c.l32 * PF_D;
+  const uint16_t* kr1 = ks + (32 + c.l32) * PF_D;
+  auto vop = [&](int db, int kk) __attribute__((always_inline)) -> b8v {
+    return *(const b8v*)(vs + (32 * db + c.l32) * PF_BN + 8 * ((2 * kk + c.hh) ^ y));
+  };
+  h8v ka[8], kb[8];
+  f32x16 s[2];
+  __builtin_amdgcn_s_setprio(1);
+  // ---- block 0
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) ka[cc] = *(const h8v*)(kr0 + 8 * ((2 * cc + c.hh) ^ x));
+  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], q[0], st.negm, 0, 0, 0);
+#pragma unroll
+  for (int cc = 1; cc < 8; ++cc)
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[cc], q[cc], s[0], 0, 0, 0);
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) kb[cc] = *(const h8v*)(kr1 + 8 * ((2 * cc + c.hh) ^ x));
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // block 0's reads
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an MFMA of block 0
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a read for block 1
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- block 1's scores under block 0's exponentials; first value operands
+  const b2v one = {(__bf16)1.f, (__bf16)1.f};
+  b8v pb[4];
+  // p = exp2(s') of block bk into pb[2 bk], pb[2 bk + 1]; returns its sum
+  auto expb = [&](int bk) __attribute__((always_inline)) -> float {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      pb[2 * bk + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(s[bk][r]);
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int ks2 = 2 * bk; ks2 < 2 * bk + 2; ++ks2) {
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks2], pb[ks2], 0, 1), one,
+                                            ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks2], pb[ks2], 2, 3), one,
+                                            ps1, false);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks2], pb[ks2], 4, 5), one,
+                                            ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks2], pb[ks2], 6, 7), one,
+                                            ps1, false);
+    }
+    return ps0 + ps1;
+  };
+  // rare: move the reference of the rows that need it to the maximum of
+  // block bk's shifted scores, rescale acc and l (O^T so far, this tile's
+  // block 0 included when bk = 1), shift the scores not yet exponentiated
+  // and redo block bk's exponentials
+  auto reference = [&](int bk, bool need, float psum) __attribute__((always_inline)) -> float {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[bk][r]);
+    mt = max_with_partner(mt);
+    const bool grow = max_with_partner(need ? 1.f : 0.f) > 0.f && mt > -INFINITY;
+    const float delta = grow ? mt : 0.f;
+    const float alpha = grow ? (st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-mt)) : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[i][r] *= alpha;
+    if (grow) st.m = (st.m == -INFINITY ? 0.f : st.m) + mt;
+    const float nm = st.m == -INFINITY ? 0.f : -st.m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.negm[r] = nm;
+#pragma unroll
+    for (int b = bk; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[b][r] -= delta;
+    return grow ? expb(bk) : psum;
+  };
+  b8v vc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vc[db] = vop(db, 0);
+  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kb[0], q[0], st.negm, 0, 0, 0);
+#pragma unroll
+  for (int cc = 1; cc < 8; ++cc)
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kb[cc], q[cc], s[1], 0, 0, 0);
+  float ps_a = expb(0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // value operands of k-step 0
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const bool need = !(ps_a <= kSumMax) || st.m == -INFINITY;
+    if (__any(need)) ps_a = reference(0, need, ps_a);
+  }
+  st.l += ps_a;
+  // ---- block 0's half of O^T += V^T P^T under block 1's exponentials
+  b8v vn[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vn[db] = vop(db, 1);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[db], pb[0], st.acc[db], 0, 0, 0);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vc[db] = vop(db, 2);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vn[db], pb[1], st.acc[db], 0, 0, 0);
+  float ps_b = expb(1);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // value operands of k-step 1
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // value operands of k-step 2
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const bool need = !(ps_b <= kSumMax) || st.m == -INFINITY;
+    if (__any(need)) ps_b = reference(1, need, ps_b);
+  }
+  st.l += ps_b;
+  // ---- block 1's half
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vn[db] = vop(db, 3);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[db], pb[2], st.acc[db], 0, 0, 0);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vn[db], pb[3], st.acc[db], 0, 0, 0);
+  __builtin_amdgcn_s_setprio(0);
+}
+
 // One key tile from stage (kc, vc) while the next one (if any) streams into
 // (kn, vn). NOMASK: a tile no mask can touch, on the hand-scheduled step
 // (the same operations per value as the generic one).
@@ -1219,11 +1367,17 @@ __global__ void __launch_bounds__(512, 1) prefill_pair_kernel(PfArgs a) {
       pair_sync(ahead);
     }
   } else {
-    // plain causal RoPE attention (the baseline): the same mask-free step as
-    // the fused pass on every tile below the diagonal
+    // plain causal RoPE attention (the baseline): a mask-free step on every
+    // tile below the diagonal (the per-block-check one, the faster of the
+    // two in this kernel)
     h8v qa[8];
     rotq(c.myq, qa);
-    for (int j = 0; j < j_free; ++j) step_nomask(j, qa);
+    for (int j = 0; j < j_free; ++j) {
+      const bool ahead = j + 2 < nkt;
+      if (ahead) tile_dma8(c, j + 2, false, kst(j + 2), vst(j + 2));
+      tile_nomask_split(c, kst(j), vst(j), qa, st);
+      pair_sync(ahead);
+    }
     for (int j = j_free; j < nkt; ++j) step(j, qa, nullptr);
   }
 

@@ -148,6 +148,49 @@ def test_prefill_bf16_small(case, mode):
     assert mx <= BF16_LSE_ABS, ("LSE", mx)
 
 
+def _reference_move_inputs(L, Hq, Hkv, d, seed):
+    """Inputs whose softmax reference must move inside the walk, not only on
+    its first tile: queries are close to one vector u placed on the lowest
+    frequency pairs (RoPE turns them by < 0.01 rad over L, at absolute and at
+    remapped positions alike), keys 0..63 lie along -u (scores about -64 in
+    the log2 domain, the first reference), keys 64..95 score about 57.4 above
+    it and keys 96..127 about 65 above it (a lane's 16-key block sum then
+    stays below the 2^64 bound in the first block and exceeds it in the
+    second), later keys are N(0, 1). After the move at keys 96..127 the keys
+    64..95 keep about 0.5% of the weight, so a wrong rescale of the products
+    already accumulated shows in every row past them."""
+    rng = np.random.default_rng(seed)
+    u = np.zeros(d, np.float32)
+    u[d // 2 - 4:d // 2] = 5.0  # |u| = 10, on the four lowest-frequency pairs
+    uh = u / 10.0
+    xq = (u[None, None, :] + 0.05 * rng.standard_normal((L, Hq, d))).astype(np.float32)
+    xk = rng.standard_normal((L, Hkv, d)).astype(np.float32)
+    b = np.zeros(L, np.float32)
+    b[:64], b[64:96], b[96:128] = -5.0, -0.5, 0.1
+    xk[:128] = b[:128, None, None] * 10.0 * uh[None, None, :] + 0.01 * xk[:128]
+    v = rng.standard_normal((L, Hkv, d)).astype(np.float32)
+    q16 = lambda a: torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+    return q16(xq), q16(xk), q16(v)
+
+
+@pytest.mark.parametrize("heads", [(8, 2), (6, 2)], ids=["pair", "one-head"])
+@pytest.mark.parametrize("mode", ["fused", "plain"])
+def test_prefill_bf16_reference_moves_inside_the_walk(heads, mode):
+    """The lazy softmax reference moves on a mask-free tile after the first
+    one (rare branch of both mask-free steps, including a move at the second
+    32-key block after the first block's products): parity with the oracle."""
+    Hq, Hkv = heads
+    L, w0, w_pre, theta = 1024, 16, 256, 1e6
+    xq, xk, v = _reference_move_inputs(L, Hq, Hkv, 128, 4242)
+    note(f"prefill bf16 reference moves L={L} Hq={Hq} Hkv={Hkv} mode={mode}")
+    o, lse = jl.bifocal_prefill(to_dev(xq), to_dev(xk), to_dev(v), w0, w_pre, theta, mode=mode)
+    torch.cuda.synchronize()
+    O, LSE = _oracle(xq, xk, v, BIG if mode == "plain" else w0, w_pre, theta)
+    assert_bf16_close(to_host(o), O, f"reference moves {heads} {mode} O")
+    mx, _ = errs(to_host(lse), LSE)
+    assert mx <= BF16_LSE_ABS, ("LSE", mx)
+
+
 # Eq. 7 subtracts pass C from pass B. On a row where the window's remapped
 # mass (W_C) dwarfs the final mass (W_A + W_B - W_C), the passes' fp32
 # rounding is amplified by ratio = (W_B + W_C) / (W_A + W_B - W_C). Rows up

@@ -65,7 +65,13 @@ typedef enum JL_ENUM_BASE { JL_BF16 = 0, JL_FP32 = 1 } jl_dtype;
 /* FUSED: one pass, each (query tile, key tile) classified local / remote /
  *        boundary, per-element select on boundary tiles.
  * IE:    the pages' three attention passes (window+absolute, causal+remapped,
- *        window+remapped) merged by Eq. 7. A checked alternative.
+ *        window+remapped) merged by Eq. 7. A checked alternative, NOT exact
+ *        in floating point: Eq. 7 subtracts pass C's weighted output from
+ *        pass B's, and on a row whose cancellation ratio (stored at
+ *        jl_prefill_ie_ratio_offset) is large the float32 passes lose digits
+ *        in proportion; above a ratio of about 1e3 the row's output is
+ *        unreliable (on peaked 128K inputs about 1% of rows, errors up to
+ *        1e5). FUSED has no subtraction and meets the tolerance on every row.
  * PLAIN: ordinary causal RoPE attention (every pair local) -- the baseline
  *        the bifocal overhead is measured against. */
 typedef enum JL_ENUM_BASE { JL_MODE_FUSED = 0, JL_MODE_IE = 1, JL_MODE_PLAIN = 2 } jl_mode;

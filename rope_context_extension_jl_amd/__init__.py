@@ -161,6 +161,14 @@ def _want(t: Optional[torch.Tensor], name: str, shape, dtype, device=None) -> No
         raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
+def _ws_bytes(workspace: torch.Tensor, device) -> int:
+    """Byte size of a workspace tensor of any dtype; it must sit on the call's
+    device (the C ABI sees a bare pointer and a byte count)."""
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}, got {workspace.device}")
+    return workspace.numel() * workspace.element_size()
+
+
 def _want_cu(cu: Optional[torch.Tensor], name: str, device) -> int:
     """Number of sequences described by an int32 [B + 1] prefix-offset tensor."""
     if cu is None:
@@ -286,11 +294,12 @@ def bifocal_prefill(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, w0: int
     need = prefill_workspace_size(T, B, Hq, Hkv, d, xq.dtype, mode)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
+    ws_n = _ws_bytes(workspace, dv)
     st = lib().jl_bifocal_prefill_timed(
         _dev(xq, "xq"), _dev(xk, "xk"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
         _dev(kcache_out, "kcache_out"), _dev(cu_seqlens, "cu_seqlens"), B, T, Hq, Hkv, d,
         int(w0), int(w_pre), float(theta), float(scale), _dtype_code(xq), _mode_code(mode, remap),
-        _dev(workspace, "workspace"), workspace.numel(), _stream(xq.device), *_events(events))
+        _dev(workspace, "workspace"), ws_n, _stream(xq.device), *_events(events))
     _check("jl_bifocal_prefill", st)
     return out, lse
 
@@ -342,11 +351,12 @@ def bifocal_prefill_cached(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch
     if workspace is None:
         need = prefill_cached_workspace_size(q_off, Tq, Hq, Hkv, d, mode)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
+    ws_n = _ws_bytes(workspace, dv)
     st = lib().jl_bifocal_prefill_cached_timed(
         _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
         _dev(lse, "lse"), int(q_off), Tq, C, Hq, Hkv, d, int(w0), int(w_pre), float(theta),
         float(scale), _dtype_code(xq), _mode_code(mode, remap), _dev(workspace, "workspace"),
-        workspace.numel(), _stream(xq.device), *_events(events))
+        ws_n, _stream(xq.device), *_events(events))
     _check("jl_bifocal_prefill_cached", st)
     return out, lse
 
@@ -374,12 +384,13 @@ def bifocal_decode(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
         lse = torch.empty((Hq,), dtype=torch.float32, device=xq.device)
     if workspace is None:
         workspace = decode_workspace(C, Hq, d, xq.device)
+    ws_n = _ws_bytes(workspace, dv)
     st = lib().jl_bifocal_decode_timed(
         _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
         _dev(lse, "lse"), int(pos), C, Hq, Hkv, d, int(w0), int(w_pre), float(theta),
         float(scale), _dtype_code(xq), _mode_code(mode, remap), int(num_splits),
         _dev(workspace, "workspace"),
-        workspace.numel(), _stream(xq.device), *_events(events))
+        ws_n, _stream(xq.device), *_events(events))
     _check("jl_bifocal_decode", st)
     return out, lse
 
@@ -420,12 +431,13 @@ def bifocal_decode_batch(xq: torch.Tensor, kcache: torch.Tensor, vcache: torch.T
         lse = torch.empty((B, Hq), dtype=torch.float32, device=xq.device)
     if workspace is None:
         workspace = decode_batch_workspace(B, max_keys, Hq, d, xq.device)
+    ws_n = _ws_bytes(workspace, dv)
     st = lib().jl_bifocal_decode_batch_timed(
         _dev(xq, "xq"), _dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(out, "out"),
         _dev(lse, "lse"), _dev(positions, "positions"), _dev(cache_starts, "cache_starts"), B,
         int(max_keys), C, Hq, Hkv, d, int(w0), int(w_pre), float(theta), float(scale),
         _dtype_code(xq), _mode_code(mode, remap), int(num_splits), _dev(workspace, "workspace"),
-        workspace.numel(), _stream(xq.device), *_events(events))
+        ws_n, _stream(xq.device), *_events(events))
     _check("jl_bifocal_decode_batch", st)
     return out, lse
 

@@ -243,6 +243,31 @@ def test_python_binding_checks_shapes_and_dtypes():
         jl.bifocal_decode_batch(qb, kc, kc, pos.long(), pos, 4, *args)
 
 
+def test_python_binding_checks_workspace_device():
+    """A workspace on another device than the call's tensors raises before any
+    launch (the C ABI sees a bare pointer); its byte count is numel times the
+    element size for any dtype."""
+    import torch
+    bf = torch.bfloat16
+    T, Hq, Hkv, d = 8, 4, 2, 128
+    q = torch.zeros(T, Hq, d, dtype=bf)
+    k = torch.zeros(T, Hkv, d, dtype=bf)
+    kc = torch.zeros(16, Hkv, d, dtype=bf)
+    other = torch.empty(64, dtype=torch.uint8, device="meta")
+    args = (1, 4, 1e4)
+    with pytest.raises(ValueError, match="workspace must be on"):
+        jl.bifocal_prefill(q, k, k, *args, workspace=other)
+    with pytest.raises(ValueError, match="workspace must be on"):
+        jl.bifocal_prefill_cached(q, kc, kc, 0, *args, workspace=other)
+    with pytest.raises(ValueError, match="workspace must be on"):
+        jl.bifocal_decode(q[0], kc, kc, 3, *args, workspace=other)
+    pos = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="workspace must be on"):
+        jl.bifocal_decode_batch(torch.zeros(2, Hq, d, dtype=bf), kc, kc, pos, pos, 4, *args,
+                                workspace=other)
+    assert jl._ws_bytes(torch.zeros(10, dtype=torch.float32), torch.device("cpu")) == 40
+
+
 def test_calibration_argument_errors():
     f, g = jl.lib().jl_calib_stream_read, jl.lib().jl_calib_mfma_bf16
     assert f(None, 1024, P, 16, None) == -1

@@ -551,6 +551,32 @@ def test_decode_workspace_reuse():
         assert_bf16_close(to_host(o1), ro, f"reuse pos={pos}")
 
 
+def test_workspace_of_any_dtype():
+    """The binding passes a workspace's size in bytes (numel times element
+    size): a float32 workspace of just enough elements serves decode and
+    prefill, with the same results bit for bit as a uint8 workspace."""
+    w0, w_pre, theta = 100, 512, 1e6
+    xq, xk, v, kc, vc, tdt = _decode_setup("bf16")
+    Hq = xq.shape[1]
+    pos = 2999
+    need = jl.decode_workspace_size(kc.shape[0], Hq, 128)
+    ws32 = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
+    note(f"decode with a float32 workspace of {ws32.numel()} elements ({need} bytes needed)")
+    o1, l1 = jl.bifocal_decode(to_dev(xq[pos]), kc, vc, pos, w0, w_pre, theta, workspace=ws32)
+    o2, l2 = jl.bifocal_decode(to_dev(xq[pos]), kc, vc, pos, w0, w_pre, theta)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    T, Hkv = 300, kc.shape[1]
+    q, k, vv = to_dev(xq[:T]), to_dev(xk[:T]), to_dev(v[:T])
+    needp = jl.prefill_workspace_size(T, 1, Hq, Hkv, 128)
+    wsp = torch.empty((needp + 1) // 2, dtype=torch.bfloat16, device="cuda")
+    note(f"prefill with a bfloat16 workspace of {wsp.numel()} elements ({needp} bytes needed)")
+    p1, s1 = jl.bifocal_prefill(q, k, vv, w0, w_pre, theta, workspace=wsp)
+    p2, s2 = jl.bifocal_prefill(q, k, vv, w0, w_pre, theta)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(s1, s2)
+
+
 @pytest.mark.parametrize("where", ["key", "query"])
 def test_decode_out_of_fp16_range_gives_nan(where):
     """A cached key beyond the fp16 range (1e6), or a query whose scaled
